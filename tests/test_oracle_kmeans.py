@@ -1,0 +1,127 @@
+"""Pins for the oracle's exact-order clustering arithmetic.
+
+* Distances and means against float64 (scipy / numpy) within the fp32 error
+  bound of a sequential sum, which fails on a dropped term, a transposed
+  operand or a wrong axis.
+* The capped greedy assignment against an independent certificate: an
+  assignment equals the greedy walk over (distance, key, cluster) in ascending
+  order if and only if, for every key, each cluster it prefers to its own is
+  full of keys whose triples come earlier (a short exchange argument shows
+  that only one assignment satisfies this).
+* A non-binding cap reduces seal to textbook Lloyd from the same initial
+  centres: scikit-learn's KMeans (algorithm="lloyd") is the library reference.
+"""
+import numpy as np
+import pytest
+from scipy.spatial.distance import cdist
+from sklearn.cluster import KMeans
+
+from oracle.kmeans import capped_greedy_assign, mean_exact, nearest, seal_window, sqdist_exact
+
+U = 2.0 ** -24
+
+
+def test_sqdist_within_sequential_sum_bound():
+    rng = np.random.default_rng(10)
+    X = rng.standard_normal((200, 128)).astype(np.float32)
+    C = (rng.standard_normal((17, 128)) * 0.5).astype(np.float32)
+    D = sqdist_exact(X, C).astype(np.float64)
+    ref = cdist(X.astype(np.float64), C.astype(np.float64), "sqeuclidean")
+    gamma = (128 + 2) * U
+    assert np.all(np.abs(D - ref) <= gamma * ref * 1.01)
+    assert np.array_equal(nearest(D), np.argmin(D, axis=1))
+
+
+def test_sqdist_is_exact_on_small_integers():
+    rng = np.random.default_rng(11)
+    X = rng.integers(-50, 50, (30, 32)).astype(np.float32)
+    C = rng.integers(-50, 50, (5, 32)).astype(np.float32)
+    ref = ((X[:, None, :].astype(np.int64) - C[None].astype(np.int64)) ** 2).sum(-1)
+    assert np.array_equal(sqdist_exact(X, C), ref.astype(np.float32))
+
+
+def test_mean_within_bound_and_exact_on_integers():
+    rng = np.random.default_rng(12)
+    rows = rng.standard_normal((300, 64)).astype(np.float32)
+    m = mean_exact(rows).astype(np.float64)
+    ref = rows.astype(np.float64).mean(0)
+    bound = (300 + 1) * U * np.abs(rows.astype(np.float64)).mean(0) * 1.01 + 1e-30
+    assert np.all(np.abs(m - ref) <= bound)
+    ints = rng.integers(-1000, 1000, (64, 8)).astype(np.float32)
+    assert np.array_equal(mean_exact(ints), (ints.astype(np.float64).sum(0) / 64).astype(np.float32))
+
+
+def _certificate_holds(D, assign, cap):
+    n, m = D.shape
+    key = lambda j, c: (D[j, c], j, c)      # the global order of triples
+    members = {c: np.nonzero(assign == c)[0] for c in range(m)}
+    if any(len(v) > cap for v in members.values()) or np.any(assign < 0):
+        return False
+    for j in range(n):
+        mine = key(j, assign[j])
+        for c in range(m):
+            if c == assign[j] or key(j, c) > mine:
+                continue
+            full_early = len(members[c]) == cap and all(key(jj, c) < key(j, c) for jj in members[c])
+            if not full_early:
+                return False
+    return True
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_capped_greedy_matches_certificate(seed):
+    rng = np.random.default_rng(20 + seed)
+    n, m = 48, 4
+    cap = 12 + seed % 3
+    # clustered data so that the cap binds
+    X = np.concatenate([rng.standard_normal((36, 3)) * 0.2, rng.standard_normal((12, 3)) + 3]).astype(np.float32)
+    C = X[rng.choice(n, m, replace=False)]
+    D = sqdist_exact(X, C)
+    if seed % 2:                      # exact distance ties
+        D = np.round(D * 2) / 2
+    a = capped_greedy_assign(D, cap)
+    assert _certificate_holds(D, a, cap)
+    # a plausible wrong walk (by key first) usually breaks the certificate
+    order = np.lexsort((np.tile(np.arange(m), n), D.reshape(-1), np.repeat(np.arange(n), m)))
+    wrong = np.full(n, -1)
+    cnt = np.zeros(m, int)
+    for t in order:
+        j, c = divmod(t, m)
+        if wrong[j] < 0 and cnt[c] < cap:
+            wrong[j] = c
+            cnt[c] += 1
+    if not np.array_equal(wrong, a):
+        assert not _certificate_holds(D, wrong, cap)
+
+
+def test_capped_greedy_equals_nearest_when_cap_does_not_bind():
+    rng = np.random.default_rng(30)
+    X = rng.standard_normal((100, 8)).astype(np.float32)
+    C = X[:5].copy()
+    D = sqdist_exact(X, C)
+    near = nearest(D)
+    cap = int(np.bincount(near, minlength=5).max())
+    assert np.array_equal(capped_greedy_assign(D, cap), near)
+    assert np.array_equal(capped_greedy_assign(D, 100), near)
+
+
+def test_seal_without_binding_cap_is_textbook_lloyd():
+    rng = np.random.default_rng(31)
+    centres = rng.standard_normal((8, 16)) * 4
+    X = (centres[rng.integers(0, 8, 1024)] + rng.standard_normal((1024, 16)) * 0.3).astype(np.float32)
+    a, C, alive = seal_window(X, 8, cap=1024, iters=10)
+    init = np.array([((2 * i + 1) * 1024) // 16 for i in range(8)])
+    km = KMeans(n_clusters=8, init=X[init], n_init=1, max_iter=10, tol=0.0, algorithm="lloyd").fit(X)
+    assert np.array_equal(a, km.labels_)
+    assert np.allclose(C[alive], km.cluster_centers_[alive], rtol=0, atol=1e-5)
+
+
+def test_seal_capped_result_is_a_greedy_fixed_point():
+    rng = np.random.default_rng(32)
+    X = (rng.standard_normal((256, 8)) * np.r_[np.ones(4) * 3, np.ones(4) * 0.1]).astype(np.float32)
+    X[:200] *= 0.05                                      # one dense blob: the cap must bind
+    a, C, alive = seal_window(X, 4, cap=80, iters=6)
+    assert np.bincount(a, minlength=4).max() <= 80
+    for c in range(4):
+        if alive[c]:
+            assert np.array_equal(C[c], mean_exact(X[a == c]))
