@@ -1,0 +1,212 @@
+/*
+ * ivftk.h — C ABI of the causal IVF-routed indexer top-k library (AMD MI355X, gfx950).
+ *
+ * What it computes (AttentionIndex: Accelerating Learned Sparse Attention with a
+ * Causal Inverted-File Index, Park & Hwu, arXiv:2611.02508; pages cited by site and
+ * section):
+ *
+ *   Indexer score (paper-daily.com explainer, "它到底在解决什么问题？" and
+ *   "代表向量为什么要学？"): for query token t with H heads and key j,
+ *       s(t, j) = sum_h w[t,h] * ReLU(q[t,h] . k[j]).
+ *   With E4M3 storage, q[t,h] = codes * q_scale[t,h] and k[j] = codes * k_scale[j];
+ *   both scales must be finite and > 0, so they factor out of the ReLU.
+ *
+ *   Exhaustive selection (same page, "它到底在解决什么问题？"): every key j <= p of
+ *   the query at position p is scored and the top k are kept.
+ *
+ *   Routed selection (same page, "查询时怎么挑候选？"): the query scores every
+ *   visible cluster representative with the same formula, ranks the clusters,
+ *   fills a candidate budget with the sink keys and the whole open window, then the
+ *   members of clusters in rank order, truncating the last one, scores the
+ *   candidates exactly and keeps the top k.
+ *
+ *   Index maintenance (same page, "索引怎么边算边建？"; kurate.org assessment,
+ *   "Core Contribution" item 1): keys are inserted into an open window; every W
+ *   keys are sealed into W/cluster_size clusters by size-capped k-means; every R
+ *   tokens the whole sealed prefix is refitted (one assignment + update round,
+ *   warm-started from the previous centres plus the new seal centres, with
+ *   upper/lower distance bounds) on a second stream; every seal and refit is a
+ *   version, and a query only sees versions whose keys all lie in its prefix.
+ *
+ * Conventions shared by every call:
+ *   - Return value: IDX_OK (0) or a negative idx_status.  On error nothing has been
+ *     enqueued and idx_last_error() gives a message (thread-local, valid until the
+ *     next call on the same thread).  No call aborts and no C++ exception crosses
+ *     this boundary.
+ *   - "device" pointers are HIP device memory (e.g. torch CUDA tensors under ROCm);
+ *     "host" pointers are ordinary CPU memory.  Every array is dense and row-major.
+ *   - Streams are hipStream_t passed as void* (NULL = the default stream).  Calls
+ *     validate on the host, enqueue work on the given stream(s) and return without
+ *     waiting, except idx_export and idx_destroy, which wait.
+ *   - Caller-owned inputs must stay valid until the stream has passed the enqueued
+ *     work; caller-owned outputs are written by that work.
+ *   - An index handle is used from one host thread at a time, with one main stream
+ *     that orders all its calls (routes, seals, publication).
+ *   - Key storage formats (idx_dtype): IDX_F32 = fp32; IDX_BF16 = bf16 (2 bytes);
+ *     IDX_E4M3 = OCP 8-bit E4M3 (e4m3fn, 1 byte, largest finite 448) with an fp32
+ *     scale per key and per (query, head).  Codes 0x7F/0xFF (NaN) must not occur.
+ *   - A row of d elements takes d * element_size bytes; queries are [T, H, d].
+ *   - Top-k outputs hold key positions sorted by (score descending, position
+ *     ascending); fewer than k candidates pad with position -1 and score -inf.
+ */
+#ifndef IVFTK_H
+#define IVFTK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct idx_index idx_index;
+
+typedef enum { IDX_F32 = 0, IDX_BF16 = 1, IDX_E4M3 = 2 } idx_dtype;
+
+typedef enum {
+  IDX_OK = 0,
+  IDX_EINVAL = -1,      /* bad argument, shape, dtype or pointer                       */
+  IDX_ENOMEM = -2,      /* device allocation failed at idx_create                      */
+  IDX_EDEVICE = -3,     /* a HIP call failed; the handle is poisoned                   */
+  IDX_ECAUSAL = -4,     /* a query position whose key has not been inserted            */
+  IDX_ESTATE = -5,      /* call not allowed in this state (poisoned, epoch retired...) */
+  IDX_ECAPACITY = -6,   /* more keys than max_keys, or a size above a create-time max  */
+  IDX_ENOTIMPL = -7     /* shape or format this build does not provide                 */
+} idx_status;
+
+/* Index configuration, fixed at idx_create.  All device memory of the index is
+ * allocated there from these numbers; no later call allocates. */
+typedef struct {
+  int32_t heads;         /* H, indexer heads per query: 1..128                                 */
+  int32_t dim;           /* d: F32 32, 64 or 128; BF16 and E4M3 64 or 128                      */
+  int32_t dtype;         /* idx_dtype of keys, queries and cluster representatives           */
+  int32_t n_sink;        /* S: keys [0, S) are always candidates and never clustered (>= 0)  */
+  int32_t window;        /* W: keys sealed per window, 2..1024                                 */
+  int32_t cluster_size;  /* W / cluster_size clusters per seal, window*(W/cluster_size) <= 8192 */
+  int32_t seal_cap;      /* most keys one seal cluster may hold; cap * clusters >= W           */
+  int32_t seal_iters;    /* Lloyd iterations per seal, 1..64                                   */
+  int32_t refit_every;   /* R: refit after every R/W seals; multiple of W; 0 = never           */
+  int32_t max_queries;   /* largest T of one idx_route_topk call                               */
+  int32_t max_budget;    /* largest budget of one idx_route_topk call (max(budget, S+W) <= 16384) */
+  int32_t max_k;         /* largest k of one idx_route_topk call (<= 4096)                     */
+  int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1)                       */
+} idx_config;
+
+/* Snapshot of the host-side index state (no device wait). */
+typedef struct {
+  int64_t n_keys;            /* keys inserted so far                                  */
+  int32_t sealed_windows;    /* m: windows [0, m) sealed                              */
+  int32_t computed_epoch;    /* newest refit epoch launched (0 = none)                */
+  int32_t published_epoch;   /* newest refit epoch visible to queries (0 = none)      */
+  int32_t clusters_per_window;
+  int32_t slots_per_epoch;   /* Q = (R/W) * clusters_per_window                       */
+  int64_t device_bytes;      /* device memory owned by the index                      */
+} idx_info;
+
+/* Optional debug outputs of idx_route_topk: all device pointers, each may be NULL.
+ * Rows are per query; cand/order rows have cand_cap/order_cap entries. */
+typedef struct {
+  int32_t* cand;         /* [T, cand_cap]: candidate positions in fill order            */
+  int32_t cand_cap;
+  int32_t* cand_len;     /* [T]: candidates of each query                               */
+  int32_t* order;        /* [T, order_cap]: clusters (slot ids) used, in rank order     */
+  int32_t* order_take;   /* [T, order_cap]: members taken from each (last may be cut)   */
+  int32_t order_cap;
+  int32_t* n_order;      /* [T]: clusters used (entries beyond order_cap not written)   */
+  float* rep_scores;     /* [T, rep_cap]: representative score of each visible slot     */
+  int32_t rep_cap;
+  int32_t* version;      /* [T, 4]: epoch r, sealed windows m, visible slots, open start */
+} idx_route_debug;
+
+/* Host buffers for idx_export.  Pass NULL arrays to read only the counts. */
+typedef struct {
+  int32_t n_slots;       /* out: slots in the exported set                              */
+  int32_t n_members;     /* out: member entries                                         */
+  int32_t* sizes;        /* [n_slots]: members per slot (0 = empty, never routed)       */
+  int32_t* offsets;      /* [n_slots]: index of the slot's first member in `members`    */
+  int32_t* members;      /* [n_members]: key positions, ascending within each slot      */
+  float* centroids;      /* [n_slots, d] fp32                                           */
+  void* reps;            /* [n_slots, d] representatives in the key format              */
+  float* rep_scale;      /* [n_slots] (1.0 unless E4M3)                                 */
+} idx_export_buf;
+
+/* Create an index on the current HIP device; *out receives the handle. */
+int idx_create(const idx_config* cfg, idx_index** out);
+
+/* Wait for all work of the device, free everything.  NULL is accepted. */
+int idx_destroy(idx_index* ix);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char* idx_last_error(void);
+
+int idx_get_info(const idx_index* ix, idx_info* out);
+
+/* Insert n keys at positions [n_keys, n_keys + n) and seal every window that fills.
+ *   keys:    device [n, d] in the index dtype; copied, free once the stream passes.
+ *   k_scale: device [n] fp32 (> 0) for E4M3, NULL otherwise.
+ * Each sealed window runs `seal_iters` Lloyd iterations with the size-capped greedy
+ * assignment in exact-order fp32 and appends its clusters (slots w*C .. w*C+C-1);
+ * a query sees them once its prefix holds the whole window.
+ * Errors: EINVAL (pointers, n < 0), ECAPACITY (n_keys + n > max_keys). */
+int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_t n, void* stream);
+
+/* Launch the next refit if one is due: sealed windows >= (e+1)*R/W for the next
+ * epoch e+1, and the previous epoch has been published.  Refit e+1 covers keys
+ * [S, S + (e+1)*R): it starts from the centroids of slots [0, (e+1)*Q) (epoch e plus
+ * the newer seal clusters), assigns every covered key to its nearest centroid (ties
+ * to the lower slot; Hamerly-style bounds skip keys whose cluster is certified), and
+ * replaces each centroid by the exact-order mean of its members.  Work runs on
+ * side_stream after everything already enqueued on `stream`.
+ *   launched: host out, 1 if a refit was launched, else 0. */
+int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched);
+
+/* Make the launched refit visible: `stream` waits for it; later routes may use the
+ * new epoch for queries whose prefix holds all of its keys.  published: host out,
+ * the newest visible epoch (may be NULL). */
+int idx_publish(idx_index* ix, void* stream, int32_t* published);
+
+/* Routed top-k for T queries at positions q_pos0 .. q_pos0 + T - 1.
+ *   q:       device [T, H, d] in the index dtype.
+ *   q_scale: device [T, H] fp32 (> 0) for E4M3, NULL otherwise.
+ *   w:       device [T, H] fp32 head weights (any sign).
+ *   k <= budget <= max_budget, k <= max_k, T <= max_queries.
+ *   topk_idx: device [T, k] int32 out; topk_score: device [T, k] fp32 out or NULL.
+ *   dbg:     host struct of optional device outputs, or NULL.
+ * Per query at position p: the version is the newest published epoch whose keys
+ * all lie below S + m*W (m = windows inside the prefix) plus the seal clusters of
+ * later windows < m; candidates are sinks [0, S), the open window [S + m*W, p] and
+ * ranked cluster members until `budget` is reached (sinks and open window count
+ * against the budget but are always taken whole).
+ * Errors: ECAUSAL (q_pos0 + T > n_keys), ESTATE (a query needs an epoch older than
+ * the two newest published ones), EINVAL / ECAPACITY for sizes. */
+int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
+                   int32_t T, int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score,
+                   const idx_route_debug* dbg, void* stream);
+
+/* Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass. */
+int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T);
+
+/* Exhaustive top-k (stateless): query t at position q_pos0 + t scores keys
+ * [0, q_pos0 + t] of `keys` and keeps the top k.
+ *   keys: device [n_keys, d]; k_scale: device [n_keys] for E4M3 else NULL;
+ *   q, q_scale, w as in idx_route_topk; q_pos0 + T <= n_keys; 1 <= k <= 4096.
+ *   workspace: device scratch of workspace_bytes >= idx_exhaustive_workspace_bytes(n_keys, 1);
+ *   queries are processed in as many passes as the workspace requires.
+ * Scores are bit-identical to the rescoring of idx_route_topk for the same (q, k). */
+int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
+                        int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
+                        int32_t T, int32_t k, int32_t* topk_idx, float* topk_score, void* workspace,
+                        int64_t workspace_bytes, void* stream);
+
+/* Copy one cluster set to host memory (waits for the index's streams).
+ *   which = -1: every sealed window's clusters (slots [0, m*C)), members grouped
+ *               per window in slot order;
+ *   which = e >= 1: refit epoch e (must be one of the last three computed), slots
+ *               [0, e*Q).
+ * Call once with NULL arrays to read n_slots / n_members, then with buffers. */
+int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* IVFTK_H */

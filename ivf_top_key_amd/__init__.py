@@ -1,0 +1,196 @@
+"""Causal IVF-routed indexer top-k on AMD MI355X (gfx950): Python binding.
+
+Each function here has the name of a C entry point in include/ivftk.h and only
+marshals arguments: torch tensors on the GPU become device pointers, the
+current torch stream becomes the HIP stream, and outputs are allocated with
+torch when the caller passes none.  All computation runs in libivftk.so; when
+the library is missing the calls raise instead of falling back to anything.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from . import _lib
+
+DTYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+IDX_OK, IDX_EINVAL, IDX_ENOMEM, IDX_EDEVICE, IDX_ECAUSAL, IDX_ESTATE, IDX_ECAPACITY, IDX_ENOTIMPL = \
+    0, -1, -2, -3, -4, -5, -6, -7
+
+
+class IdxError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+def lib():
+    return _lib.load()
+
+
+def idx_last_error() -> str:
+    return (lib().idx_last_error() or b"").decode()
+
+
+def _check(rc: int):
+    if rc != IDX_OK:
+        raise IdxError(rc, idx_last_error())
+
+
+def _ptr(t, elem_bytes=None, name="tensor"):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if elem_bytes is not None and t.element_size() != elem_bytes:
+        raise ValueError(f"{name} must have {elem_bytes}-byte elements (got {t.element_size()})")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+class Index:
+    """Handle of one index (C: idx_index*).  Holds its configuration for the binding."""
+
+    def __init__(self, handle, cfg: dict):
+        self.handle = handle
+        self.cfg = cfg
+
+    @property
+    def dtype(self) -> str:
+        return self.cfg["dtype"]
+
+
+def idx_create(heads: int, dim: int, dtype: str, max_keys: int, n_sink: int = 4, window: int = 1024,
+               cluster_size: int = 128, seal_cap: int = 256, seal_iters: int = 10, refit_every: int = 16384,
+               max_queries: int = 4096, max_budget: int = 8192, max_k: int = 2048) -> Index:
+    cfg = dict(heads=heads, dim=dim, dtype=dtype, n_sink=n_sink, window=window, cluster_size=cluster_size,
+               seal_cap=seal_cap, seal_iters=seal_iters, refit_every=refit_every, max_queries=max_queries,
+               max_budget=max_budget, max_k=max_k, max_keys=max_keys)
+    c = _lib.idx_config(heads, dim, DTYPES[dtype], n_sink, window, cluster_size, seal_cap, seal_iters,
+                        refit_every, max_queries, max_budget, max_k, max_keys)
+    h = ctypes.c_void_p()
+    _check(lib().idx_create(ctypes.byref(c), ctypes.byref(h)))
+    return Index(h, cfg)
+
+
+def idx_destroy(ix: Index):
+    if ix.handle:
+        _check(lib().idx_destroy(ix.handle))
+        ix.handle = None
+
+
+def idx_get_info(ix: Index) -> dict:
+    info = _lib.idx_info()
+    _check(lib().idx_get_info(ix.handle, ctypes.byref(info)))
+    return {k: getattr(info, k) for k, _ in _lib.idx_info._fields_}
+
+
+def idx_build_seal(ix: Index, keys: torch.Tensor, k_scale: torch.Tensor | None = None, stream=None):
+    eb = ELEM_BYTES[ix.dtype]
+    n = keys.shape[0]
+    _check(lib().idx_build_seal(ix.handle, _ptr(keys, eb, "keys"), _ptr(k_scale, 4, "k_scale"), n,
+                                _stream(stream)))
+
+
+def idx_refit(ix: Index, stream=None, side_stream=None) -> bool:
+    launched = ctypes.c_int32(0)
+    side = side_stream if side_stream is not None else stream
+    _check(lib().idx_refit(ix.handle, _stream(stream), _stream(side), ctypes.byref(launched)))
+    return bool(launched.value)
+
+
+def idx_publish(ix: Index, stream=None) -> int:
+    pub = ctypes.c_int32(0)
+    _check(lib().idx_publish(ix.handle, _stream(stream), ctypes.byref(pub)))
+    return pub.value
+
+
+def make_route_debug(T: int, cand_cap: int, order_cap: int, rep_cap: int, device="cuda") -> dict:
+    """Device buffers for the optional debug outputs of idx_route_topk."""
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(cand=torch.full((T, cand_cap), -1, **i32), cand_len=torch.zeros(T, **i32),
+                order=torch.full((T, order_cap), -1, **i32), order_take=torch.zeros((T, order_cap), **i32),
+                n_order=torch.zeros(T, **i32),
+                rep_scores=torch.zeros((T, rep_cap), dtype=torch.float32, device=device),
+                version=torch.zeros((T, 4), **i32))
+
+
+def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0: int, k: int, budget: int,
+                   topk_idx=None, topk_score=None, debug: dict | None = None, stream=None):
+    T = q.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=q.device)
+    if topk_score is None:
+        topk_score = torch.empty((T, k), dtype=torch.float32, device=q.device)
+    dbg = None
+    if debug is not None:
+        dbg = _lib.idx_route_debug(
+            _ptr(debug.get("cand")), debug["cand"].shape[1] if debug.get("cand") is not None else 0,
+            _ptr(debug.get("cand_len")), _ptr(debug.get("order")), _ptr(debug.get("order_take")),
+            debug["order"].shape[1] if debug.get("order") is not None else 0, _ptr(debug.get("n_order")),
+            _ptr(debug.get("rep_scores")),
+            debug["rep_scores"].shape[1] if debug.get("rep_scores") is not None else 0,
+            _ptr(debug.get("version")))
+    _check(lib().idx_route_topk(ix.handle, _ptr(q, ELEM_BYTES[ix.dtype], "q"), _ptr(q_scale, 4, "q_scale"),
+                                _ptr(w, 4, "w"), q_pos0, T, k, budget, _ptr(topk_idx, 4, "topk_idx"),
+                                _ptr(topk_score, 4, "topk_score"), ctypes.byref(dbg) if dbg is not None else None,
+                                _stream(stream)))
+    return topk_idx, topk_score
+
+
+def idx_exhaustive_workspace_bytes(n_keys: int, T: int) -> int:
+    return int(lib().idx_exhaustive_workspace_bytes(n_keys, T))
+
+
+def idx_exhaustive_topk(keys: torch.Tensor, k_scale, dtype: str, heads: int, q: torch.Tensor, q_scale,
+                        w: torch.Tensor, q_pos0: int, k: int, topk_idx=None, topk_score=None, workspace=None,
+                        n_keys: int | None = None, stream=None):
+    T = q.shape[0]
+    d = keys.shape[-1]
+    n_keys = keys.shape[0] if n_keys is None else n_keys
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=q.device)
+    if topk_score is None:
+        topk_score = torch.empty((T, k), dtype=torch.float32, device=q.device)
+    if workspace is None:
+        nbytes = idx_exhaustive_workspace_bytes(q_pos0 + T, T)
+        workspace = torch.empty(nbytes // 4, dtype=torch.float32, device=q.device)
+    eb = ELEM_BYTES[dtype]
+    _check(lib().idx_exhaustive_topk(_ptr(keys, eb, "keys"), _ptr(k_scale, 4, "k_scale"), n_keys, DTYPES[dtype],
+                                     heads, d, _ptr(q, eb, "q"), _ptr(q_scale, 4, "q_scale"), _ptr(w, 4, "w"),
+                                     q_pos0, T, k, _ptr(topk_idx, 4, "topk_idx"), _ptr(topk_score, 4, "topk_score"),
+                                     _ptr(workspace, None, "workspace"), workspace.numel() * workspace.element_size(),
+                                     _stream(stream)))
+    return topk_idx, topk_score
+
+
+def idx_export(ix: Index, which: int) -> dict:
+    """Host copy of one cluster set: which=-1 sealed windows, which=e epoch e."""
+    buf = _lib.idx_export_buf()
+    _check(lib().idx_export(ix.handle, which, ctypes.byref(buf)))
+    ns, nm, d = buf.n_slots, buf.n_members, ix.cfg["dim"]
+    out = dict(sizes=np.zeros(ns, np.int32), offsets=np.zeros(ns, np.int32), members=np.zeros(nm, np.int32),
+               centroids=np.zeros((ns, d), np.float32),
+               reps=np.zeros((ns, d), {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[ix.dtype]),
+               rep_scale=np.zeros(ns, np.float32))
+    for k in out:
+        setattr(buf, k, out[k].ctypes.data if out[k].size else None)
+    _check(lib().idx_export(ix.handle, which, ctypes.byref(buf)))
+    return out
+
+
+__all__ = ["IdxError", "Index", "idx_create", "idx_destroy", "idx_last_error", "idx_get_info", "idx_build_seal",
+           "idx_refit", "idx_publish", "idx_route_topk", "idx_exhaustive_workspace_bytes", "idx_exhaustive_topk",
+           "idx_export", "make_route_debug", "DTYPES"]

@@ -1,0 +1,369 @@
+// Device-side building blocks shared by every kernel of the library (gfx950, wave64).
+//
+// * Stored formats: fp32, bf16, OCP E4M3 (e4m3fn).  Decoding is exact; encoding is
+//   round-to-nearest-even, saturating at +-448 for E4M3.
+// * Composite sort keys: (order-preserving bits of an fp32 score) << 32 | ~position,
+//   so that a larger key means a higher score and, among equal scores, a lower
+//   position (the tie rule of the top-k and of cluster ranking).
+// * LDS bitonic sort and a weighted radix select over such keys.
+// * The indexer-score tile: for one query (H heads) against 32 keys, MFMA contracts
+//   q[h] . k[j] over d with fp32 accumulation, then the epilogue reduces
+//   sum_h w'[h] * max(acc[h][j], 0) over heads inside the wave.  The same tile serves
+//   representative scoring, candidate rescoring and exhaustive scoring, so a (query,
+//   key) pair gets bit-identical scores on every path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ivftk {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
+
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+template <int DT>
+struct Elem;
+template <>
+struct Elem<DT_F32> { static constexpr int bytes = 4; };
+template <>
+struct Elem<DT_BF16> { static constexpr int bytes = 2; };
+template <>
+struct Elem<DT_E4M3> { static constexpr int bytes = 1; };
+
+// ---------------------------------------------------------------------------
+// stored formats
+// ---------------------------------------------------------------------------
+
+// E4M3 code -> fp32 (exact).  Exponent field 0 is subnormal: m * 2^-9.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
+  const uint32_t sign = (code & 0x80u) << 24;
+  const uint32_t e = (code >> 3) & 0xFu;
+  const uint32_t m = code & 7u;
+  if (e == 0) {
+    const float v = (float)m * 0x1p-9f;
+    return __uint_as_float(__float_as_uint(v) | sign);
+  }
+  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
+  const uint32_t b = __float_as_uint(v);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// fp32 -> E4M3 code, round to nearest even, saturating at 448, sign bit kept.
+__device__ __forceinline__ uint32_t f32_to_e4m3(float v) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t sign = (b >> 24) & 0x80u;
+  const uint32_t mag = b & 0x7FFFFFFFu;
+  uint32_t code;
+  if (mag >= 0x43E00000u) {                 // >= 448
+    code = 0x7Eu;
+  } else if (mag >= 0x3C800000u) {          // >= 2^-6: normal, keep 3 mantissa bits
+    const uint32_t r = (mag + 0x7FFFFu + ((mag >> 20) & 1u)) >> 20;
+    code = r - (120u << 3);
+    if (code > 0x7Eu) code = 0x7Eu;
+  } else {                                  // subnormal: multiple of 2^-9
+    code = (uint32_t)__builtin_rintf(__uint_as_float(mag) * 512.0f);
+  }
+  return code | sign;
+}
+
+// Element i of a stored row as fp32 (no scale).
+template <int DT>
+__device__ __forceinline__ float load_elem(const uint8_t* row, int i) {
+  if constexpr (DT == DT_F32) {
+    return reinterpret_cast<const float*>(row)[i];
+  } else if constexpr (DT == DT_BF16) {
+    return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[i]);
+  } else {
+    return e4m3_to_f32(row[i]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// composite keys
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0;              // -0 ranks as +0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float from_order_bits(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o ^ 0x80000000u) : ~o);
+}
+
+__device__ __forceinline__ uint64_t make_comp(float score, uint32_t id) {
+  return ((uint64_t)order_bits(score) << 32) | (uint64_t)(~id);
+}
+
+__device__ __forceinline__ uint32_t comp_id(uint64_t c) { return ~(uint32_t)c; }
+__device__ __forceinline__ float comp_score(uint64_t c) { return from_order_bits((uint32_t)(c >> 32)); }
+
+__host__ __device__ __forceinline__ int next_pow2(int n) {
+  int p = 1;
+  while (p < n) p <<= 1;
+  return p;
+}
+
+// ---------------------------------------------------------------------------
+// block-wide helpers (all threads of the block must call them)
+// ---------------------------------------------------------------------------
+
+// Sort a[0..n) (n a power of two) into descending order.
+__device__ inline void bitonic_sort_desc(uint64_t* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = a[i], y = a[ixj];
+          const bool desc = (i & k) == 0;
+          if (desc ? (x < y) : (x > y)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Sort a[0..n) (n a power of two) into ascending order.
+__device__ inline void bitonic_sort_asc(uint64_t* a, int n) {
+  for (int k = 2; k <= n; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < n; i += blockDim.x) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t x = a[i], y = a[ixj];
+          const bool asc = (i & k) == 0;
+          if (asc ? (x > y) : (x < y)) {
+            a[i] = y;
+            a[ixj] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+struct SelectScratch {
+  int hist[256];
+  int cnt[256];
+  uint64_t prefix;
+  int need;
+  int count;
+  uint64_t result;
+};
+
+// Weighted radix select over unique nonzero keys a[0..n).  Returns the key T with
+//   sum_{a > T} w < target <= sum_{a >= T} w,
+// where w = wts[i] (or 1 when wts is null).  Requires 1 <= target <= sum of w.
+// Keys equal to 0 are ignored (padding).
+__device__ inline uint64_t radix_select_desc(const uint64_t* a, const int* wts, int n, int target,
+                                             SelectScratch& sc) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sc.prefix = 0;
+    sc.need = target;
+  }
+  __syncthreads();
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += blockDim.x) {
+      sc.hist[i] = 0;
+      sc.cnt[i] = 0;
+    }
+    __syncthreads();
+    const uint64_t prefix = sc.prefix;
+    const uint64_t mask = (shift == 56) ? 0ull : (~0ull << (shift + 8));
+    for (int i = tid; i < n; i += blockDim.x) {
+      const uint64_t v = a[i];
+      if (v != 0 && (v & mask) == prefix) {
+        const int d = (int)((v >> shift) & 255u);
+        atomicAdd(&sc.hist[d], wts ? wts[i] : 1);
+        atomicAdd(&sc.cnt[d], 1);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      // lane L owns digits 255-4L .. 252-4L (descending)
+      const int lane = tid;
+      int s = 0;
+      for (int q = 0; q < 4; ++q) s += sc.hist[255 - 4 * lane - q];
+      int incl = s;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int excl = incl - s;
+      const int need = sc.need;
+      if (excl < need && need <= incl) {
+        int acc = excl;
+        for (int q = 0; q < 4; ++q) {
+          const int d = 255 - 4 * lane - q;
+          if (acc + sc.hist[d] >= need) {
+            sc.need = need - acc;
+            sc.prefix = prefix | ((uint64_t)d << shift);
+            sc.count = sc.cnt[d];
+            break;
+          }
+          acc += sc.hist[d];
+        }
+      }
+    }
+    __syncthreads();
+    if (sc.count == 1 || shift == 0) {
+      const uint64_t p = sc.prefix;
+      const uint64_t m2 = ~0ull << shift;
+      for (int i = tid; i < n; i += blockDim.x) {
+        const uint64_t v = a[i];
+        if (v != 0 && (v & m2) == p) sc.result = v;
+      }
+      __syncthreads();
+      return sc.result;
+    }
+  }
+  return 0;  // not reached
+}
+
+// Exclusive scan of v over the block in thread order; *total receives the sum.
+// tmp must hold one int per wave (blockDim.x / 64 <= 16).
+__device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  int incl = v;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int x = tmp[i];
+    if (i < wave) base += x;
+    tot += x;
+  }
+  __syncthreads();
+  if (total) *total = tot;
+  return base + incl - v;
+}
+
+// ---------------------------------------------------------------------------
+// the indexer-score tile
+// ---------------------------------------------------------------------------
+//
+// MFMA shapes (32x32 output, 16 accumulators per lane):
+//   fp32: v_mfma_f32_32x32x2_f32, bf16: v_mfma_f32_32x32x16_bf16,
+//   E4M3: v_mfma_f32_32x32x64_f8f6f4 (both operands OCP E4M3).
+// Operand layout: lane l feeds row/column (l & 31) and holds a contiguous half of
+// that row, bytes [g*RB/2, (g+1)*RB/2) with g = l >> 5, consumed in KS steps.  A
+// and B use the same split of the d dimension, so the contraction is over all of
+// d whatever order the unit walks the elements of one step in.
+// Output: lane l holds column (l & 31), rows 8*(v>>2) + 4*g + (v&3), v = 0..15.
+
+template <int DT, int D>
+struct Geo {
+  static constexpr int RB = D * Elem<DT>::bytes;   // bytes per row
+  static constexpr int HW = RB / 8;                // dwords per lane (half a row)
+  static constexpr int KD = (DT == DT_F32) ? 1 : (DT == DT_BF16 ? 4 : 8);  // dwords per MFMA step
+  static constexpr int KS = HW / KD;               // MFMA steps per 32x32 tile
+  static_assert(HW % 4 == 0, "half row must be a multiple of 16 bytes");
+};
+
+template <int DT>
+__device__ __forceinline__ void mfma_step(v16f& acc, const uint32_t* a, const uint32_t* b) {
+  if constexpr (DT == DT_F32) {
+    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a[0]), __uint_as_float(b[0]), acc, 0, 0, 0);
+  } else if constexpr (DT == DT_BF16) {
+    v8bf av, bv;
+    __builtin_memcpy(&av, a, 16);
+    __builtin_memcpy(&bv, b, 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+  } else {
+    v8i av, bv;
+    __builtin_memcpy(&av, a, 32);
+    __builtin_memcpy(&bv, b, 32);
+    // format selectors 0/0 = E4M3 for A and B; zero scales select the unscaled op
+    acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc, 0, 0, 0, 0, 0, 0);
+  }
+}
+
+// Load this lane's half row (HW dwords) from `row` (the row's first byte).
+template <int DT, int D>
+__device__ __forceinline__ void load_half_row(uint32_t* r, const uint8_t* row) {
+  const int g = (threadIdx.x >> 5) & 1;
+  const uint4* p = reinterpret_cast<const uint4*>(row + g * (Geo<DT, D>::RB / 2));
+#pragma unroll
+  for (int i = 0; i < Geo<DT, D>::HW / 4; ++i) {
+    const uint4 v = p[i];
+    r[4 * i + 0] = v.x;
+    r[4 * i + 1] = v.y;
+    r[4 * i + 2] = v.z;
+    r[4 * i + 3] = v.w;
+  }
+}
+
+// One query's operands: HT tiles of 32 heads.
+template <int DT, int D, int HT>
+struct QueryFrag {
+  uint32_t a[HT][Geo<DT, D>::HW];
+  float wq[HT][16];   // w[h] * q_scale[h] for this lane's accumulator rows (0 beyond H)
+};
+
+// q_t: the query's [H][RB] rows; w_t, qs_t: [H] (qs_t may be null).
+template <int DT, int D, int HT>
+__device__ __forceinline__ void load_query(QueryFrag<DT, D, HT>& f, const uint8_t* q_t, const float* w_t,
+                                           const float* qs_t, int H) {
+  const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+    const int head = ht * 32 + r;
+    if (head < H) {
+      load_half_row<DT, D>(f.a[ht], q_t + (size_t)head * Geo<DT, D>::RB);
+    } else {
+#pragma unroll
+      for (int i = 0; i < Geo<DT, D>::HW; ++i) f.a[ht][i] = 0;
+    }
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h = ht * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
+      f.wq[ht][v] = (h < H) ? (qs_t ? w_t[h] * qs_t[h] : w_t[h]) : 0.0f;
+    }
+  }
+}
+
+// Score of this lane's column (key) against the query, before the key scale.
+// Lanes l and l+32 return the same value.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const uint32_t (&b)[Geo<DT, D>::HW]) {
+  v16f acc[HT];
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[ht][v] = 0.0f;
+#pragma unroll
+    for (int s = 0; s < Geo<DT, D>::KS; ++s)
+      mfma_step<DT>(acc[ht], &f.a[ht][s * Geo<DT, D>::KD], &b[s * Geo<DT, D>::KD]);
+  }
+  float p = 0.0f;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.wq[ht][v], __builtin_fmaxf(acc[ht][v], 0.0f), p);
+  }
+  const float o = __shfl_xor(p, 32);
+  return p + o;
+}
+
+}  // namespace ivftk

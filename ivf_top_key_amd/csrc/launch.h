@@ -1,0 +1,19 @@
+// Host-side launchers of the kernels (each returns the launch status).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "params.h"
+
+namespace ivftk {
+
+hipError_t launch_exh_score(const ExhParams& p, int dtype, int dim, int ht, int64_t n_max, hipStream_t s);
+hipError_t launch_topk_rows(const ExhParams& p, hipStream_t s);
+hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s);
+hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s);
+hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
+hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, hipStream_t s);
+hipError_t launch_refit(const RefitParams& p, int dtype, int dim, hipStream_t s);
+
+}  // namespace ivftk

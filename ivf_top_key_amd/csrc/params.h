@@ -1,0 +1,124 @@
+// Kernel parameter blocks shared by the host runtime and the kernels.
+#pragma once
+
+#include <stdint.h>
+
+namespace ivftk {
+
+// One set of clusters in device memory, indexed by slot id.
+//   size[s]      members of slot s (0 = empty: never ranked, never a warm start)
+//   off[s]       index of the slot's first member in `members`
+//   members[]    key positions, ascending within a slot
+//   cent[s*d]    fp32 centroid; rep[s*RB] representative in the key format;
+//   rsc[s]       representative scale (E4M3), 1 otherwise
+struct StoreView {
+  const int* size;
+  const int* off;
+  const int* members;
+  const float* cent;
+  const uint8_t* rep;
+  const float* rsc;
+};
+
+// Everything the routed path needs.  Query t sits at position q_pos0 + t; its
+// version is computed on the device from (S, W, Cs, wpr, P): m = windows inside
+// the prefix, epoch r = min(P, m / wpr), slots [0, r*wpr*Cs) come from epoch r's
+// store and slots [r*wpr*Cs, m*Cs) from the seal store.
+struct RouteParams {
+  const uint8_t* keys;
+  const float* kscale;
+  const uint8_t* q;
+  const float* qscale;
+  const float* w;
+  int64_t n_keys;      // keys inserted (positions read from index data are clamped below it)
+  int H;
+  int T;
+  int64_t q_pos0;
+  int k;
+  int budget;
+  int S, W, Cs, wpr, P;
+  StoreView ep[3];     // epoch r lives in ep[r % 3] (the host checks every epoch used is held)
+  StoreView seal;
+  float* srep;         // [T, srep_ld] representative scores
+  int64_t srep_ld;
+  int* cand;           // [T, cand_ld] candidate positions
+  int64_t cand_ld;
+  int* cand_len;       // [T]
+  int* topk_idx;       // [T, k]
+  float* topk_score;   // [T, k] or null
+  // optional debug outputs (null when unused)
+  int* dbg_order;
+  int* dbg_take;
+  int dbg_order_cap;
+  int* dbg_n_order;
+  int* dbg_version;
+};
+
+struct ExhParams {
+  const uint8_t* keys;
+  const float* kscale;
+  const uint8_t* q;
+  const float* qscale;
+  const float* w;
+  int H;
+  int64_t q_pos0;
+  int t0;              // first query of this pass
+  int Tb;              // queries in this pass
+  float* ws;           // [Tb, ld] scores
+  int64_t ld;
+  int kchunk;          // keys per block of the score kernel
+  int k;
+  int* topk_idx;       // [T, k] (row t0 + tl)
+  float* topk_score;
+};
+
+// Seal of windows [w0, w0 + gridDim.x).
+struct SealParams {
+  const uint8_t* keys;
+  const float* kscale;
+  int S, W, Cs, cap, iters;
+  int w0;
+  int* size;          // seal store, indexed by slot w*Cs + c
+  int* off;
+  int* members;       // [windows * W], window w's members at [w*W, (w+1)*W)
+  float* cent;
+  uint8_t* rep;
+  float* rsc;
+};
+
+// One refit: epoch r from slots [0, r*Q) (prev epoch for s < (r-1)*Q, seal store
+// otherwise) over keys [S, B_r), B_r = S + r*R.
+struct RefitParams {
+  const uint8_t* keys;
+  const float* kscale;
+  int64_t n_keys;
+  int S, r, Q;
+  int64_t B_prev;      // S + (r-1)*R : keys below carry bounds from epoch r-1
+  int64_t B_r;         // S + r*R
+  StoreView prev;      // epoch r-1 (size/cent used; valid when r >= 2)
+  const float* prev_drift;      // [slots of r-1]: centroid movement of epoch r-1's update
+  const float* prev_drift_max;  // device scalar
+  StoreView seal;
+  // per-key state, indexed by position
+  int* assign;
+  float* ub;
+  float* lb;
+  // work list of keys that need all centroids
+  int* work;
+  int* work_count;
+  // output epoch store
+  int* size;
+  int* off;
+  int* members;
+  float* cent;
+  uint8_t* rep;
+  float* rsc;
+  float* drift;
+  float* drift_max;
+  // tile histogram scratch [n_tiles, Q*r]
+  int* tile_cnt;
+  int tile;            // keys per tile
+  int n_tiles;
+};
+
+}  // namespace ivftk

@@ -1,0 +1,167 @@
+// Cluster ranking, cut and candidate fill for the routed path (one block per query).
+//
+// AttentionIndex, paper-daily.com explainer, "查询时怎么挑候选？": clusters are
+// ranked by representative score, high to low; the first few keys (sinks) and the
+// open window take fixed slots; the remaining slots take every member of the
+// clusters in rank order and the last cluster that does not fit is truncated.
+// Ranking ties go to the lower slot id; a truncated cluster gives its lowest
+// positions (members are stored in ascending position).
+//
+// The cut is a weighted radix select over composite keys (score bits, ~slot) with
+// the cluster sizes as weights: it finds the cluster at which the running member
+// count first reaches the free budget without sorting every visible cluster.  Only
+// the selected clusters are sorted, and the fill writes their members with one
+// binary search per candidate slot.
+#include "dev.h"
+#include "launch.h"
+#include "params.h"
+
+namespace ivftk {
+
+struct QV {
+  int64_t n;
+  int m, r, split, cvis;
+  int64_t open_lo;
+};
+
+__device__ __forceinline__ QV qversion(const RouteParams& p, int t) {
+  QV v;
+  v.n = p.q_pos0 + t + 1;
+  v.m = v.n >= p.S ? (int)((v.n - p.S) / p.W) : 0;
+  v.r = p.wpr ? min(p.P, v.m / p.wpr) : 0;
+  v.split = v.r * p.wpr * p.Cs;
+  v.cvis = v.m * p.Cs;
+  v.open_lo = (int64_t)p.S + (int64_t)v.m * p.W;
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_pow2) {
+  extern __shared__ uint64_t lds[];
+  uint64_t* comp = lds;                                   // [slot_pow2]
+  int* wt = reinterpret_cast<int*>(lds + slot_pow2);      // [slot_pow2]: sizes, later prefix sums
+  __shared__ SelectScratch sc;
+  __shared__ int wtmp[16];
+  __shared__ int s_total, s_nsel;
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int t = blockIdx.x;
+  const QV v = qversion(p, t);
+  const StoreView ep = p.ep[v.r % 3];
+  int* cand = p.cand + (size_t)t * p.cand_ld;
+
+  // sinks [0, min(S, n)) then the open window [open_lo, n)
+  const int n_sink = (int)(v.n < p.S ? v.n : p.S);
+  const int n_open = v.n > v.open_lo ? (int)(v.n - v.open_lo) : 0;
+  const int base_len = n_sink + n_open;
+  for (int i = tid; i < base_len; i += bd)
+    cand[i] = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+  if (p.dbg_version && tid == 0) {
+    p.dbg_version[4 * t + 0] = v.r;
+    p.dbg_version[4 * t + 1] = v.m;
+    p.dbg_version[4 * t + 2] = v.cvis;
+    p.dbg_version[4 * t + 3] = (int)v.open_lo;
+  }
+  const int room = p.budget - base_len;
+  if (room <= 0 || v.cvis == 0) {
+    if (tid == 0) {
+      p.cand_len[t] = base_len;
+      if (p.dbg_n_order) p.dbg_n_order[t] = 0;
+    }
+    return;
+  }
+
+  // composites and sizes of the visible slots; empty slots get key 0
+  const float* srep = p.srep + (size_t)t * p.srep_ld;
+  int alive_total = 0;
+  for (int s = tid; s < slot_pow2; s += bd) {
+    uint64_t c = 0;
+    int sz = 0;
+    if (s < v.cvis) {
+      sz = (s < v.split ? ep.size : p.seal.size)[s];
+      if (sz > 0) c = make_comp(srep[s], (uint32_t)s);
+    }
+    comp[s] = c;
+    wt[s] = sz;
+    alive_total += sz;
+  }
+  int total;
+  block_exclusive_scan(alive_total, wtmp, &total);
+  const uint64_t thr = (total <= room) ? 1ull : radix_select_desc(comp, wt, v.cvis, room, sc);
+
+  // stable in-place compaction of the selected clusters (comp >= thr, nonzero)
+  if (tid == 0) s_nsel = 0;
+  __syncthreads();
+  for (int b0 = 0; b0 < v.cvis; b0 += bd) {
+    const int i = b0 + tid;
+    const uint64_t c = i < v.cvis ? comp[i] : 0ull;
+    const int flag = (c != 0 && c >= thr) ? 1 : 0;
+    int tot;
+    const int ex = block_exclusive_scan(flag, wtmp, &tot);
+    const int base = s_nsel;
+    __syncthreads();
+    if (flag) comp[base + ex] = c;
+    __syncthreads();
+    if (tid == 0) s_nsel = base + tot;
+    __syncthreads();
+  }
+  const int nsel = s_nsel;
+  const int P2 = next_pow2(nsel);
+  for (int i = nsel + tid; i < P2; i += bd) comp[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc(comp, P2);
+
+  // prefix sums of member counts in rank order
+  int chunk_base = 0;
+  for (int b0 = 0; b0 < nsel; b0 += bd) {
+    const int i = b0 + tid;
+    int sz = 0;
+    if (i < nsel) {
+      const int s = (int)comp_id(comp[i]);
+      sz = (s < v.split ? ep.size : p.seal.size)[s];
+    }
+    int tot;
+    const int ex = block_exclusive_scan(sz, wtmp, &tot);
+    if (i < nsel) wt[i] = chunk_base + ex;
+    chunk_base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) s_total = chunk_base;
+  __syncthreads();
+  const int used = min(room, s_total);
+
+  // fill: candidate c -> cluster i with wt[i] <= c < wt[i+1]
+  for (int c = tid; c < used; c += bd) {
+    int lo = 0, hi = nsel - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (wt[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int s = (int)comp_id(comp[lo]);
+    const bool from_epoch = s < v.split;
+    const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
+    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[off + (c - wt[lo])];
+  }
+  if (p.dbg_order) {
+    for (int i = tid; i < nsel && i < p.dbg_order_cap; i += bd) {
+      const int s = (int)comp_id(comp[i]);
+      const int sz = (s < v.split ? ep.size : p.seal.size)[s];
+      p.dbg_order[(size_t)t * p.dbg_order_cap + i] = s;
+      if (p.dbg_take) p.dbg_take[(size_t)t * p.dbg_order_cap + i] = min(sz, room - wt[i]);
+    }
+  }
+  if (tid == 0) {
+    p.cand_len[t] = base_len + used;
+    if (p.dbg_n_order) p.dbg_n_order[t] = nsel;
+  }
+}
+
+hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s) {
+  const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);
+  const size_t lds = (size_t)slot_pow2 * (sizeof(uint64_t) + sizeof(int));
+  hipError_t e = hipFuncSetAttribute((const void*)k_route_select, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_route_select, dim3(p.T), dim3(256), lds, s, p, slot_pow2);
+  return hipGetLastError();
+}
+
+}  // namespace ivftk

@@ -1,0 +1,562 @@
+// Host runtime behind the C ABI in include/ivftk.h: argument and state checks,
+// device memory owned by an index, version bookkeeping, streams and events.
+//
+// Index layout in device memory (all allocated at idx_create):
+//   keys [max_keys, d] in the key format, k_scale [max_keys] (E4M3);
+//   seal store, one entry per sealed-window cluster, slot s = w*C + c: size, offset,
+//     members (window w's keys at [w*W, (w+1)*W), grouped by cluster), fp32
+//     centroid, representative and its scale;
+//   three epoch stores (a ring: the published epoch, the one before it, and a refit
+//     in flight) with slots [0, r*Q), members [0, r*R), centroids, representatives,
+//     and the centroid drift of the epoch's update;
+//   per-key bound state (assigned slot, upper and lower distance bound) and the
+//     refit work list; per-tile slot counts for the stable member placement;
+//   routing scratch: representative scores [max_queries, slots] and candidate
+//     lists [max_queries, cand_cap].
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/ivftk.h"
+#include "launch.h"
+
+using namespace ivftk;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int elem_bytes(int dt) { return dt == IDX_F32 ? 4 : (dt == IDX_BF16 ? 2 : 1); }
+
+bool dim_supported(int dt, int d) {
+  if (dt == IDX_F32) return d == 32 || d == 64 || d == 128;
+  if (dt == IDX_BF16 || dt == IDX_E4M3) return d == 64 || d == 128;
+  return false;
+}
+
+int head_tiles(int H) { return H <= 32 ? 1 : (H <= 64 ? 2 : 4); }
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+struct EpochStore {
+  int* size = nullptr;
+  int* off = nullptr;
+  int* members = nullptr;
+  float* cent = nullptr;
+  uint8_t* rep = nullptr;
+  float* rsc = nullptr;
+  float* drift = nullptr;
+  float* drift_max = nullptr;
+};
+
+constexpr int TILE = 1024;
+constexpr size_t LDS_BYTES = 163840;
+
+}  // namespace
+
+struct idx_index {
+  idx_config cfg{};
+  int device = 0;
+  int Cs = 0, wpr = 0, Q = 0, RB = 0, HT = 1;
+  int64_t max_windows = 0, slot_cap = 0, member_cap = 0;
+  int64_t ep_slot_cap = 0, ep_member_cap = 0;
+  int cand_cap = 0;
+  int n_tiles_cap = 0;
+  uint8_t* keys = nullptr;
+  float* kscale = nullptr;
+  int *sl_size = nullptr, *sl_off = nullptr, *sl_members = nullptr;
+  float* sl_cent = nullptr;
+  uint8_t* sl_rep = nullptr;
+  float* sl_rsc = nullptr;
+  EpochStore ep[3];
+  int* assign = nullptr;
+  float* ub = nullptr;
+  float* lb = nullptr;
+  int* work = nullptr;
+  int* work_count = nullptr;
+  int* tile_cnt = nullptr;
+  float* srep = nullptr;
+  int* cand = nullptr;
+  int* cand_len = nullptr;
+  std::vector<void*> allocs;
+  int64_t bytes = 0;
+  int64_t n_keys = 0;
+  int sealed = 0;
+  int computed = 0;
+  int published = 0;
+  hipEvent_t ev_main = nullptr, ev_refit = nullptr;
+  bool poisoned = false;
+
+  template <typename T>
+  bool alloc(T** p, int64_t count) {
+    *p = nullptr;
+    if (count <= 0) return true;
+    void* v = nullptr;
+    const size_t b = (size_t)count * sizeof(T);
+    if (hipMalloc(&v, b) != hipSuccess) return false;
+    if (hipMemset(v, 0, b) != hipSuccess) return false;
+    allocs.push_back(v);
+    bytes += (int64_t)b;
+    *p = static_cast<T*>(v);
+    return true;
+  }
+
+  void release() {
+    for (void* p : allocs) (void)hipFree(p);
+    allocs.clear();
+    if (ev_main) (void)hipEventDestroy(ev_main);
+    if (ev_refit) (void)hipEventDestroy(ev_refit);
+    ev_main = ev_refit = nullptr;
+  }
+
+  StoreView seal_view() const { return StoreView{sl_size, sl_off, sl_members, sl_cent, sl_rep, sl_rsc}; }
+  StoreView epoch_view(int r) const {
+    if (r <= 0) return StoreView{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    const EpochStore& e = ep[r % 3];
+    return StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc};
+  }
+};
+
+namespace {
+
+int device_error(idx_index* ix, hipError_t e, const char* what) {
+  if (ix) ix->poisoned = true;
+  return fail(IDX_EDEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+int check_handle(const idx_index* ix) {
+  if (!ix) return fail(IDX_EINVAL, "null index handle");
+  if (ix->poisoned) return fail(IDX_ESTATE, "index handle is poisoned by an earlier device error");
+  return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* idx_last_error(void) { return g_err.c_str(); }
+
+int idx_create(const idx_config* cfg, idx_index** out) {
+  g_err.clear();
+  if (!cfg || !out) return fail(IDX_EINVAL, "null config or output pointer");
+  *out = nullptr;
+  const idx_config c = *cfg;
+  if (c.dtype < IDX_F32 || c.dtype > IDX_E4M3) return fail(IDX_EINVAL, "unknown dtype %d", c.dtype);
+  if (c.heads < 1 || c.heads > 128) return fail(IDX_EINVAL, "heads must be 1..128 (got %d)", c.heads);
+  if (!dim_supported(c.dtype, c.dim)) return fail(IDX_ENOTIMPL, "dim %d not built for dtype %d", c.dim, c.dtype);
+  if (c.n_sink < 0) return fail(IDX_EINVAL, "n_sink must be >= 0");
+  if (c.window < 2 || c.window > 1024) return fail(IDX_EINVAL, "window must be 2..1024");
+  if (c.cluster_size < 1 || c.window % c.cluster_size) return fail(IDX_EINVAL, "window must be a multiple of cluster_size");
+  const int Cs = c.window / c.cluster_size;
+  if (Cs != 1 && Cs != 2 && Cs != 4 && Cs != 8) return fail(IDX_ENOTIMPL, "clusters per window must be 1, 2, 4 or 8 (got %d)", Cs);
+  if ((int64_t)c.window * Cs > 8192) return fail(IDX_EINVAL, "window * clusters per window must be <= 8192");
+  if (c.seal_cap < 1 || (int64_t)c.seal_cap * Cs < c.window) return fail(IDX_EINVAL, "seal_cap * clusters per window must be >= window");
+  if (c.seal_iters < 1 || c.seal_iters > 64) return fail(IDX_EINVAL, "seal_iters must be 1..64");
+  if (c.refit_every < 0 || (c.refit_every && c.refit_every % c.window)) return fail(IDX_EINVAL, "refit_every must be 0 or a multiple of window");
+  if (c.max_queries < 1) return fail(IDX_EINVAL, "max_queries must be >= 1");
+  if (c.max_k < 1 || c.max_k > 4096) return fail(IDX_EINVAL, "max_k must be 1..4096");
+  if (c.max_budget < c.max_k) return fail(IDX_EINVAL, "max_budget must be >= max_k");
+  if (c.max_keys < 1 || c.max_keys > (int64_t)1 << 30) return fail(IDX_EINVAL, "max_keys must be 1..2^30");
+
+  idx_index* ix = new (std::nothrow) idx_index();
+  if (!ix) return fail(IDX_ENOMEM, "host allocation failed");
+  ix->cfg = c;
+  (void)hipGetDevice(&ix->device);
+  ix->Cs = Cs;
+  ix->wpr = c.refit_every ? c.refit_every / c.window : 0;
+  ix->Q = ix->wpr * Cs;
+  ix->RB = c.dim * elem_bytes(c.dtype);
+  ix->HT = head_tiles(c.heads);
+  ix->max_windows = c.max_keys > c.n_sink ? (c.max_keys - c.n_sink) / c.window : 0;
+  ix->slot_cap = ix->max_windows * Cs;
+  ix->member_cap = ix->max_windows * c.window;
+  const int64_t max_refits = ix->wpr ? ix->max_windows / ix->wpr : 0;
+  ix->ep_slot_cap = max_refits * ix->Q;
+  ix->ep_member_cap = max_refits * ix->wpr * (int64_t)c.window;
+  ix->cand_cap = (int)round_up(std::max<int64_t>(c.max_budget, (int64_t)c.n_sink + c.window), 32);
+  ix->n_tiles_cap = (int)((ix->member_cap + TILE - 1) / TILE);
+  if (ix->slot_cap > 8192) {
+    delete ix;
+    return fail(IDX_ECAPACITY, "max_keys allows %lld clusters; at most 8192 are routed", (long long)(ix->slot_cap));
+  }
+  {
+    auto p2 = [](int64_t n) { int64_t p = 1; while (p < n) p <<= 1; return p; };
+    const int64_t lds = (p2(ix->cand_cap) + p2(c.max_k)) * 8 + 4096;
+    if (lds > (int64_t)LDS_BYTES) {
+      delete ix;
+      return fail(IDX_ECAPACITY, "max(budget, n_sink + window) and max_k do not fit one block's LDS");
+    }
+  }
+  bool ok = ix->alloc(&ix->keys, c.max_keys * ix->RB) &&
+            (c.dtype != IDX_E4M3 || ix->alloc(&ix->kscale, c.max_keys)) &&
+            ix->alloc(&ix->sl_size, ix->slot_cap) && ix->alloc(&ix->sl_off, ix->slot_cap) &&
+            ix->alloc(&ix->sl_members, ix->member_cap) && ix->alloc(&ix->sl_cent, ix->slot_cap * c.dim) &&
+            ix->alloc(&ix->sl_rep, ix->slot_cap * ix->RB) && ix->alloc(&ix->sl_rsc, ix->slot_cap) &&
+            ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
+            ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
+            ix->alloc(&ix->cand_len, c.max_queries);
+  if (ok && ix->wpr) {
+    for (int i = 0; i < 3 && ok; ++i) {
+      EpochStore& e = ix->ep[i];
+      ok = ix->alloc(&e.size, ix->ep_slot_cap) && ix->alloc(&e.off, ix->ep_slot_cap) &&
+           ix->alloc(&e.members, ix->ep_member_cap) && ix->alloc(&e.cent, ix->ep_slot_cap * c.dim) &&
+           ix->alloc(&e.rep, ix->ep_slot_cap * ix->RB) && ix->alloc(&e.rsc, ix->ep_slot_cap) &&
+           ix->alloc(&e.drift, ix->ep_slot_cap) && ix->alloc(&e.drift_max, 1);
+    }
+    ok = ok && ix->alloc(&ix->assign, c.max_keys) && ix->alloc(&ix->ub, c.max_keys) &&
+         ix->alloc(&ix->lb, c.max_keys) && ix->alloc(&ix->work, c.max_keys) && ix->alloc(&ix->work_count, 1) &&
+         ix->alloc(&ix->tile_cnt, (int64_t)ix->n_tiles_cap * std::max<int64_t>(ix->ep_slot_cap, 1));
+  }
+  if (!ok) {
+    ix->release();
+    delete ix;
+    return fail(IDX_ENOMEM, "device allocation failed");
+  }
+  if (hipEventCreateWithFlags(&ix->ev_main, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&ix->ev_refit, hipEventDisableTiming) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    ix->release();
+    delete ix;
+    return fail(IDX_EDEVICE, "event creation failed");
+  }
+  *out = ix;
+  return IDX_OK;
+}
+
+int idx_destroy(idx_index* ix) {
+  g_err.clear();
+  if (!ix) return IDX_OK;
+  (void)hipSetDevice(ix->device);
+  (void)hipDeviceSynchronize();
+  ix->release();
+  delete ix;
+  return IDX_OK;
+}
+
+int idx_get_info(const idx_index* ix, idx_info* out) {
+  g_err.clear();
+  if (!ix || !out) return fail(IDX_EINVAL, "null argument");
+  out->n_keys = ix->n_keys;
+  out->sealed_windows = ix->sealed;
+  out->computed_epoch = ix->computed;
+  out->published_epoch = ix->published;
+  out->clusters_per_window = ix->Cs;
+  out->slots_per_epoch = ix->Q;
+  out->device_bytes = ix->bytes;
+  return IDX_OK;
+}
+
+int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_t n, void* stream) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  const idx_config& c = ix->cfg;
+  if (n < 0) return fail(IDX_EINVAL, "n must be >= 0");
+  if (n == 0) return IDX_OK;
+  if (!keys) return fail(IDX_EINVAL, "null keys");
+  if (c.dtype == IDX_E4M3 && !k_scale) return fail(IDX_EINVAL, "E4M3 keys need k_scale");
+  if (ix->n_keys + n > c.max_keys)
+    return fail(IDX_ECAPACITY, "inserting %lld keys after %lld exceeds max_keys %lld", (long long)n,
+                (long long)ix->n_keys, (long long)c.max_keys);
+  (void)hipSetDevice(ix->device);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = hipMemcpyAsync(ix->keys + (size_t)ix->n_keys * ix->RB, keys, (size_t)n * ix->RB,
+                                hipMemcpyDefault, s);
+  if (e == hipSuccess && c.dtype == IDX_E4M3)
+    e = hipMemcpyAsync(ix->kscale + ix->n_keys, k_scale, (size_t)n * sizeof(float), hipMemcpyDefault, s);
+  if (e != hipSuccess) return device_error(ix, e, "key copy");
+  ix->n_keys += n;
+  const int64_t full = ix->n_keys > c.n_sink ? (ix->n_keys - c.n_sink) / c.window : 0;
+  const int new_windows = (int)(full - ix->sealed);
+  if (new_windows > 0) {
+    SealParams p{};
+    p.keys = ix->keys;
+    p.kscale = ix->kscale;
+    p.S = c.n_sink;
+    p.W = c.window;
+    p.Cs = ix->Cs;
+    p.cap = c.seal_cap;
+    p.iters = c.seal_iters;
+    p.w0 = ix->sealed;
+    p.size = ix->sl_size;
+    p.off = ix->sl_off;
+    p.members = ix->sl_members;
+    p.cent = ix->sl_cent;
+    p.rep = ix->sl_rep;
+    p.rsc = ix->sl_rsc;
+    e = launch_seal(p, c.dtype, c.dim, new_windows, s);
+    if (e != hipSuccess) return device_error(ix, e, "seal launch");
+    ix->sealed = (int)full;
+  }
+  return IDX_OK;
+}
+
+int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (launched) *launched = 0;
+  const idx_config& c = ix->cfg;
+  if (!ix->wpr) return IDX_OK;
+  if (ix->computed != ix->published) return IDX_OK;               // previous refit not published yet
+  const int r = ix->computed + 1;
+  if (ix->sealed < r * ix->wpr) return IDX_OK;                      // boundary not sealed past
+  (void)hipSetDevice(ix->device);
+  hipStream_t s = (hipStream_t)stream, side = (hipStream_t)side_stream;
+  hipError_t e = hipEventRecord(ix->ev_main, s);
+  if (e == hipSuccess) e = hipStreamWaitEvent(side, ix->ev_main, 0);
+  if (e != hipSuccess) return device_error(ix, e, "refit stream ordering");
+  RefitParams p{};
+  p.keys = ix->keys;
+  p.kscale = ix->kscale;
+  p.n_keys = ix->n_keys;
+  p.S = c.n_sink;
+  p.r = r;
+  p.Q = ix->Q;
+  p.B_prev = (int64_t)c.n_sink + (int64_t)(r - 1) * c.refit_every;
+  p.B_r = (int64_t)c.n_sink + (int64_t)r * c.refit_every;
+  const StoreView pv = ix->epoch_view(r - 1);
+  p.prev = pv;
+  p.prev_drift = r >= 2 ? ix->ep[(r - 1) % 3].drift : nullptr;
+  p.prev_drift_max = r >= 2 ? ix->ep[(r - 1) % 3].drift_max : nullptr;
+  p.seal = ix->seal_view();
+  p.assign = ix->assign;
+  p.ub = ix->ub;
+  p.lb = ix->lb;
+  p.work = ix->work;
+  p.work_count = ix->work_count;
+  EpochStore& out = ix->ep[r % 3];
+  p.size = out.size;
+  p.off = out.off;
+  p.members = out.members;
+  p.cent = out.cent;
+  p.rep = out.rep;
+  p.rsc = out.rsc;
+  p.drift = out.drift;
+  p.drift_max = out.drift_max;
+  p.tile_cnt = ix->tile_cnt;
+  p.tile = TILE;
+  p.n_tiles = (int)((p.B_r - p.S + TILE - 1) / TILE);
+  e = launch_refit(p, c.dtype, c.dim, side);
+  if (e == hipSuccess) e = hipEventRecord(ix->ev_refit, side);
+  if (e != hipSuccess) return device_error(ix, e, "refit launch");
+  ix->computed = r;
+  if (launched) *launched = 1;
+  return IDX_OK;
+}
+
+int idx_publish(idx_index* ix, void* stream, int32_t* published) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (ix->computed > ix->published) {
+    (void)hipSetDevice(ix->device);
+    hipError_t e = hipStreamWaitEvent((hipStream_t)stream, ix->ev_refit, 0);
+    if (e != hipSuccess) return device_error(ix, e, "publish wait");
+    ix->published = ix->computed;
+  }
+  if (published) *published = ix->published;
+  return IDX_OK;
+}
+
+int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
+                   int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score, const idx_route_debug* dbg,
+                   void* stream) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  const idx_config& c = ix->cfg;
+  if (!q || !w || !topk_idx) return fail(IDX_EINVAL, "null q, w or topk_idx");
+  if (c.dtype == IDX_E4M3 && !q_scale) return fail(IDX_EINVAL, "E4M3 queries need q_scale");
+  if (T < 1) return fail(IDX_EINVAL, "T must be >= 1");
+  if (T > c.max_queries) return fail(IDX_ECAPACITY, "T %d exceeds max_queries %d", T, c.max_queries);
+  if (k < 1 || k > c.max_k) return fail(IDX_ECAPACITY, "k %d outside 1..max_k %d", k, c.max_k);
+  if (budget < k) return fail(IDX_EINVAL, "budget %d < k %d", budget, k);
+  if (budget > c.max_budget) return fail(IDX_ECAPACITY, "budget %d exceeds max_budget %d", budget, c.max_budget);
+  if (q_pos0 < 0) return fail(IDX_EINVAL, "q_pos0 must be >= 0");
+  if (q_pos0 + T > ix->n_keys)
+    return fail(IDX_ECAUSAL, "query position %lld has no inserted key (%lld keys)", (long long)(q_pos0 + T - 1),
+                (long long)ix->n_keys);
+  const int P = ix->published;
+  auto windows_in = [&](int64_t n) -> int {
+    return n >= c.n_sink ? (int)((n - c.n_sink) / c.window) : 0;
+  };
+  if (ix->wpr) {
+    // epochs used by this call: r_t = min(P, m_t / wpr) grows by at most one per window,
+    // so every epoch between the first and the last query's is used; each must still
+    // be held (the ring keeps three stores and a refit in flight overwrites the oldest)
+    const int r0 = std::min(P, windows_in(q_pos0 + 1) / ix->wpr);
+    const int r1 = std::min(P, windows_in(q_pos0 + T) / ix->wpr);
+    const int oldest = std::max(1, ix->computed - 2);
+    const int lo = std::max(r0, 1);
+    if (r1 >= 1 && lo < oldest)
+      return fail(IDX_ESTATE, "queries at %lld..%lld need epoch %d; epochs below %d are no longer held",
+                  (long long)q_pos0, (long long)(q_pos0 + T - 1), lo, oldest);
+  }
+  (void)hipSetDevice(ix->device);
+  hipStream_t s = (hipStream_t)stream;
+  RouteParams p{};
+  p.keys = ix->keys;
+  p.kscale = ix->kscale;
+  p.q = static_cast<const uint8_t*>(q);
+  p.qscale = c.dtype == IDX_E4M3 ? q_scale : nullptr;
+  p.w = w;
+  p.n_keys = ix->n_keys;
+  p.H = c.heads;
+  p.T = T;
+  p.q_pos0 = q_pos0;
+  p.k = k;
+  p.budget = budget;
+  p.S = c.n_sink;
+  p.W = c.window;
+  p.Cs = ix->Cs;
+  p.wpr = ix->wpr;
+  p.P = P;
+  for (int i = 0; i < 3; ++i) {
+    const EpochStore& e = ix->ep[i];
+    p.ep[i] = StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc};
+  }
+  p.seal = ix->seal_view();
+  p.srep = ix->srep;
+  p.srep_ld = std::max<int64_t>(ix->slot_cap, 1);
+  p.cand = ix->cand;
+  p.cand_ld = ix->cand_cap;
+  p.cand_len = ix->cand_len;
+  p.topk_idx = topk_idx;
+  p.topk_score = topk_score;
+  if (dbg) {
+    p.dbg_order = dbg->order;
+    p.dbg_take = dbg->order_take;
+    p.dbg_order_cap = dbg->order_cap;
+    p.dbg_n_order = dbg->n_order;
+    p.dbg_version = dbg->version;
+  }
+  const int max_slots = windows_in(q_pos0 + T) * ix->Cs;
+  hipError_t e = hipSuccess;
+  if (max_slots > 0) e = launch_rep_score(p, c.dtype, c.dim, ix->HT, max_slots, s);
+  if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
+  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
+  if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
+  if (e != hipSuccess) return device_error(ix, e, "route launch");
+  if (dbg) {
+    if (dbg->cand && dbg->cand_cap > 0) {
+      const size_t wcols = (size_t)std::min(dbg->cand_cap, ix->cand_cap);
+      e = hipMemcpy2DAsync(dbg->cand, (size_t)dbg->cand_cap * 4, ix->cand, (size_t)ix->cand_cap * 4, wcols * 4, T,
+                           hipMemcpyDeviceToDevice, s);
+    }
+    if (e == hipSuccess && dbg->cand_len)
+      e = hipMemcpyAsync(dbg->cand_len, ix->cand_len, (size_t)T * 4, hipMemcpyDeviceToDevice, s);
+    if (e == hipSuccess && dbg->rep_scores && dbg->rep_cap > 0 && max_slots > 0) {
+      const size_t wcols = (size_t)std::min<int64_t>(dbg->rep_cap, p.srep_ld);
+      e = hipMemcpy2DAsync(dbg->rep_scores, (size_t)dbg->rep_cap * 4, ix->srep, (size_t)p.srep_ld * 4, wcols * 4, T,
+                           hipMemcpyDeviceToDevice, s);
+    }
+    if (e != hipSuccess) return device_error(ix, e, "route debug copy");
+  }
+  return IDX_OK;
+}
+
+int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T) {
+  if (n_keys < 1 || T < 1) return 0;
+  return (int64_t)T * round_up(n_keys, 64) * (int64_t)sizeof(float);
+}
+
+int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
+                        int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
+                        int32_t k, int32_t* topk_idx, float* topk_score, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+  g_err.clear();
+  if (dtype < IDX_F32 || dtype > IDX_E4M3) return fail(IDX_EINVAL, "unknown dtype %d", dtype);
+  if (heads < 1 || heads > 128) return fail(IDX_EINVAL, "heads must be 1..128");
+  if (!dim_supported(dtype, dim)) return fail(IDX_ENOTIMPL, "dim %d not built for dtype %d", dim, dtype);
+  if (!keys || !q || !w || !topk_idx || !workspace) return fail(IDX_EINVAL, "null pointer argument");
+  if (dtype == IDX_E4M3 && (!k_scale || !q_scale)) return fail(IDX_EINVAL, "E4M3 needs k_scale and q_scale");
+  if (T < 1) return fail(IDX_EINVAL, "T must be >= 1");
+  if (k < 1 || k > 4096) return fail(IDX_EINVAL, "k must be 1..4096");
+  if (q_pos0 < 0) return fail(IDX_EINVAL, "q_pos0 must be >= 0");
+  if (q_pos0 + T > n_keys) return fail(IDX_ECAUSAL, "query position beyond n_keys");
+  const int64_t n_max = q_pos0 + T;
+  const int64_t ld = round_up(n_max, 64);
+  const int64_t per_query = ld * (int64_t)sizeof(float);
+  if (workspace_bytes < per_query) return fail(IDX_EINVAL, "workspace too small: %lld bytes, need >= %lld",
+                                               (long long)workspace_bytes, (long long)per_query);
+  const int Tb_max = (int)std::min<int64_t>(T, workspace_bytes / per_query);
+  hipStream_t s = (hipStream_t)stream;
+  for (int t0 = 0; t0 < T; t0 += Tb_max) {
+    ExhParams p{};
+    p.keys = static_cast<const uint8_t*>(keys);
+    p.kscale = dtype == IDX_E4M3 ? k_scale : nullptr;
+    p.q = static_cast<const uint8_t*>(q);
+    p.qscale = dtype == IDX_E4M3 ? q_scale : nullptr;
+    p.w = w;
+    p.H = heads;
+    p.q_pos0 = q_pos0;
+    p.t0 = t0;
+    p.Tb = std::min(Tb_max, T - t0);
+    p.ws = static_cast<float*>(workspace);
+    p.ld = ld;
+    p.kchunk = 8192;
+    p.k = k;
+    p.topk_idx = topk_idx;
+    p.topk_score = topk_score;
+    const int64_t n_batch = q_pos0 + t0 + p.Tb;
+    hipError_t e = launch_exh_score(p, dtype, dim, head_tiles(heads), n_batch, s);
+    if (e == hipSuccess) e = launch_topk_rows(p, s);
+    if (e != hipSuccess) return fail(IDX_EDEVICE, "exhaustive launch: %s", hipGetErrorString(e));
+  }
+  return IDX_OK;
+}
+
+int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (!buf) return fail(IDX_EINVAL, "null export buffer");
+  const idx_config& c = ix->cfg;
+  const int *size, *off, *members;
+  const float *cent, *rsc;
+  const uint8_t* rep;
+  int64_t n_slots, n_members;
+  if (which == -1) {
+    n_slots = (int64_t)ix->sealed * ix->Cs;
+    n_members = (int64_t)ix->sealed * c.window;
+    size = ix->sl_size; off = ix->sl_off; members = ix->sl_members;
+    cent = ix->sl_cent; rep = ix->sl_rep; rsc = ix->sl_rsc;
+  } else {
+    if (which < 1 || which > ix->computed || which <= ix->computed - 3)
+      return fail(IDX_ESTATE, "epoch %d is not held (computed %d)", which, ix->computed);
+    n_slots = (int64_t)which * ix->Q;
+    n_members = (int64_t)which * ix->wpr * c.window;
+    const EpochStore& e = ix->ep[which % 3];
+    size = e.size; off = e.off; members = e.members; cent = e.cent; rep = e.rep; rsc = e.rsc;
+  }
+  buf->n_slots = (int32_t)n_slots;
+  buf->n_members = (int32_t)n_members;
+  (void)hipSetDevice(ix->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return device_error(ix, e, "export wait");
+  auto cp = [&](void* dst, const void* src, size_t bytes) {
+    if (dst && bytes && e == hipSuccess) e = hipMemcpy(dst, src, bytes, hipMemcpyDeviceToHost);
+  };
+  cp(buf->sizes, size, (size_t)n_slots * 4);
+  cp(buf->offsets, off, (size_t)n_slots * 4);
+  cp(buf->members, members, (size_t)n_members * 4);
+  cp(buf->centroids, cent, (size_t)n_slots * c.dim * 4);
+  cp(buf->reps, rep, (size_t)n_slots * ix->RB);
+  cp(buf->rep_scale, rsc, (size_t)n_slots * 4);
+  if (e != hipSuccess) return device_error(ix, e, "export copy");
+  return IDX_OK;
+}
+
+}  // extern "C"

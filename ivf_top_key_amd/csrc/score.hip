@@ -1,0 +1,355 @@
+// Indexer scoring kernels: exhaustive scores, representative scores, candidate
+// rescoring with the top-k selection, and the top-k of exhaustive score rows.
+//
+// Score (AttentionIndex, paper-daily.com explainer, "它到底在解决什么问题？"):
+//   s(t, j) = sum_h w[t,h] * ReLU(q[t,h] . k[j]); with E4M3, the per-(t,h) query
+//   scale folds into the head weight and the per-key scale multiplies the sum.
+// Every path evaluates s through score_tile (dev.h), so one (query, key) pair gets
+// the same fp32 bits on the exhaustive and the routed path.
+#include "dispatch.h"
+#include "launch.h"
+#include "params.h"
+
+namespace ivftk {
+
+// ---------------------------------------------------------------------------
+// exhaustive scores: block = 4 waves = 4 queries, one chunk of keys
+// ---------------------------------------------------------------------------
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
+  using G = Geo<DT, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+  const int tl = blockIdx.x * 4 + wave;
+  if (tl >= p.Tb) return;
+  const int t = p.t0 + tl;
+  const int64_t n = p.q_pos0 + t + 1;
+  const int64_t j0 = (int64_t)blockIdx.y * p.kchunk;
+  const int64_t j1 = (j0 + p.kchunk < n) ? j0 + p.kchunk : n;
+  if (j0 >= j1) return;
+  QueryFrag<DT, D, HT> f;
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
+                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  float* out = p.ws + (size_t)tl * p.ld;
+  uint32_t ba[G::HW], bb[G::HW];
+  for (int64_t jb = j0; jb < j1; jb += 64) {
+    const int64_t ja = jb + col, jbb = jb + 32 + col;
+    const int64_t ca = ja < j1 ? ja : j1 - 1;
+    const int64_t cb = jbb < j1 ? jbb : j1 - 1;
+    load_half_row<DT, D>(ba, p.keys + (size_t)ca * G::RB);
+    load_half_row<DT, D>(bb, p.keys + (size_t)cb * G::RB);
+    float sa = score_tile<DT, D, HT>(f, ba);
+    if constexpr (DT == DT_E4M3) sa *= p.kscale[ca];
+    if (lane < 32 && ja < j1) out[ja] = sa;
+    if (jb + 32 < j1) {
+      float sb = score_tile<DT, D, HT>(f, bb);
+      if constexpr (DT == DT_E4M3) sb *= p.kscale[cb];
+      if (lane < 32 && jbb < j1) out[jbb] = sb;
+    }
+  }
+}
+
+template <int DT, int D, int HT>
+static hipError_t launch_exh_score_t(const ExhParams& p, int64_t n_max, hipStream_t s) {
+  dim3 grid((p.Tb + 3) / 4, (unsigned)((n_max + p.kchunk - 1) / p.kchunk));
+  hipLaunchKernelGGL((k_exh_score<DT, D, HT>), grid, dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_exh_score(const ExhParams& p, int dtype, int dim, int ht, int64_t n_max, hipStream_t s) {
+  IVFTK_DISPATCH(launch_exh_score_t, dtype, dim, ht, p, n_max, s);
+}
+
+// ---------------------------------------------------------------------------
+// top-k of one exhaustive score row per block
+// ---------------------------------------------------------------------------
+constexpr int ROW_CAP = 8192;   // composites held in LDS
+
+// Digit search over a histogram in descending digit order: finds d with
+// count(> d) < need <= count(>= d).  All threads call; results in shared vars.
+__device__ inline void block_find_digit(const int* hist, int nbins, int need, int* wtmp, int* o_digit,
+                                        int* o_above, int* o_in) {
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int per = (nbins + bd - 1) / bd;
+  int s = 0;
+  for (int q = 0; q < per; ++q) {
+    const int d = nbins - 1 - tid * per - q;
+    if (d >= 0) s += hist[d];
+  }
+  int tot;
+  const int excl = block_exclusive_scan(s, wtmp, &tot);
+  if (excl < need && need <= excl + s) {
+    int acc = excl;
+    for (int q = 0; q < per; ++q) {
+      const int d = nbins - 1 - tid * per - q;
+      if (d < 0) break;
+      if (acc + hist[d] >= need) {
+        *o_digit = d;
+        *o_above = acc;
+        *o_in = hist[d];
+        break;
+      }
+      acc += hist[d];
+    }
+  }
+  __syncthreads();
+}
+
+__device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const uint64_t v = i < avail ? buf[i] : 0ull;
+    oi[i] = v ? (int)comp_id(v) : -1;
+    if (os) os[i] = v ? comp_score(v) : -__builtin_inff();
+  }
+}
+
+__global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
+  __shared__ uint64_t buf[ROW_CAP];
+  __shared__ int hist[4096];
+  __shared__ int wtmp[16];
+  __shared__ int s_cnt, s_digit, s_above, s_in, s_taken;
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int tl = blockIdx.x, t = p.t0 + tl;
+  const int64_t n = p.q_pos0 + t + 1;
+  const float* row = p.ws + (size_t)tl * p.ld;
+  const int K = p.k;
+  int* oi = p.topk_idx + (size_t)t * K;
+  float* os = p.topk_score ? p.topk_score + (size_t)t * K : nullptr;
+
+  if (n <= ROW_CAP) {
+    const int P2 = next_pow2((int)n);
+    for (int i = tid; i < P2; i += bd) buf[i] = i < n ? make_comp(row[i], (uint32_t)i) : 0ull;
+    __syncthreads();
+    bitonic_sort_desc(buf, P2);
+    write_topk(buf, P2, K, oi, os);
+    return;
+  }
+  // pass 1: top 12 bits of the order key
+  for (int i = tid; i < 4096; i += bd) hist[i] = 0;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  for (int64_t j = tid; j < n; j += bd) atomicAdd(&hist[order_bits(row[j]) >> 20], 1);
+  __syncthreads();
+  block_find_digit(hist, 4096, K, wtmp, &s_digit, &s_above, &s_in);
+  const uint32_t d1 = (uint32_t)s_digit;
+  int above = s_above;
+  if (above + s_in <= ROW_CAP) {
+    for (int64_t j = tid; j < n; j += bd) {
+      const float v = row[j];
+      if ((order_bits(v) >> 20) >= d1) buf[atomicAdd(&s_cnt, 1)] = make_comp(v, (uint32_t)j);
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    const int P2 = next_pow2(cnt);
+    for (int i = cnt + tid; i < P2; i += bd) buf[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(buf, P2);
+    write_topk(buf, P2, K, oi, os);
+    return;
+  }
+  // pass 2: next 12 bits inside bin d1
+  __syncthreads();
+  for (int i = tid; i < 4096; i += bd) hist[i] = 0;
+  __syncthreads();
+  for (int64_t j = tid; j < n; j += bd) {
+    const uint32_t o = order_bits(row[j]);
+    if ((o >> 20) == d1) atomicAdd(&hist[(o >> 8) & 0xFFFu], 1);
+  }
+  __syncthreads();
+  block_find_digit(hist, 4096, K - above, wtmp, &s_digit, &s_above, &s_in);
+  const uint32_t p2 = (d1 << 12) | (uint32_t)s_digit;
+  above += s_above;
+  if (above + s_in <= ROW_CAP) {
+    for (int64_t j = tid; j < n; j += bd) {
+      const float v = row[j];
+      if ((order_bits(v) >> 8) >= p2) buf[atomicAdd(&s_cnt, 1)] = make_comp(v, (uint32_t)j);
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    const int P2 = next_pow2(cnt);
+    for (int i = cnt + tid; i < P2; i += bd) buf[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(buf, P2);
+    write_topk(buf, P2, K, oi, os);
+    return;
+  }
+  // pass 3: last 8 bits -> exact threshold key; then ties by position
+  __syncthreads();
+  for (int i = tid; i < 256; i += bd) hist[i] = 0;
+  __syncthreads();
+  for (int64_t j = tid; j < n; j += bd) {
+    const uint32_t o = order_bits(row[j]);
+    if ((o >> 8) == p2) atomicAdd(&hist[o & 0xFFu], 1);
+  }
+  __syncthreads();
+  block_find_digit(hist, 256, K - above, wtmp, &s_digit, &s_above, &s_in);
+  const uint32_t thr = (p2 << 8) | (uint32_t)s_digit;
+  above += s_above;   // keys strictly above thr: fewer than K
+  for (int64_t j = tid; j < n; j += bd) {
+    const float v = row[j];
+    if (order_bits(v) > thr) buf[atomicAdd(&s_cnt, 1)] = make_comp(v, (uint32_t)j);
+  }
+  if (tid == 0) s_taken = 0;
+  __syncthreads();
+  const int need_eq = K - above;
+  for (int64_t base = 0; base < n; base += bd) {
+    const int taken = s_taken;
+    if (taken >= need_eq) break;
+    const int64_t j = base + tid;
+    const float v = j < n ? row[j] : 0.0f;
+    const int flag = (j < n && order_bits(v) == thr) ? 1 : 0;
+    int tot;
+    const int ex = block_exclusive_scan(flag, wtmp, &tot);
+    if (flag && taken + ex < need_eq) buf[above + taken + ex] = make_comp(v, (uint32_t)j);
+    __syncthreads();
+    if (tid == 0) s_taken = taken + tot;
+    __syncthreads();
+  }
+  const int P2 = next_pow2(K);
+  for (int i = K + tid; i < P2; i += bd) buf[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc(buf, P2);
+  write_topk(buf, P2, K, oi, os);
+}
+
+hipError_t launch_topk_rows(const ExhParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_topk_rows, dim3(p.Tb), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// query version (routed path)
+// ---------------------------------------------------------------------------
+struct QVer {
+  int64_t n;       // prefix length
+  int m;           // sealed windows inside the prefix
+  int r;           // refit epoch used
+  int split;       // slots below come from the epoch store
+  int cvis;        // visible slots [0, cvis)
+  int64_t open_lo; // open window [open_lo, n)
+};
+
+__device__ __forceinline__ QVer query_version(const RouteParams& p, int t) {
+  QVer v;
+  v.n = p.q_pos0 + t + 1;
+  v.m = v.n >= p.S ? (int)((v.n - p.S) / p.W) : 0;
+  v.r = p.wpr ? min(p.P, v.m / p.wpr) : 0;
+  v.split = v.r * p.wpr * p.Cs;
+  v.cvis = v.m * p.Cs;
+  v.open_lo = (int64_t)p.S + (int64_t)v.m * p.W;
+  return v;
+}
+
+__device__ __forceinline__ StoreView epoch_store(const RouteParams& p, int r) { return p.ep[r % 3]; }
+
+// ---------------------------------------------------------------------------
+// representative scores: block = 4 queries, one chunk of slots
+// ---------------------------------------------------------------------------
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
+  using G = Geo<DT, D>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= p.T) return;
+  const QVer v = query_version(p, t);
+  const int s0 = blockIdx.y * chunk;
+  const int s1 = min(v.cvis, s0 + chunk);
+  if (s0 >= s1) return;
+  const StoreView ep = epoch_store(p, v.r);
+  QueryFrag<DT, D, HT> f;
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
+                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  float* out = p.srep + (size_t)t * p.srep_ld;
+  uint32_t b[G::HW];
+  for (int sb = s0; sb < s1; sb += 32) {
+    const int s = sb + col;
+    const int sc = s < s1 ? s : s1 - 1;
+    const bool from_epoch = sc < v.split;
+    const uint8_t* rep = from_epoch ? ep.rep : p.seal.rep;
+    load_half_row<DT, D>(b, rep + (size_t)sc * G::RB);
+    float x = score_tile<DT, D, HT>(f, b);
+    if constexpr (DT == DT_E4M3) x *= (from_epoch ? ep.rsc : p.seal.rsc)[sc];
+    if (lane < 32 && s < s1) out[s] = x;
+  }
+}
+
+template <int DT, int D, int HT>
+static hipError_t launch_rep_score_t(const RouteParams& p, int max_slots, hipStream_t s) {
+  const int chunk = 1024;
+  dim3 grid((p.T + 3) / 4, (max_slots + chunk - 1) / chunk);
+  hipLaunchKernelGGL((k_rep_score<DT, D, HT>), grid, dim3(256), 0, s, p, chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s) {
+  IVFTK_DISPATCH(launch_rep_score_t, dtype, dim, ht, p, max_slots, s);
+}
+
+// ---------------------------------------------------------------------------
+// candidate rescoring + top-k: one block per query
+// ---------------------------------------------------------------------------
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(512) void k_rescore_topk(RouteParams p, int cap_pow2, int k_pow2) {
+  using G = Geo<DT, D>;
+  extern __shared__ uint64_t lds[];
+  uint64_t* buf = lds;               // [cap_pow2]
+  uint64_t* sel = lds + cap_pow2;    // [k_pow2]
+  __shared__ SelectScratch sc;
+  __shared__ int s_cnt;
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
+  const int t = blockIdx.x;
+  const int L = p.cand_len[t];
+  const int* cand = p.cand + (size_t)t * p.cand_ld;
+  const int K = p.k;
+  QueryFrag<DT, D, HT> f;
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
+                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  uint32_t b[G::HW];
+  for (int blk = wave; blk * 32 < L; blk += nw) {
+    const int i = blk * 32 + col;
+    int j = cand[i < L ? i : L - 1];
+    j = j < 0 ? 0 : (j >= p.n_keys ? (int)(p.n_keys - 1) : j);   // guard against corrupt lists
+    load_half_row<DT, D>(b, p.keys + (size_t)j * G::RB);
+    float x = score_tile<DT, D, HT>(f, b);
+    if constexpr (DT == DT_E4M3) x *= p.kscale[j];
+    if (lane < 32 && i < L) buf[i] = make_comp(x, (uint32_t)j);
+  }
+  const int P2 = next_pow2(L > 0 ? L : 1);
+  for (int i = L + tid; i < P2; i += bd) buf[i] = 0ull;
+  if (tid == 0) s_cnt = 0;
+  __syncthreads();
+  int* oi = p.topk_idx + (size_t)t * K;
+  float* os = p.topk_score ? p.topk_score + (size_t)t * K : nullptr;
+  if (L <= K) {
+    bitonic_sort_desc(buf, P2);
+    write_topk(buf, P2 < L ? P2 : L, K, oi, os);
+    return;
+  }
+  const uint64_t thr = radix_select_desc(buf, nullptr, L, K, sc);
+  for (int i = tid; i < L; i += bd) {
+    const uint64_t v = buf[i];
+    if (v >= thr) sel[atomicAdd(&s_cnt, 1)] = v;
+  }
+  for (int i = K + tid; i < k_pow2; i += bd) sel[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc(sel, k_pow2);
+  write_topk(sel, K, K, oi, os);
+}
+
+template <int DT, int D, int HT>
+static hipError_t launch_rescore_topk_t(const RouteParams& p, int cand_cap, hipStream_t s) {
+  const int cap_pow2 = next_pow2(cand_cap);
+  const int k_pow2 = next_pow2(p.k);
+  const size_t lds = (size_t)(cap_pow2 + k_pow2) * sizeof(uint64_t);
+  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT>), dim3(p.T), dim3(512), lds, s, p, cap_pow2, k_pow2);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s) {
+  IVFTK_DISPATCH(launch_rescore_topk_t, dtype, dim, ht, p, cand_cap, s);
+}
+
+}  // namespace ivftk

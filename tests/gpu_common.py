@@ -1,0 +1,158 @@
+"""Shared helpers of the GPU parity tests: inputs, building both sides, comparisons.
+
+Tolerances.  Scores are compared against the oracle's float64 scores relative to
+sigma(t, j) = sum_h |w| * sum_i |q_i k_i| (the error scale of any fp32
+evaluation).  The fp32 MFMA accumulation over d terms plus the fp32 sum over H
+heads is off by at most about (d + H) * 2^-24 * sigma = 1.2e-5 sigma for d=128,
+H=64, and 2.1e-6 sigma for d=32, H=4.  Tests assert 1e-5 sigma for fp32 (the
+stated bar) and 1e-4 sigma for bf16/E4M3 (tighter than the stated 2e-2), and
+treat two candidates whose oracle scores are within that tolerance of each
+other as a near tie, where either order is correct.
+"""
+from __future__ import annotations
+
+import os
+import sys
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import datagen  # noqa: E402
+from datagen.workloads import WORKLOADS  # noqa: E402
+from oracle import OracleConfig, OracleIndex, fill_budget  # noqa: E402
+from oracle.index import query_values, topk_sorted  # noqa: E402
+from oracle.score import indexer_scores, score_error_scale  # noqa: E402
+
+RTOL = {"f32": 1e-5, "bf16": 1e-4, "e4m3": 1e-4}
+CFG_KEYS = ("n_sink", "window", "cluster_size", "seal_cap", "seal_iters", "refit_every")
+
+
+def ensure_built():
+    from ivf_top_key_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from ivf_top_key_amd.build import build
+        build()
+
+
+def say(msg):
+    print(msg, flush=True)
+
+
+def workload(name, **over):
+    wl = dict(WORKLOADS[name], **over)
+    inp = datagen.workload_inputs(wl["seed"], wl["N"], wl["T"], wl["q_pos0"], wl["H"], wl["d"], wl["M"],
+                                  wl["dtype"])
+    return wl, inp
+
+
+def oracle_cfg(wl):
+    return OracleConfig(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], **{k: wl[k] for k in CFG_KEYS})
+
+
+def oracle_index(wl, inp, n_keys=None):
+    n = wl["N"] if n_keys is None else n_keys
+    ix = OracleIndex(oracle_cfg(wl))
+    ix.append(inp["keys"][:n], None if inp["k_scale"] is None else inp["k_scale"][:n])
+    while ix.refit_due():
+        ix.refit()
+        ix.publish()
+    return ix
+
+
+def to_dev(a, device="cuda"):
+    import torch
+    if a is None:
+        return None
+    return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+
+def gpu_index(wl, inp, n_keys=None, chunk=None, max_queries=None, max_budget=None, max_k=None):
+    """Insert keys (in chunks) and run every due refit, published at once."""
+    import ivf_top_key_amd as ivf
+    n = wl["N"] if n_keys is None else n_keys
+    ix = ivf.idx_create(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], max_keys=wl["N"],
+                        max_queries=max_queries or wl["T"], max_budget=max_budget or max(wl["budget"], wl["N"]),
+                        max_k=max_k or wl["k"], **{k: wl[k] for k in CFG_KEYS})
+    keys = to_dev(inp["keys"][:n])
+    ks = to_dev(inp["k_scale"][:n]) if inp["k_scale"] is not None else None
+    chunk = chunk or n
+    for a in range(0, n, chunk):
+        b = min(n, a + chunk)
+        ivf.idx_build_seal(ix, keys[a:b], None if ks is None else ks[a:b])
+        while ivf.idx_refit(ix):
+            ivf.idx_publish(ix)
+    return ix
+
+
+def compare_cluster_set(got, clusters, n_members_base, dtype, label):
+    """Bit-exact comparison of an exported cluster set with oracle clusters (slot order)."""
+    assert got["sizes"].shape[0] == len(clusters), label
+    for c in clusters:
+        s = c.slot
+        size = int(got["sizes"][s])
+        assert size == c.members.size, f"{label}: slot {s} size {size} vs oracle {c.members.size}"
+        if size:
+            off = int(got["offsets"][s])
+            mem = got["members"][off:off + size]
+            assert np.array_equal(mem, c.members), f"{label}: slot {s} members differ"
+            assert np.array_equal(got["centroids"][s].view(np.uint32), c.centroid.view(np.uint32)), \
+                f"{label}: slot {s} centroid bits differ (max abs diff " \
+                f"{np.abs(got['centroids'][s] - c.centroid).max():.3g})"
+            assert np.array_equal(got["reps"][s], c.rep_raw), f"{label}: slot {s} representative differs"
+            assert np.float32(got["rep_scale"][s]) == np.float32(c.rep_scale), f"{label}: slot {s} rep scale"
+
+
+def compare_seal_store(ivf, gix, oix, label):
+    got = ivf.idx_export(gix, -1)
+    clusters = [c for w in oix.seals for c in w]
+    compare_cluster_set(got, clusters, 0, oix.cfg.dtype, label + " seal")
+    return got
+
+
+def compare_epoch(ivf, gix, oix, r, label):
+    got = ivf.idx_export(gix, r)
+    compare_cluster_set(got, oix.epochs[r], 0, oix.cfg.dtype, f"{label} epoch {r}")
+    return got
+
+
+def check_scores(idx, sc, qv, w, kv, t, dtype, label):
+    """GPU scores of the returned positions against float64 within rtol * sigma."""
+    ok = idx >= 0
+    j = idx[ok]
+    ref = indexer_scores(qv[t:t + 1], w[t:t + 1], kv[j])[0]
+    sig = score_error_scale(qv[t:t + 1], w[t:t + 1], kv[j])[0]
+    err = np.abs(sc[ok].astype(np.float64) - ref)
+    bound = RTOL[dtype] * sig + 1e-30
+    assert np.all(err <= bound), f"{label}: score error {np.max(err / bound):.3g} x tolerance"
+    return float(np.max(err / np.maximum(sig, 1e-30))) if err.size else 0.0
+
+
+def topk_matches(got_idx, cand, qv, w, kv, t, k, dtype):
+    """True if got_idx is a correct top-k of `cand` up to near ties (oracle float64 scores).
+
+    Returns (ok, n_exempt): every position in the symmetric difference with the
+    oracle's top-k must score within the tolerance of the oracle's k-th score."""
+    cand = np.asarray(cand, dtype=np.int64)
+    s = indexer_scores(qv[t:t + 1], w[t:t + 1], kv[cand])[0]
+    sig = score_error_scale(qv[t:t + 1], w[t:t + 1], kv[cand])[0]
+    ref_idx, ref_sc = topk_sorted(cand, s, k)
+    g = set(int(x) for x in got_idx if x >= 0)
+    r = set(int(x) for x in ref_idx if x >= 0)
+    if len(g) != len(r):
+        return False, 0
+    diff = g ^ r
+    if not diff:
+        return True, 0
+    kth = ref_sc[min(k, len(r)) - 1]
+    pos = {int(c): i for i, c in enumerate(cand)}
+    tol_k = RTOL[dtype] * sig[pos[int(ref_idx[min(k, len(r)) - 1])]]
+    for x in diff:
+        i = pos.get(x)
+        if i is None:
+            return False, 0
+        if abs(s[i] - kth) > 2 * max(RTOL[dtype] * sig[i], tol_k):
+            return False, 0
+    return True, len(diff)

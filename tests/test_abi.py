@@ -1,0 +1,97 @@
+"""The C ABI on the CPU: the library loads without a GPU, exports every function
+include/ivftk.h declares, and rejects bad arguments before touching a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ivftk.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from ivf_top_key_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from ivf_top_key_amd.build import build
+        build()
+    return _lib.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(idx_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for required in ("idx_build_seal", "idx_refit", "idx_route_topk", "idx_exhaustive_topk", "idx_create",
+                     "idx_destroy", "idx_last_error", "idx_publish", "idx_export", "idx_get_info",
+                     "idx_exhaustive_workspace_bytes"):
+        assert required in names
+
+
+def test_every_declared_function_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    from ivf_top_key_amd._lib import SIGNATURES
+    assert sorted(n for n, _, _ in SIGNATURES) == declared_functions()
+
+
+def _cfg(**over):
+    from ivf_top_key_amd._lib import idx_config
+    base = dict(heads=64, dim=128, dtype=2, n_sink=4, window=1024, cluster_size=128, seal_cap=256, seal_iters=10,
+                refit_every=16384, max_queries=4096, max_budget=8192, max_k=2048, max_keys=1 << 20)
+    base.update(over)
+    return idx_config(*[base[f] for f, _ in idx_config._fields_])
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(dtype=7), -1), (dict(heads=0), -1), (dict(heads=200), -1), (dict(dim=96), -7),
+    (dict(dtype=1, dim=32), -7), (dict(window=1000), -1), (dict(cluster_size=64), -7),
+    (dict(seal_cap=100), -1), (dict(seal_iters=0), -1), (dict(refit_every=1000), -1),
+    (dict(max_k=5000), -1), (dict(max_budget=100), -1), (dict(max_keys=0), -1),
+    (dict(max_keys=1 << 21), -6), (dict(max_budget=16384, max_k=4096), -6),
+])
+def test_create_rejects_bad_config(lib, over, code):
+    h = ctypes.c_void_p()
+    rc = lib.idx_create(ctypes.byref(_cfg(**over)), ctypes.byref(h))
+    assert rc == code, lib.idx_last_error()
+    assert h.value is None
+    assert lib.idx_last_error()
+
+
+def test_calls_on_null_handle(lib):
+    assert lib.idx_build_seal(None, None, None, 0, None) == -1
+    assert lib.idx_refit(None, None, None, None) == -1
+    assert lib.idx_publish(None, None, None) == -1
+    assert lib.idx_route_topk(None, None, None, None, 0, 1, 1, 1, None, None, None, None) == -1
+    assert lib.idx_export(None, -1, None) == -1
+    assert lib.idx_get_info(None, None) == -1
+    assert lib.idx_destroy(None) == 0
+
+
+def test_exhaustive_rejects_bad_arguments(lib):
+    p = ctypes.c_void_p(16)   # never dereferenced: every case fails validation first
+    call = lambda **kw: lib.idx_exhaustive_topk(
+        kw.get("keys", p), kw.get("ks", p), kw.get("n", 100), kw.get("dt", 1), kw.get("H", 64), kw.get("d", 128),
+        p, kw.get("qs", p), p, kw.get("q0", 10), kw.get("T", 4), kw.get("k", 8), p, p, p, kw.get("ws", 1 << 20),
+        None)
+    assert call(dt=9) == -1
+    assert call(H=0) == -1
+    assert call(d=96) == -7
+    assert call(keys=None) == -1
+    assert call(dt=2, ks=None) == -1
+    assert call(T=0) == -1
+    assert call(k=0) == -1 and call(k=5000) == -1
+    assert call(q0=-1) == -1
+    assert call(q0=97, T=4) == -4        # query position 100 has no key
+    assert call(ws=16) == -1             # workspace below one query row
+    assert "workspace" in lib.idx_last_error().decode()
+
+
+def test_workspace_size(lib):
+    assert lib.idx_exhaustive_workspace_bytes(1000, 3) == 3 * 1024 * 4
+    assert lib.idx_exhaustive_workspace_bytes(0, 3) == 0

@@ -1,0 +1,155 @@
+"""GPU parity: routed top-k (idx_route_topk) against the CPU oracle.
+
+Per query: the version (epoch, sealed windows, open window) must match exactly;
+representative scores within the score tolerance; the ranked clusters and the
+candidate list must equal the oracle's, except that clusters whose oracle
+representative scores are within the tolerance of each other may swap (then the
+oracle's fill, fed the GPU's cluster order, must reproduce the GPU's candidate
+list exactly and the GPU's order must be a valid ranking); the top-k must be a
+correct top-k of the candidates up to near ties, with scores within tolerance.
+Also: a budget covering the prefix makes the routed output bit-identical to the
+GPU's exhaustive output (same scores through the same score tile)."""
+import numpy as np
+import pytest
+
+from gpu_common import (RTOL, ensure_built, gpu_index, oracle_index, say, to_dev, topk_matches, workload)
+from oracle import fill_budget
+from oracle.index import query_values
+from oracle.score import indexer_scores, score_error_scale
+
+pytestmark = pytest.mark.gpu
+
+
+def route_parity(name, budget=None, k=None, T=None, q_pos0=None, **over):
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload(name, **over)
+    budget = wl["budget"] if budget is None else budget
+    k = wl["k"] if k is None else k
+    T = wl["T"] if T is None else T
+    q_pos0 = wl["q_pos0"] if q_pos0 is None else q_pos0
+    dt = wl["dtype"]
+    say(f"route {name} dtype={dt} T={T} q_pos0={q_pos0} k={k} budget={budget}")
+    gix = gpu_index(wl, inp, max_budget=max(budget, wl["budget"]), max_queries=max(T, wl["T"]))
+    try:
+        oix = oracle_index(wl, inp)
+        q = to_dev(inp["q"][:T])
+        qs = to_dev(inp["q_scale"][:T]) if inp["q_scale"] is not None else None
+        w = to_dev(inp["w"][:T])
+        cfg = oix.cfg
+        cand_cap = max(budget, cfg.n_sink + cfg.window) + 32
+        n_slots = ((q_pos0 + T - cfg.n_sink) // cfg.window) * cfg.n_clusters
+        dbg = ivf.make_route_debug(T, cand_cap, max(n_slots, 1), max(n_slots, 1))
+        idx, sc = ivf.idx_route_topk(gix, q, qs, w, q_pos0, k, budget, debug=dbg)
+        torch.cuda.synchronize()
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        d = {kk: v.cpu().numpy() for kk, v in dbg.items()}
+        qraw = inp["q"][:T]
+        qsc = None if inp["q_scale"] is None else inp["q_scale"][:T]
+        ridx, rsc, odbg = oix.route(qraw, qsc, inp["w"][:T], q_pos0, k, budget, debug=True)
+        qv = query_values(qraw, qsc, dt)
+        wv = inp["w"][:T].astype(np.float64)
+        stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
+        for t in range(T):
+            od = odbg[t]
+            r, m = od["epoch"], od["windows"]
+            assert d["version"][t].tolist() == [r, m, m * cfg.n_clusters, cfg.n_sink + m * cfg.window], \
+                f"query {t}: version {d['version'][t].tolist()} vs ({r}, {m})"
+            vis = {c.slot: c for c in oix.visible(od["n"])}
+            # representative scores of visible live slots
+            if vis:
+                slots = np.array(sorted(vis))
+                reps = np.stack([vis[s].rep_value for s in slots])
+                ref = indexer_scores(qv[t:t + 1], wv[t:t + 1], reps)[0]
+                sig = score_error_scale(qv[t:t + 1], wv[t:t + 1], reps)[0]
+                err = np.abs(d["rep_scores"][t, slots].astype(np.float64) - ref)
+                assert np.all(err <= RTOL[dt] * sig + 1e-30), f"query {t}: representative score error"
+                srep = dict(zip(slots.tolist(), ref.tolist()))
+                ssig = dict(zip(slots.tolist(), sig.tolist()))
+            n_ord = int(d["n_order"][t])
+            g_order = d["order"][t, :n_ord].tolist()
+            g_take = d["order_take"][t, :n_ord].tolist()
+            o_used = od["used"]
+            L = int(d["cand_len"][t])
+            g_cand = d["cand"][t, :L]
+            if [s for s, _ in o_used] == g_order:
+                assert [tk for _, tk in o_used] == g_take, f"query {t}: takes differ"
+                assert np.array_equal(g_cand, od["cand"]), f"query {t}: candidate list differs"
+            else:
+                # near ties only: a valid ranking under the tolerance, and the oracle's
+                # fill with this order reproduces the GPU's list exactly
+                stats["order_swaps"] += 1
+                tol = lambda a, b: 2 * RTOL[dt] * max(ssig[a], ssig[b])
+                for a, b in zip(g_order, g_order[1:]):
+                    assert srep[a] >= srep[b] - tol(a, b), f"query {t}: clusters {a},{b} out of order"
+                chosen = set(g_order)
+                last = g_order[-1]
+                for u in vis:
+                    if u not in chosen:
+                        assert srep[u] <= srep[last] + tol(u, last), f"query {t}: skipped cluster {u}"
+                cand, used = fill_budget(oix.base_candidates(od["n"]), [vis[s] for s in g_order], budget)
+                assert [s for s, _ in used] == g_order and [x for _, x in used] == g_take
+                assert np.array_equal(g_cand, cand), f"query {t}: fill with the GPU order differs"
+            ok, ex = topk_matches(idx[t], g_cand, qv, wv, oix.kv, t, k, dt)
+            assert ok, f"query {t}: top-k is not a top-k of the candidates"
+            stats["topk_exempt"] += ex
+            valid = idx[t] >= 0
+            assert valid.sum() == min(k, L)
+            gj = idx[t][valid]
+            ref = indexer_scores(qv[t:t + 1], wv[t:t + 1], oix.kv[gj])[0]
+            sig = score_error_scale(qv[t:t + 1], wv[t:t + 1], oix.kv[gj])[0]
+            err = np.abs(sc[t][valid].astype(np.float64) - ref)
+            assert np.all(err <= RTOL[dt] * sig + 1e-30), f"query {t}: candidate score error"
+            if err.size:
+                stats["max_err"] = max(stats["max_err"], float(np.max(err / np.maximum(sig, 1e-300))))
+        say(f"  ok {stats}")
+        return stats
+    finally:
+        ivf.idx_destroy(gix)
+
+
+def test_route_fp32_tiny():
+    route_parity("c1")
+
+
+def test_route_fp32_with_refits():
+    route_parity("c1r")
+
+
+def test_route_bf16():
+    route_parity("bf16_small")
+
+
+def test_route_e4m3():
+    route_parity("e4m3_small")
+
+
+def test_route_queries_straddling_windows_and_epochs():
+    """Queries from before the first seal to past the second refit boundary in one
+    call: several versions inside one chunk (epochs 0, 1 and 2, windows 0..7)."""
+    route_parity("c1r", q_pos0=900, T=3300, budget=1200)
+
+
+def test_route_sinks_and_open_window_exceed_budget():
+    route_parity("c1r", budget=96, k=64, q_pos0=5000, T=200)
+
+
+def test_route_budget_covering_prefix_is_exhaustive_bit_exact():
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload("bf16_small")
+    T, q_pos0, k = 64, wl["N"] - 64, wl["k"]
+    budget = 16384
+    gix = gpu_index(wl, inp, max_budget=budget)
+    try:
+        q = to_dev(inp["q"][:T])
+        w = to_dev(inp["w"][:T])
+        idx, sc = ivf.idx_route_topk(gix, q, None, w, q_pos0, k, budget)
+        eidx, esc = ivf.idx_exhaustive_topk(to_dev(inp["keys"]), None, "bf16", wl["H"], q, None, w, q_pos0, k)
+        torch.cuda.synchronize()
+        assert torch.equal(idx, eidx)
+        assert torch.equal(sc.view(torch.int32), esc.view(torch.int32))
+    finally:
+        ivf.idx_destroy(gix)
