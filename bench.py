@@ -1,0 +1,352 @@
+"""Benchmark: routed indexer top-k at a 1M-token prefix on one MI355X.
+
+Workload (synthetic, seeded; the pages' models and datasets are not available):
+1,048,576 E4M3 keys with per-token fp32 scales, H=64 heads, d=128, 4096 queries at
+the tail of the prefix (positions 1,044,480 .. 1,048,575), k=2048, budget 8192.
+The index is built first (untimed; its seal and refit costs are reported apart),
+then one step = one idx_route_topk call over the 4096 queries: version select,
+representative scores, cluster cut + fill, candidate rescoring + top-k.
+
+Reported next to the routed throughput: the exhaustive top-k time on the same
+queries (our own baseline), recall of routed vs exhaustive, a budget sweep
+(4096 / 8192 / 16384), per-kernel times from HIP events recorded around each
+kernel during the timed steps, the roofline of the dominant kernel, and the CPU
+oracle timed on a bounded sample of the same queries.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "routed top-k queries/s at 1M-token prefix, k=2048, 8K budget; recall vs exhaustive"
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Hip:
+    """hipEvent helpers through the HIP runtime that torch already loaded."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def event(self):
+        ev = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed(self, a, b):
+        ms = ctypes.c_float()
+        assert self.h.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    def sync(self, ev):
+        self.h.hipEventSynchronize(ctypes.c_void_p(ev))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="c4")
+    ap.add_argument("--budget", type=int, default=8192)
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-exhaustive", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one 1 GiB elementwise copy (reference for HBM counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the path shards by query with no exchange; see the design notes)", flush=True)
+        sys.exit(2)
+
+    import torch
+    import datagen
+    from datagen.workloads import WORKLOADS
+    import ivf_top_key_amd as ivf
+    from ivf_top_key_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from ivf_top_key_amd.build import build
+        build()
+
+    wl = dict(WORKLOADS[args.workload])
+    N, T, H, d, k, dt = wl["N"], wl["T"], wl["H"], wl["d"], wl["k"], wl["dtype"]
+    q_pos0, R, W = wl["q_pos0"], wl["refit_every"], wl["window"]
+    budget = args.budget
+    dev = torch.device("cuda:0")
+    hip = Hip()
+
+    t0 = time.time()
+    inp = datagen.workload_inputs(wl["seed"], N, T, q_pos0, H, d, wl["M"], dt)
+    log(f"inputs generated in {time.time() - t0:.1f}s")
+    keys = torch.from_numpy(inp["keys"]).to(dev)
+    ks = torch.from_numpy(inp["k_scale"]).to(dev) if inp["k_scale"] is not None else None
+    q = torch.from_numpy(np.ascontiguousarray(inp["q"])).to(dev)
+    qs = torch.from_numpy(inp["q_scale"]).to(dev) if inp["q_scale"] is not None else None
+    w = torch.from_numpy(inp["w"]).to(dev)
+
+    # ---- build the index by streaming the prefix, R keys at a time ----
+    ix = ivf.idx_create(heads=H, dim=d, dtype=dt, max_keys=N, n_sink=wl["n_sink"], window=W,
+                        cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"], seal_iters=wl["seal_iters"],
+                        refit_every=R, max_queries=T, max_budget=16384, max_k=k)
+    stream = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    seal_ms, refit_ms = [], []
+    for a in range(0, N, R):
+        b = min(N, a + R)
+        e0, e1 = hip.event(), hip.event()
+        hip.h.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
+        ivf.idx_build_seal(ix, keys[a:b], None if ks is None else ks[a:b])
+        hip.h.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
+        r0, r1 = hip.event(), hip.event()
+        hip.h.hipEventRecord(ctypes.c_void_p(r0), ctypes.c_void_p(stream.cuda_stream))
+        launched = ivf.idx_refit(ix, stream=stream, side_stream=side)
+        hip.h.hipEventRecord(ctypes.c_void_p(r1), ctypes.c_void_p(side.cuda_stream))
+        ivf.idx_publish(ix, stream=stream)
+        hip.sync(e1)
+        hip.sync(r1)
+        seal_ms.append((hip.elapsed(e0, e1), (b - a) // W))
+        if launched:
+            refit_ms.append(hip.elapsed(r0, r1))
+    torch.cuda.synchronize()
+    build_s = time.time() - t0
+    info = ivf.idx_get_info(ix)
+    log(f"index built in {build_s:.2f}s: {info}")
+
+    if args.copy_calibration:
+        # a plain copy of known size: 1 GiB read + 1 GiB written
+        xa = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        ya = torch.empty_like(xa)
+        torch.mul(xa, 1.0, out=ya)
+        torch.cuda.synchronize()
+        del xa, ya
+
+    # ---- routed steps ----
+    out_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+    out_sc = torch.empty((T, k), dtype=torch.float32, device=dev)
+    for _ in range(args.warmup):
+        ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc)
+    torch.cuda.synchronize()
+    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    start, stop = hip.event(), hip.event()
+    torch.cuda.synchronize()
+    hip.h.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream.cuda_stream))
+    for s in range(args.steps):
+        ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc, debug={"events": evs[s]})
+    hip.h.hipEventRecord(ctypes.c_void_p(stop), ctypes.c_void_p(stream.cuda_stream))
+    torch.cuda.synchronize()
+    total_ms = hip.elapsed(start, stop)
+    ms_per_step = total_ms / args.steps
+    names = ["rep_score", "route_select", "rescore_topk"]
+    kern = {n: float(np.mean([hip.elapsed(e[2 * i], e[2 * i + 1]) for e in evs])) for i, n in enumerate(names)}
+    value = T / (ms_per_step / 1e3)
+    log(f"routed: {ms_per_step:.3f} ms/step, {value:.0f} q/s, kernels {kern}")
+
+    # ---- algorithmic work of one step ----
+    Cs = W // wl["cluster_size"]
+    S = wl["n_sink"]
+    n_t = q_pos0 + 1 + np.arange(T, dtype=np.int64)
+    m_t = (n_t - S) // W
+    c_vis = m_t * Cs
+    open_t = n_t - S - m_t * W
+    cand_t = np.minimum(n_t, np.maximum(budget, S + open_t))
+    rb = d * {"f32": 4, "bf16": 2, "e4m3": 1}[dt]
+    scale_b = 4 if dt == "e4m3" else 0
+    rep_flops = float(2 * H * d * c_vis.sum())
+    rescore_bytes = float(cand_t.sum() * (rb + scale_b + 4) + T * H * (rb + 8) + T * k * 8)
+    rescore_flops = float(2 * H * d * cand_t.sum())
+    keys_scored = float((c_vis + cand_t).sum())
+    peak_mfma = {"e4m3": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS, "f32": FP32_PEAK_TFLOPS}[dt]
+    rep_frac = rep_flops / (kern["rep_score"] * 1e-3) / 1e12 / peak_mfma
+    resc_gbs = rescore_bytes / (kern["rescore_topk"] * 1e-3) / 1e9
+    if kern["rescore_topk"] >= kern["rep_score"]:
+        roof = dict(kernel="rescore_topk", bound="hbm", achieved=round(resc_gbs, 1), peak=HBM_PEAK_GBS,
+                    unit="GB/s", frac=round(resc_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                    algorithmic_bytes=rescore_bytes, avg_launch_ms=round(kern["rescore_topk"], 4))
+    else:
+        ach = rep_flops / (kern["rep_score"] * 1e-3) / 1e12
+        roof = dict(kernel="rep_score", bound="mfma", achieved=round(ach, 2), peak=peak_mfma, unit="TFLOP/s",
+                    frac=round(rep_frac, 4), traffic=None, algorithmic_flops=rep_flops,
+                    avg_launch_ms=round(kern["rep_score"], 4))
+
+    # ---- exhaustive baseline + recall ----
+    extra = {}
+    if not args.no_exhaustive:
+        ws_q = 1024
+        ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(q_pos0 + T, ws_q) // 4, dtype=torch.float32, device=dev)
+        e_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        e_sc = torch.empty((T, k), dtype=torch.float32, device=dev)
+        ivf.idx_exhaustive_topk(keys, ks, dt, H, q, qs, w, q_pos0, k, e_idx, e_sc, workspace=ws)
+        torch.cuda.synchronize()
+        reps = 2
+        a0, a1 = hip.event(), hip.event()
+        hip.h.hipEventRecord(ctypes.c_void_p(a0), ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(reps):
+            ivf.idx_exhaustive_topk(keys, ks, dt, H, q, qs, w, q_pos0, k, e_idx, e_sc, workspace=ws)
+        hip.h.hipEventRecord(ctypes.c_void_p(a1), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        exh_ms = hip.elapsed(a0, a1) / reps
+        exh_flops = float(2 * H * d * n_t.sum())
+        r_np, e_np = out_idx.cpu().numpy(), e_idx.cpu().numpy()
+        rec = summarize(recall_per_query(r_np, e_np))
+        extra.update(exhaustive_ms=round(exh_ms, 3), exhaustive_qps=round(T / (exh_ms * 1e-3), 1),
+                     exhaustive_tflops=round(exh_flops / (exh_ms * 1e-3) / 1e12, 1),
+                     routed_speedup_vs_exhaustive=round(exh_ms / ms_per_step, 2), recall=rec)
+        log(f"exhaustive {exh_ms:.2f} ms, speedup {exh_ms / ms_per_step:.2f}x, recall {rec}")
+        if not args.no_sweep:
+            sweep = {}
+            for B in (4096, 8192, 16384):
+                for _ in range(2):
+                    ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, B, out_idx, out_sc)
+                b0, b1 = hip.event(), hip.event()
+                hip.h.hipEventRecord(ctypes.c_void_p(b0), ctypes.c_void_p(stream.cuda_stream))
+                for _ in range(5):
+                    ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, B, out_idx, out_sc)
+                hip.h.hipEventRecord(ctypes.c_void_p(b1), ctypes.c_void_p(stream.cuda_stream))
+                torch.cuda.synchronize()
+                bms = hip.elapsed(b0, b1) / 5
+                rb_ = summarize(recall_per_query(out_idx.cpu().numpy(), e_np))
+                sweep[str(B)] = dict(ms=round(bms, 3), qps=round(T / (bms * 1e-3), 1), recall=rb_,
+                                     speedup_vs_exhaustive=round(exh_ms / bms, 2))
+                log(f"budget {B}: {bms:.3f} ms, recall {rb_}")
+            extra["budget_sweep"] = sweep
+        del ws
+
+    # ---- CPU oracle on a bounded sample of the same queries ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(ix, inp, wl, budget, args.cpu_sample)
+        log(f"cpu baseline {cpu}")
+
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt,
+        "data": "synthetic",
+        "config": {"workload": f"1M-token prefix ({N} keys), {dt} keys+queries with fp32 scales, H={H}, d={d}, "
+                               f"{T} tail queries, k={k}, budget {budget}",
+                   "global_batch": T, "seq_len": N, "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "keys_scored_per_s": round(keys_scored / (ms_per_step * 1e-3), 1),
+        "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
+        "rep_score_mfma_frac": round(rep_frac, 4),
+        "rescore_hbm_gbs": round(resc_gbs, 1),
+        "rescore_tflops": round(rescore_flops / (kern["rescore_topk"] * 1e-3) / 1e12, 1),
+        "maintenance": {
+            "build_s": round(build_s, 3),
+            "seal_ms_per_window_last_chunk": round(seal_ms[-1][0] / max(1, seal_ms[-1][1]), 4),
+            "refits": len(refit_ms),
+            "refit_ms_last": round(refit_ms[-1], 3) if refit_ms else None,
+            "refit_ms_mean": round(float(np.mean(refit_ms)), 3) if refit_ms else None,
+        },
+        **extra,
+    }
+    ivf.idx_destroy(ix)
+    print(json.dumps(res), flush=True)
+
+
+def recall_per_query(routed, reference):
+    """|routed_t & reference_t| / |reference_t| per query (padding -1 ignored)."""
+    out = np.empty(routed.shape[0])
+    for t in range(routed.shape[0]):
+        ref = reference[t][reference[t] >= 0]
+        out[t] = 1.0 if ref.size == 0 else np.intersect1d(ref, routed[t][routed[t] >= 0]).size / ref.size
+    return out
+
+
+def summarize(r):
+    return dict(mean=round(float(np.mean(r)), 5), p5=round(float(np.percentile(r, 5)), 5),
+                min=round(float(np.min(r)), 5))
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return os.cpu_count()
+
+
+def cpu_baseline(ix, inp, wl, budget, sample):
+    """Time the CPU oracle's routing (representative scores, ranking, budget fill,
+    fp64 rescoring, top-k) for `sample` of the tail queries over the same index.
+    The oracle cannot rebuild a 1M-key index in a benchmark's time (each refit is a
+    brute-force pass over every key), so its cluster tables are loaded from the
+    library's export; only the routing is timed."""
+    import ivf_top_key_amd as ivf
+    from oracle import OracleConfig, OracleIndex
+    from oracle.index import key_values, make_cluster
+
+    cfg = OracleConfig(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], n_sink=wl["n_sink"], window=wl["window"],
+                       cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"], seal_iters=wl["seal_iters"],
+                       refit_every=wl["refit_every"])
+    oix = OracleIndex(cfg)
+    oix.kv = key_values(inp["keys"], inp["k_scale"], wl["dtype"])
+    oix.X = np.zeros((oix.kv.shape[0], 0), np.float32)          # routing never reads fp32 keys
+    info = ivf.idx_get_info(ix)
+    P = info["published_epoch"]
+
+    def clusters(exp, lo_slot=0):
+        out = []
+        for s in range(exp["sizes"].shape[0]):
+            sz, off = int(exp["sizes"][s]), int(exp["offsets"][s])
+            out.append(make_cluster(s, exp["members"][off:off + sz].astype(np.int64), exp["centroids"][s],
+                                    wl["dtype"]))
+        return out
+
+    seal = clusters(ivf.idx_export(ix, -1))
+    Cs = cfg.n_clusters
+    oix.seals = [seal[i:i + Cs] for i in range(0, len(seal), Cs)]
+    if P >= 1:
+        oix.epochs[P] = clusters(ivf.idx_export(ix, P))
+    oix.computed = oix.published = P
+    rng = np.random.default_rng(0)
+    T = wl["T"]
+    pick = np.sort(rng.choice(T, size=min(sample, T), replace=False))
+    threads = blas_threads()
+    t0 = time.perf_counter()
+    for t in pick:
+        oix.route(inp["q"][t:t + 1], None if inp["q_scale"] is None else inp["q_scale"][t:t + 1],
+                  inp["w"][t:t + 1], wl["q_pos0"] + int(t), wl["k"], budget)
+    dt_s = time.perf_counter() - t0
+    return {"value": round(len(pick) / dt_s, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(pick)} of the {T} tail queries (seeded), routed by the numpy oracle over the same "
+                      f"1M-key index (cluster tables loaded from the library's export; fp64 scores; "
+                      f"{threads} BLAS threads); {dt_s:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -115,6 +115,8 @@ typedef struct {
   float* rep_scores;     /* [T, rep_cap]: representative score of each visible slot     */
   int32_t rep_cap;
   int32_t* version;      /* [T, 4]: epoch r, sealed windows m, visible slots, open start */
+  void** events;         /* host array of 6 hipEvent_t: recorded before and after each of the
+                            three kernels (representative scores, cut + fill, rescore + top-k) */
 } idx_route_debug;
 
 /* Host buffers for idx_export.  Pass NULL arrays to read only the counts. */
@@ -176,8 +178,9 @@ int idx_publish(idx_index* ix, void* stream, int32_t* published);
  * later windows < m; candidates are sinks [0, S), the open window [S + m*W, p] and
  * ranked cluster members until `budget` is reached (sinks and open window count
  * against the budget but are always taken whole).
- * Errors: ECAUSAL (q_pos0 + T > n_keys), ESTATE (a query needs an epoch older than
- * the two newest published ones), EINVAL / ECAPACITY for sizes. */
+ * Errors: ECAUSAL (q_pos0 + T > n_keys), ESTATE (a query needs an epoch that is no
+ * longer held: the three newest computed epochs are held, two while a refit is in
+ * flight), EINVAL / ECAPACITY for sizes. */
 int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
                    int32_t T, int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score,
                    const idx_route_debug* dbg, void* stream);

@@ -136,13 +136,16 @@ def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0:
         topk_score = torch.empty((T, k), dtype=torch.float32, device=q.device)
     dbg = None
     if debug is not None:
+        ev = debug.get("events")
+        if ev is not None:
+            ev = ctypes.cast((ctypes.c_void_p * len(ev))(*ev), ctypes.POINTER(ctypes.c_void_p))
         dbg = _lib.idx_route_debug(
             _ptr(debug.get("cand")), debug["cand"].shape[1] if debug.get("cand") is not None else 0,
             _ptr(debug.get("cand_len")), _ptr(debug.get("order")), _ptr(debug.get("order_take")),
             debug["order"].shape[1] if debug.get("order") is not None else 0, _ptr(debug.get("n_order")),
             _ptr(debug.get("rep_scores")),
             debug["rep_scores"].shape[1] if debug.get("rep_scores") is not None else 0,
-            _ptr(debug.get("version")))
+            _ptr(debug.get("version")), ev)
     _check(lib().idx_route_topk(ix.handle, _ptr(q, ELEM_BYTES[ix.dtype], "q"), _ptr(q_scale, 4, "q_scale"),
                                 _ptr(w, 4, "w"), q_pos0, T, k, budget, _ptr(topk_idx, 4, "topk_idx"),
                                 _ptr(topk_score, 4, "topk_score"), ctypes.byref(dbg) if dbg is not None else None,

@@ -444,11 +444,21 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
     p.dbg_version = dbg->version;
   }
   const int max_slots = windows_in(q_pos0 + T) * ix->Cs;
+  hipEvent_t* ev = (dbg && dbg->events) ? reinterpret_cast<hipEvent_t*>(dbg->events) : nullptr;
   hipError_t e = hipSuccess;
-  if (max_slots > 0) e = launch_rep_score(p, c.dtype, c.dim, ix->HT, max_slots, s);
+  auto mark = [&](int i) {
+    if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
+  };
+  mark(0);
+  if (max_slots > 0 && e == hipSuccess) e = launch_rep_score(p, c.dtype, c.dim, ix->HT, max_slots, s);
+  mark(1);
+  mark(2);
   if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
+  mark(3);
   const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
+  mark(4);
   if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
+  mark(5);
   if (e != hipSuccess) return device_error(ix, e, "route launch");
   if (dbg) {
     if (dbg->cand && dbg->cand_cap > 0) {

@@ -24,14 +24,17 @@ def route_parity(name, budget=None, k=None, T=None, q_pos0=None, **over):
     import torch
     import ivf_top_key_amd as ivf
     ensure_built()
+    if T is not None:
+        over["T"] = T
+    if q_pos0 is not None:
+        over["q_pos0"] = q_pos0
     wl, inp = workload(name, **over)
     budget = wl["budget"] if budget is None else budget
     k = wl["k"] if k is None else k
-    T = wl["T"] if T is None else T
-    q_pos0 = wl["q_pos0"] if q_pos0 is None else q_pos0
+    T, q_pos0 = wl["T"], wl["q_pos0"]
     dt = wl["dtype"]
     say(f"route {name} dtype={dt} T={T} q_pos0={q_pos0} k={k} budget={budget}")
-    gix = gpu_index(wl, inp, max_budget=max(budget, wl["budget"]), max_queries=max(T, wl["T"]))
+    gix = gpu_index(wl, inp, max_budget=max(budget, wl["budget"]), max_queries=T, max_k=max(k, wl["k"]))
     try:
         oix = oracle_index(wl, inp)
         q = to_dev(inp["q"][:T])
