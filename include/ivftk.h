@@ -117,6 +117,9 @@ typedef struct {
   int32_t* version;      /* [T, 4]: epoch r, sealed windows m, visible slots, open start */
   void** events;         /* host array of 6 hipEvent_t: recorded before and after each of the
                             three kernels (representative scores, cut + fill, rescore + top-k) */
+  int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut kernel at this
+                            size so the full cut kernel takes over sooner (testing)        */
+  float* cand_scores;    /* [T, cand_cap]: exact score of each candidate, fill order      */
 } idx_route_debug;
 
 /* Host buffers for idx_export.  Pass NULL arrays to read only the counts. */

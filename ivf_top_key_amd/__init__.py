@@ -124,7 +124,8 @@ def make_route_debug(T: int, cand_cap: int, order_cap: int, rep_cap: int, device
                 order=torch.full((T, order_cap), -1, **i32), order_take=torch.zeros((T, order_cap), **i32),
                 n_order=torch.zeros(T, **i32),
                 rep_scores=torch.zeros((T, rep_cap), dtype=torch.float32, device=device),
-                version=torch.zeros((T, 4), **i32))
+                version=torch.zeros((T, 4), **i32),
+                cand_scores=torch.full((T, cand_cap), float("nan"), dtype=torch.float32, device=device))
 
 
 def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0: int, k: int, budget: int,
@@ -145,7 +146,7 @@ def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0:
             debug["order"].shape[1] if debug.get("order") is not None else 0, _ptr(debug.get("n_order")),
             _ptr(debug.get("rep_scores")),
             debug["rep_scores"].shape[1] if debug.get("rep_scores") is not None else 0,
-            _ptr(debug.get("version")), ev)
+            _ptr(debug.get("version")), ev, int(debug.get("list_cap", 0)), _ptr(debug.get("cand_scores")))
     _check(lib().idx_route_topk(ix.handle, _ptr(q, ELEM_BYTES[ix.dtype], "q"), _ptr(q_scale, 4, "q_scale"),
                                 _ptr(w, 4, "w"), q_pos0, T, k, budget, _ptr(topk_idx, 4, "topk_idx"),
                                 _ptr(topk_score, 4, "topk_score"), ctypes.byref(dbg) if dbg is not None else None,

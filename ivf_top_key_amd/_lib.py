@@ -27,7 +27,8 @@ class idx_info(ctypes.Structure):
 class idx_route_debug(ctypes.Structure):
     _fields_ = [("cand", c_vp), ("cand_cap", c_i32), ("cand_len", c_vp), ("order", c_vp), ("order_take", c_vp),
                 ("order_cap", c_i32), ("n_order", c_vp), ("rep_scores", c_vp), ("rep_cap", c_i32),
-                ("version", c_vp), ("events", ctypes.POINTER(c_vp))]
+                ("version", c_vp), ("events", ctypes.POINTER(c_vp)), ("list_cap", c_i32),
+                ("cand_scores", c_vp)]
 
 
 class idx_export_buf(ctypes.Structure):

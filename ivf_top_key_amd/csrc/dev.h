@@ -237,6 +237,115 @@ __device__ inline uint64_t radix_select_desc(const uint64_t* a, const int* wts, 
   return 0;  // not reached
 }
 
+struct Select32Scratch {
+  int hist[256];
+  uint32_t prefix;
+  int need;
+  int above;
+};
+
+// Radix select over 32-bit keys a[0..n): returns T with
+//   count(a > T) < target <= count(a >= T); sc.above receives count(a > T).
+// Requires 1 <= target <= n.  All threads of the block must call it.
+__device__ inline uint32_t radix_select32_desc(const uint32_t* a, int n, int target, Select32Scratch& sc) {
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    sc.prefix = 0;
+    sc.need = target;
+    sc.above = 0;
+  }
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += blockDim.x) sc.hist[i] = 0;
+    __syncthreads();
+    const uint32_t prefix = sc.prefix;
+    const uint32_t mask = (shift == 24) ? 0u : (~0u << (shift + 8));
+    for (int i = tid; i < n; i += blockDim.x) {
+      const uint32_t v = a[i];
+      if ((v & mask) == prefix) atomicAdd(&sc.hist[(v >> shift) & 255u], 1);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const int lane = tid;
+      int s = 0;
+      for (int q = 0; q < 4; ++q) s += sc.hist[255 - 4 * lane - q];
+      int incl = s;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      const int excl = incl - s;
+      const int need = sc.need;
+      if (excl < need && need <= incl) {
+        int acc = excl;
+        for (int q = 0; q < 4; ++q) {
+          const int d = 255 - 4 * lane - q;
+          if (acc + sc.hist[d] >= need) {
+            sc.need = need - acc;
+            sc.above += acc;
+            sc.prefix = prefix | ((uint32_t)d << shift);
+            break;
+          }
+          acc += sc.hist[d];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  return sc.prefix;
+}
+
+// Block-wide min and max of 32-bit keys (threads pass their partial min/max).
+// tmp must hold 2 * (blockDim.x / 64) uints.
+__device__ inline void block_minmax(uint32_t& mn, uint32_t& mx, uint32_t* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  for (int off = 32; off > 0; off >>= 1) {
+    const uint32_t a = __shfl_xor(mn, off), b = __shfl_xor(mx, off);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    tmp[2 * wave] = mn;
+    tmp[2 * wave + 1] = mx;
+  }
+  __syncthreads();
+  mn = 0xFFFFFFFFu;
+  mx = 0u;
+  for (int i = 0; i < nw; ++i) {
+    mn = tmp[2 * i] < mn ? tmp[2 * i] : mn;
+    mx = tmp[2 * i + 1] > mx ? tmp[2 * i + 1] : mx;
+  }
+  __syncthreads();
+}
+
+// Monotone binning of scores by value: the keys' scores in [lo, hi] (lo, hi = the
+// scores of the smallest and largest key) map to bin = trunc((x - lo) * nbin / (hi -
+// lo)), clamped to [0, nbin).  Subtraction of a constant, multiplication by a
+// positive constant and truncation never reverse an order, so a higher score never
+// lands in a lower bin and equal scores share a bin.  Binning by value spreads a
+// block's scores over the bins (keys in order-key space are logarithmic in the
+// magnitude, which crowds most scores into a few bins and serialises the histogram
+// atomics).
+struct ValBins {
+  float lo;
+  float scale;
+  int top;
+  __device__ __forceinline__ uint32_t operator()(uint32_t okey) const {
+    const float x = from_order_bits(okey);
+    const int b = (int)((x - lo) * scale);
+    return (uint32_t)(b < 0 ? 0 : (b > top ? top : b));
+  }
+};
+
+// mn_key < mx_key are order keys; returns bins over their scores.
+__device__ __forceinline__ ValBins make_bins(uint32_t mn_key, uint32_t mx_key, int nbin) {
+  ValBins b;
+  b.lo = from_order_bits(mn_key);
+  const float span = from_order_bits(mx_key) - b.lo;
+  b.scale = (span > 0.0f && span < __builtin_inff()) ? (float)nbin / span : 0.0f;
+  b.top = nbin - 1;
+  return b;
+}
+
 // Exclusive scan of v over the block in thread order; *total receives the sum.
 // tmp must hold one int per wave (blockDim.x / 64 <= 16).
 __device__ inline int block_exclusive_scan(int v, int* tmp, int* total) {
@@ -314,18 +423,16 @@ __device__ __forceinline__ void load_half_row(uint32_t* r, const uint8_t* row) {
   }
 }
 
-// One query's operands: HT tiles of 32 heads.
+// One query's A operands: HT tiles of 32 heads (rows beyond H are zero).
 template <int DT, int D, int HT>
 struct QueryFrag {
   uint32_t a[HT][Geo<DT, D>::HW];
-  float wq[HT][16];   // w[h] * q_scale[h] for this lane's accumulator rows (0 beyond H)
 };
 
-// q_t: the query's [H][RB] rows; w_t, qs_t: [H] (qs_t may be null).
+// q_t: the query's [H][RB] rows.
 template <int DT, int D, int HT>
-__device__ __forceinline__ void load_query(QueryFrag<DT, D, HT>& f, const uint8_t* q_t, const float* w_t,
-                                           const float* qs_t, int H) {
-  const int lane = threadIdx.x & 63, r = lane & 31, g = lane >> 5;
+__device__ __forceinline__ void load_query(QueryFrag<DT, D, HT>& f, const uint8_t* q_t, int H) {
+  const int r = threadIdx.x & 31;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
     const int head = ht * 32 + r;
@@ -335,18 +442,22 @@ __device__ __forceinline__ void load_query(QueryFrag<DT, D, HT>& f, const uint8_
 #pragma unroll
       for (int i = 0; i < Geo<DT, D>::HW; ++i) f.a[ht][i] = 0;
     }
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int h = ht * 32 + 8 * (v >> 2) + 4 * g + (v & 3);
-      f.wq[ht][v] = (h < H) ? (qs_t ? w_t[h] * qs_t[h] : w_t[h]) : 0.0f;
-    }
   }
 }
 
+// Head weights of one query into LDS: wq[h] = w[h] * q_scale[h] for h < H, 0 up to
+// HT*32.  Called by the wave that uses them (lane-strided).
+template <int HT>
+__device__ __forceinline__ void load_query_weights(float* wq, const float* w_t, const float* qs_t, int H) {
+  const int lane = threadIdx.x & 63;
+  for (int h = lane; h < HT * 32; h += 64) wq[h] = (h < H) ? (qs_t ? w_t[h] * qs_t[h] : w_t[h]) : 0.0f;
+}
+
 // Score of this lane's column (key) against the query, before the key scale.
-// Lanes l and l+32 return the same value.
+// wq: the query's LDS head weights.  Lanes l and l+32 return the same value.
 template <int DT, int D, int HT>
-__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const uint32_t (&b)[Geo<DT, D>::HW]) {
+__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const float* wq, const uint32_t* b) {
+  const int g = (threadIdx.x >> 5) & 1;
   v16f acc[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -360,10 +471,45 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
-    for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.wq[ht][v], __builtin_fmaxf(acc[ht][v], 0.0f), p);
+    for (int j = 0; j < 4; ++j) {
+      // rows 8j + 4g + 0..3 of this head tile
+      const float4 w4 = *reinterpret_cast<const float4*>(wq + ht * 32 + 8 * j + 4 * g);
+      p = __builtin_fmaf(w4.x, __builtin_fmaxf(acc[ht][4 * j + 0], 0.0f), p);
+      p = __builtin_fmaf(w4.y, __builtin_fmaxf(acc[ht][4 * j + 1], 0.0f), p);
+      p = __builtin_fmaf(w4.z, __builtin_fmaxf(acc[ht][4 * j + 2], 0.0f), p);
+      p = __builtin_fmaf(w4.w, __builtin_fmaxf(acc[ht][4 * j + 3], 0.0f), p);
+    }
   }
   const float o = __shfl_xor(p, 32);
   return p + o;
+}
+
+// Score column blocks blk = first, first + step, ... < nblk of one query with a ring
+// of DEPTH row buffers: the rows of block i + (DEPTH-1)*step are in flight while
+// block i is contracted.  fetch(blk, buf, scale) issues this lane's loads for a
+// block; sink(blk, score) consumes the score of this lane's column.
+template <int DT, int D, int HT, int DEPTH, class Fetch, class Sink>
+__device__ __forceinline__ void score_blocks(const QueryFrag<DT, D, HT>& f, const float* wq, int first, int step,
+                                             int nblk, Fetch fetch, Sink sink) {
+  uint32_t buf[DEPTH][Geo<DT, D>::HW];
+  float sc[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) {
+    const int blk = first + d * step;
+    if (blk < nblk) fetch(blk, buf[d], sc[d]);
+  }
+  for (int base = first; base < nblk; base += DEPTH * step) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int blk = base + d * step;
+      if (blk < nblk) {
+        const float x = score_tile<DT, D, HT>(f, wq, buf[d]) * sc[d];
+        sink(blk, x);
+        const int nxt = blk + DEPTH * step;
+        if (nxt < nblk) fetch(nxt, buf[d], sc[d]);
+      }
+    }
+  }
 }
 
 }  // namespace ivftk

@@ -44,6 +44,7 @@ struct RouteParams {
   int* cand;           // [T, cand_ld] candidate positions
   int64_t cand_ld;
   int* cand_len;       // [T]
+  int* redo;           // [T]: 1 when the fast cut kernel left the query to the full one
   int* topk_idx;       // [T, k]
   float* topk_score;   // [T, k] or null
   // optional debug outputs (null when unused)
@@ -52,6 +53,9 @@ struct RouteParams {
   int dbg_order_cap;
   int* dbg_n_order;
   int* dbg_version;
+  int list_cap;        // > 0: smaller cluster-list capacity of the fast cut kernel (tests)
+  float* dbg_cand_scores;  // [T, dbg_cand_ld]
+  int dbg_cand_ld;
 };
 
 struct ExhParams {

@@ -55,6 +55,28 @@ __device__ __forceinline__ float sqdist(const float (&x)[D], const float* c) {
   return acc;
 }
 
+// Four distances at once (four independent chains, each in the fixed order).
+template <int D>
+__device__ __forceinline__ void sqdist4(const float (&x)[D], const float* c, float& d0, float& d1, float& d2,
+                                        float& d3) {
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+#pragma unroll
+  for (int i = 0; i < D; ++i) {
+    const float t0 = x[i] - c[i];
+    const float t1 = x[i] - c[D + i];
+    const float t2 = x[i] - c[2 * D + i];
+    const float t3 = x[i] - c[3 * D + i];
+    a0 = a0 + t0 * t0;
+    a1 = a1 + t1 * t1;
+    a2 = a2 + t2 * t2;
+    a3 = a3 + t3 * t3;
+  }
+  d0 = a0;
+  d1 = a1;
+  d2 = a2;
+  d3 = a3;
+}
+
 // warm centroid and liveness of slot s
 __device__ __forceinline__ const float* warm_cent(const RefitParams& p, int s, int D) {
   return (s < (p.r - 1) * p.Q) ? p.prev.cent + (size_t)s * D : p.seal.cent + (size_t)s * D;
@@ -95,10 +117,17 @@ __global__ __launch_bounds__(256) void k_refit_old(RefitParams p) {
     for (int i = threadIdx.x; i < nt; i += blockDim.x) alive[i] = p.seal.size[t0 + i] > 0;
     __syncthreads();
     if (active) {
-      for (int c = 0; c < nt; ++c) {
+      int c = 0;
+      for (; c + 4 <= nt; c += 4) {
+        float d4[4];
+        sqdist4<D>(xv, tile + c * D, d4[0], d4[1], d4[2], d4[3]);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (alive[c + u]) dnew = __builtin_fminf(dnew, d4[u]);
+      }
+      for (; c < nt; ++c) {
         if (!alive[c]) continue;
-        const float dd = sqdist<D>(xv, tile + c * D);
-        dnew = __builtin_fminf(dnew, dd);
+        dnew = __builtin_fminf(dnew, sqdist<D>(xv, tile + c * D));
       }
     }
   }
@@ -149,17 +178,18 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
       for (int i = threadIdx.x; i < nt; i += blockDim.x) alive[i] = warm_alive(p, t0 + i);
       __syncthreads();
       if (active) {
-        for (int c = 0; c < nt; ++c) {
-          if (!alive[c]) continue;
-          const float dd = sqdist<D>(xv, tile + c * D);
+        auto take = [&](float dd, int slot) {
           if (dd < b1) {
             b2 = b1;
             b1 = dd;
-            best = t0 + c;
+            best = slot;
           } else if (dd < b2) {
             b2 = dd;
           }
-        }
+        };
+        // ascending slot order keeps ties on the lower slot
+        for (int c = 0; c < nt; ++c)
+          if (alive[c]) take(sqdist<D>(xv, tile + c * D), t0 + c);
       }
     }
     if (active) {

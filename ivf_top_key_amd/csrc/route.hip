@@ -35,7 +35,10 @@ __device__ __forceinline__ QV qversion(const RouteParams& p, int t) {
   return v;
 }
 
+// Full version: every visible cluster in LDS, weighted radix select over composite
+// keys.  Runs only for queries the fast kernel handed over (redo[t] = 1).
 __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_pow2) {
+  if (p.redo[blockIdx.x] == 0) return;
   extern __shared__ uint64_t lds[];
   uint64_t* comp = lds;                                   // [slot_pow2]
   int* wt = reinterpret_cast<int*>(lds + slot_pow2);      // [slot_pow2]: sizes, later prefix sums
@@ -154,7 +157,174 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   }
 }
 
+// Fast version: one pass builds a 4096-bin histogram of the live clusters' score
+// keys (linear bins between the smallest and largest key), weighted by cluster
+// size; the bin holding the cut is found by a suffix scan, and only clusters in
+// that bin or above (the selected ones plus the cut bin's other members) are
+// gathered and sorted exactly.  If that list would exceed LIST_CAP the query is
+// left to the full kernel.
+constexpr int LIST_CAP = 2048;
+
+__device__ inline void find_bin_desc(const int* hist, int nbins, int need, int* wtmp, int* o_digit) {
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int per = (nbins + bd - 1) / bd;
+  int s = 0;
+  for (int q = 0; q < per; ++q) {
+    const int d = nbins - 1 - tid * per - q;
+    if (d >= 0) s += hist[d];
+  }
+  int tot;
+  const int excl = block_exclusive_scan(s, wtmp, &tot);
+  if (excl < need && need <= excl + s) {
+    int acc = excl;
+    for (int q = 0; q < per; ++q) {
+      const int d = nbins - 1 - tid * per - q;
+      if (d < 0) break;
+      if (acc + hist[d] >= need) {
+        *o_digit = d;
+        break;
+      }
+      acc += hist[d];
+    }
+  }
+  __syncthreads();
+}
+
+__global__ __launch_bounds__(512) void k_route_select_fast(RouteParams p) {
+  __shared__ int hist[4096];
+  __shared__ uint64_t list[LIST_CAP];
+  __shared__ int pre[LIST_CAP];
+  __shared__ int wtmp[16];
+  __shared__ uint32_t mm_tmp[16];
+  __shared__ int s_digit, s_cnt, s_nsel;
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int t = blockIdx.x;
+  const QV v = qversion(p, t);
+  const StoreView ep = p.ep[v.r % 3];
+  int* cand = p.cand + (size_t)t * p.cand_ld;
+  const int n_sink = (int)(v.n < p.S ? v.n : p.S);
+  const int n_open = v.n > v.open_lo ? (int)(v.n - v.open_lo) : 0;
+  const int base_len = n_sink + n_open;
+  for (int i = tid; i < base_len; i += bd)
+    cand[i] = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+  if (p.dbg_version && tid == 0) {
+    p.dbg_version[4 * t + 0] = v.r;
+    p.dbg_version[4 * t + 1] = v.m;
+    p.dbg_version[4 * t + 2] = v.cvis;
+    p.dbg_version[4 * t + 3] = (int)v.open_lo;
+  }
+  const int room = p.budget - base_len;
+  if (room <= 0 || v.cvis == 0) {
+    if (tid == 0) {
+      p.cand_len[t] = base_len;
+      p.redo[t] = 0;
+      if (p.dbg_n_order) p.dbg_n_order[t] = 0;
+    }
+    return;
+  }
+  const float* srep = p.srep + (size_t)t * p.srep_ld;
+  for (int i = tid; i < 4096; i += bd) hist[i] = 0;
+  if (tid == 0) {
+    s_cnt = 0;
+    s_digit = 0;
+    s_nsel = 0;
+  }
+  __syncthreads();
+  // linear bins over [min, max] of the live clusters' score keys
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
+  for (int s = tid; s < v.cvis; s += bd) {
+    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
+    if (sz > 0) {
+      const uint32_t o = order_bits(srep[s]);
+      mn = o < mn ? o : mn;
+      mx = o > mx ? o : mx;
+    }
+  }
+  block_minmax(mn, mx, mm_tmp);
+  const ValBins bins = make_bins(mn, mx < mn ? mn : mx, 4096);
+  int mine = 0;
+  for (int s = tid; s < v.cvis; s += bd) {
+    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
+    if (sz > 0) {
+      atomicAdd(&hist[bins(order_bits(srep[s]))], sz);
+      mine += sz;
+    }
+  }
+  int total;
+  block_exclusive_scan(mine, wtmp, &total);
+  // total <= room: every live cluster is taken (bin 0 and up)
+  if (total > room) find_bin_desc(hist, 4096, room, wtmp, &s_digit);
+  const uint32_t cut_bin = (uint32_t)s_digit;
+  for (int s = tid; s < v.cvis; s += bd) {
+    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
+    if (sz > 0) {
+      const float x = srep[s];
+      if (bins(order_bits(x)) >= cut_bin) {
+        const int i = atomicAdd(&s_cnt, 1);
+        if (i < LIST_CAP) list[i] = make_comp(x, (uint32_t)s);
+      }
+    }
+  }
+  __syncthreads();
+  const int cnt = s_cnt;
+  if (cnt > (p.list_cap > 0 ? min(p.list_cap, LIST_CAP) : LIST_CAP)) {
+    if (tid == 0) p.redo[t] = 1;
+    return;
+  }
+  const int P2 = next_pow2(cnt);
+  for (int i = cnt + tid; i < P2; i += bd) list[i] = 0ull;
+  __syncthreads();
+  bitonic_sort_desc(list, P2);
+  // prefix sums of member counts in rank order
+  int run = 0;
+  for (int b0 = 0; b0 < cnt; b0 += bd) {
+    const int i = b0 + tid;
+    int sz = 0;
+    if (i < cnt) {
+      const int s = (int)comp_id(list[i]);
+      sz = (s < v.split ? ep.size : p.seal.size)[s];
+    }
+    int tot;
+    const int ex = block_exclusive_scan(sz, wtmp, &tot);
+    if (i < cnt) pre[i] = run + ex;
+    run += tot;
+    __syncthreads();
+  }
+  const int used = min(room, run);
+  for (int i = tid; i < cnt; i += bd)
+    if (pre[i] < used && (i == cnt - 1 || pre[i + 1] >= used)) s_nsel = i + 1;
+  __syncthreads();
+  const int nsel = s_nsel;
+  for (int c = tid; c < used; c += bd) {
+    int lo = 0, hi = nsel - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+    }
+    const int s = (int)comp_id(list[lo]);
+    const bool from_epoch = s < v.split;
+    const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
+    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[off + (c - pre[lo])];
+  }
+  if (p.dbg_order) {
+    for (int i = tid; i < nsel && i < p.dbg_order_cap; i += bd) {
+      const int s = (int)comp_id(list[i]);
+      const int sz = (s < v.split ? ep.size : p.seal.size)[s];
+      p.dbg_order[(size_t)t * p.dbg_order_cap + i] = s;
+      if (p.dbg_take) p.dbg_take[(size_t)t * p.dbg_order_cap + i] = min(sz, room - pre[i]);
+    }
+  }
+  if (tid == 0) {
+    p.cand_len[t] = base_len + used;
+    p.redo[t] = 0;
+    if (p.dbg_n_order) p.dbg_n_order[t] = nsel;
+  }
+}
+
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s) {
+  hipLaunchKernelGGL(k_route_select_fast, dim3(p.T), dim3(512), 0, s, p);
+  hipError_t e0 = hipGetLastError();
+  if (e0 != hipSuccess) return e0;
   const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);
   const size_t lds = (size_t)slot_pow2 * (sizeof(uint64_t) + sizeof(int));
   hipError_t e = hipFuncSetAttribute((const void*)k_route_select, hipFuncAttributeMaxDynamicSharedMemorySize,

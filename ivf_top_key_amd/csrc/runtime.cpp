@@ -23,7 +23,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/ivftk.h"
+#include "ivftk.h"
 #include "launch.h"
 
 using namespace ivftk;
@@ -94,6 +94,7 @@ struct idx_index {
   float* srep = nullptr;
   int* cand = nullptr;
   int* cand_len = nullptr;
+  int* redo = nullptr;
   std::vector<void*> allocs;
   int64_t bytes = 0;
   int64_t n_keys = 0;
@@ -197,7 +198,8 @@ int idx_create(const idx_config* cfg, idx_index** out) {
   }
   {
     auto p2 = [](int64_t n) { int64_t p = 1; while (p < n) p <<= 1; return p; };
-    const int64_t lds = (p2(ix->cand_cap) + p2(c.max_k)) * 8 + 4096;
+    // rescore block: winners + cut-bin buffer (8 B each), score keys (4 B), ~20 KB static
+    const int64_t lds = (p2(c.max_k) + 1024) * 8 + p2(ix->cand_cap) * 4 + 20480;
     if (lds > (int64_t)LDS_BYTES) {
       delete ix;
       return fail(IDX_ECAPACITY, "max(budget, n_sink + window) and max_k do not fit one block's LDS");
@@ -210,7 +212,7 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->sl_rep, ix->slot_cap * ix->RB) && ix->alloc(&ix->sl_rsc, ix->slot_cap) &&
             ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
             ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
-            ix->alloc(&ix->cand_len, c.max_queries);
+            ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries);
   if (ok && ix->wpr) {
     for (int i = 0; i < 3 && ok; ++i) {
       EpochStore& e = ix->ep[i];
@@ -434,6 +436,7 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
   p.cand = ix->cand;
   p.cand_ld = ix->cand_cap;
   p.cand_len = ix->cand_len;
+  p.redo = ix->redo;
   p.topk_idx = topk_idx;
   p.topk_score = topk_score;
   if (dbg) {
@@ -442,6 +445,9 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
     p.dbg_order_cap = dbg->order_cap;
     p.dbg_n_order = dbg->n_order;
     p.dbg_version = dbg->version;
+    p.list_cap = dbg->list_cap;
+    p.dbg_cand_scores = dbg->cand_scores;
+    p.dbg_cand_ld = dbg->cand_cap;
   }
   const int max_slots = windows_in(q_pos0 + T) * ix->Cs;
   hipEvent_t* ev = (dbg && dbg->events) ? reinterpret_cast<hipEvent_t*>(dbg->events) : nullptr;

@@ -18,34 +18,36 @@ namespace ivftk {
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
   using G = Geo<DT, D>;
+  __shared__ float wq_s[4][HT * 32];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
   const int tl = blockIdx.x * 4 + wave;
-  if (tl >= p.Tb) return;
   const int t = p.t0 + tl;
+  const bool active = tl < p.Tb;
+  if (active)
+    load_query_weights<HT>(wq_s[wave], p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr,
+                           p.H);
+  __syncthreads();
+  if (!active) return;
   const int64_t n = p.q_pos0 + t + 1;
   const int64_t j0 = (int64_t)blockIdx.y * p.kchunk;
   const int64_t j1 = (j0 + p.kchunk < n) ? j0 + p.kchunk : n;
   if (j0 >= j1) return;
   QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
-                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
   float* out = p.ws + (size_t)tl * p.ld;
-  uint32_t ba[G::HW], bb[G::HW];
-  for (int64_t jb = j0; jb < j1; jb += 64) {
-    const int64_t ja = jb + col, jbb = jb + 32 + col;
-    const int64_t ca = ja < j1 ? ja : j1 - 1;
-    const int64_t cb = jbb < j1 ? jbb : j1 - 1;
-    load_half_row<DT, D>(ba, p.keys + (size_t)ca * G::RB);
-    load_half_row<DT, D>(bb, p.keys + (size_t)cb * G::RB);
-    float sa = score_tile<DT, D, HT>(f, ba);
-    if constexpr (DT == DT_E4M3) sa *= p.kscale[ca];
-    if (lane < 32 && ja < j1) out[ja] = sa;
-    if (jb + 32 < j1) {
-      float sb = score_tile<DT, D, HT>(f, bb);
-      if constexpr (DT == DT_E4M3) sb *= p.kscale[cb];
-      if (lane < 32 && jbb < j1) out[jbb] = sb;
-    }
-  }
+  const int nblk = (int)((j1 - j0 + 31) >> 5);
+  score_blocks<DT, D, HT, 3>(
+      f, wq_s[wave], 0, 1, nblk,
+      [&](int blk, uint32_t* buf, float& sc) {
+        int64_t j = j0 + blk * 32 + col;
+        j = j < j1 ? j : j1 - 1;
+        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
+        sc = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
+      },
+      [&](int blk, float x) {
+        const int64_t j = j0 + blk * 32 + col;
+        if (lane < 32 && j < j1) out[j] = x;
+      });
 }
 
 template <int DT, int D, int HT>
@@ -247,29 +249,37 @@ __device__ __forceinline__ StoreView epoch_store(const RouteParams& p, int r) { 
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
   using G = Geo<DT, D>;
+  __shared__ float wq_s[4][HT * 32];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
   const int t = blockIdx.x * 4 + wave;
-  if (t >= p.T) return;
+  const bool active = t < p.T;
+  if (active)
+    load_query_weights<HT>(wq_s[wave], p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr,
+                           p.H);
+  __syncthreads();
+  if (!active) return;
   const QVer v = query_version(p, t);
   const int s0 = blockIdx.y * chunk;
   const int s1 = min(v.cvis, s0 + chunk);
   if (s0 >= s1) return;
   const StoreView ep = epoch_store(p, v.r);
   QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
-                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
   float* out = p.srep + (size_t)t * p.srep_ld;
-  uint32_t b[G::HW];
-  for (int sb = s0; sb < s1; sb += 32) {
-    const int s = sb + col;
-    const int sc = s < s1 ? s : s1 - 1;
-    const bool from_epoch = sc < v.split;
-    const uint8_t* rep = from_epoch ? ep.rep : p.seal.rep;
-    load_half_row<DT, D>(b, rep + (size_t)sc * G::RB);
-    float x = score_tile<DT, D, HT>(f, b);
-    if constexpr (DT == DT_E4M3) x *= (from_epoch ? ep.rsc : p.seal.rsc)[sc];
-    if (lane < 32 && s < s1) out[s] = x;
-  }
+  const int nblk = (s1 - s0 + 31) >> 5;
+  score_blocks<DT, D, HT, 3>(
+      f, wq_s[wave], 0, 1, nblk,
+      [&](int blk, uint32_t* buf, float& sc) {
+        int s = s0 + blk * 32 + col;
+        s = s < s1 ? s : s1 - 1;
+        const bool from_epoch = s < v.split;
+        load_half_row<DT, D>(buf, (from_epoch ? ep.rep : p.seal.rep) + (size_t)s * G::RB);
+        sc = (DT == DT_E4M3) ? (from_epoch ? ep.rsc : p.seal.rsc)[s] : 1.0f;
+      },
+      [&](int blk, float x) {
+        const int s = s0 + blk * 32 + col;
+        if (lane < 32 && s < s1) out[s] = x;
+      });
 }
 
 template <int DT, int D, int HT>
@@ -287,48 +297,159 @@ hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, in
 // ---------------------------------------------------------------------------
 // candidate rescoring + top-k: one block per query
 // ---------------------------------------------------------------------------
+// Scores of the candidates stay in LDS as 32-bit order keys; a 32-bit radix select
+// finds the k-th score, ties at that score go to the lowest positions, and the k
+// winners are sorted by (score desc, position asc).  Key rows are gathered one
+// block of 32 ahead of the MFMA work so a wave always has loads in flight.
+constexpr int RS_NBIN = 2048;      // linear bins of the top-k histogram
+constexpr int RS_TIE_CAP = 1024;   // largest cut bin resolved by a local sort
+
 template <int DT, int D, int HT>
-__global__ __launch_bounds__(512) void k_rescore_topk(RouteParams p, int cap_pow2, int k_pow2) {
+__global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow2, int k_pow2) {
   using G = Geo<DT, D>;
   extern __shared__ uint64_t lds[];
-  uint64_t* buf = lds;               // [cap_pow2]
-  uint64_t* sel = lds + cap_pow2;    // [k_pow2]
-  __shared__ SelectScratch sc;
-  __shared__ int s_cnt;
+  __shared__ float wq_s[HT * 32];
+  uint64_t* sel = lds;                                                     // [k_pow2] winners
+  uint64_t* tie = lds + k_pow2;                                            // [RS_TIE_CAP] cut bin
+  uint32_t* okey = reinterpret_cast<uint32_t*>(lds + k_pow2 + RS_TIE_CAP);  // [cap_pow2] score keys
+  __shared__ Select32Scratch sc;
+  __shared__ int hist[RS_NBIN];
+  __shared__ int offs[RS_NBIN];
+  __shared__ uint32_t mm_tmp[16];
+  __shared__ int wtmp[16];
+  __shared__ int s_cnt, s_tie, s_bstar;
   const int tid = threadIdx.x, bd = blockDim.x;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
   const int t = blockIdx.x;
   const int L = p.cand_len[t];
   const int* cand = p.cand + (size_t)t * p.cand_ld;
   const int K = p.k;
+  const int nk1 = (int)(p.n_keys - 1);
+  if (wave == 0)
+    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
   QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.w + (size_t)t * p.H,
-                        p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
-  uint32_t b[G::HW];
-  for (int blk = wave; blk * 32 < L; blk += nw) {
-    const int i = blk * 32 + col;
-    int j = cand[i < L ? i : L - 1];
-    j = j < 0 ? 0 : (j >= p.n_keys ? (int)(p.n_keys - 1) : j);   // guard against corrupt lists
-    load_half_row<DT, D>(b, p.keys + (size_t)j * G::RB);
-    float x = score_tile<DT, D, HT>(f, b);
-    if constexpr (DT == DT_E4M3) x *= p.kscale[j];
-    if (lane < 32 && i < L) buf[i] = make_comp(x, (uint32_t)j);
-  }
-  const int P2 = next_pow2(L > 0 ? L : 1);
-  for (int i = L + tid; i < P2; i += bd) buf[i] = 0ull;
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
+  __syncthreads();
+  const int nb = (L + 31) >> 5;
+  score_blocks<DT, D, HT, 3>(
+      f, wq_s, wave, nw, nb,
+      [&](int blk, uint32_t* buf, float& sc) {
+        const int i = blk * 32 + col;
+        int j = cand[i < L ? i : L - 1];
+        j = j < 0 ? 0 : (j > nk1 ? nk1 : j);
+        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
+        sc = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
+      },
+      [&](int blk, float x) {
+        const int i = blk * 32 + col;
+        if (lane < 32 && i < L) {
+          okey[i] = order_bits(x);
+          if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x;
+        }
+      });
   if (tid == 0) s_cnt = 0;
   __syncthreads();
   int* oi = p.topk_idx + (size_t)t * K;
   float* os = p.topk_score ? p.topk_score + (size_t)t * K : nullptr;
+  auto comp_of = [&](int i) -> uint64_t { return ((uint64_t)okey[i] << 32) | (uint64_t)(~(uint32_t)cand[i]); };
+  auto put = [&](int idx, uint64_t v) {
+    oi[idx] = (int)comp_id(v);
+    if (os) os[idx] = comp_score(v);
+  };
   if (L <= K) {
-    bitonic_sort_desc(buf, P2);
-    write_topk(buf, P2 < L ? P2 : L, K, oi, os);
+    const int P2 = next_pow2(L > 0 ? L : 1);
+    for (int i = tid; i < P2; i += bd) sel[i] = i < L ? comp_of(i) : 0ull;
+    __syncthreads();
+    bitonic_sort_desc(sel, P2);
+    write_topk(sel, L, K, oi, os);
     return;
   }
-  const uint64_t thr = radix_select_desc(buf, nullptr, L, K, sc);
+  // ---- linear-bin histogram over [min, max] of the score keys ----
+  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
   for (int i = tid; i < L; i += bd) {
-    const uint64_t v = buf[i];
-    if (v >= thr) sel[atomicAdd(&s_cnt, 1)] = v;
+    const uint32_t v = okey[i];
+    mn = v < mn ? v : mn;
+    mx = v > mx ? v : mx;
+  }
+  block_minmax(mn, mx, mm_tmp);
+  bool fallback = (mn == mx);
+  ValBins bins;
+  int bstar = 0, above = 0, in_bin = 0;
+  if (!fallback) {
+    bins = make_bins(mn, mx, RS_NBIN);
+    for (int i = tid; i < RS_NBIN; i += bd) hist[i] = 0;
+    __syncthreads();
+    for (int i = tid; i < L; i += bd) atomicAdd(&hist[bins(okey[i])], 1);
+    __syncthreads();
+    // offs[b] = entries in bins above b (descending order); the bin holding the K-th
+    const int per = RS_NBIN / bd;
+    int sum = 0;
+    for (int q = 0; q < per; ++q) sum += hist[RS_NBIN - 1 - tid * per - q];
+    int tot;
+    int run = block_exclusive_scan(sum, wtmp, &tot);
+    for (int q = 0; q < per; ++q) {
+      const int bb = RS_NBIN - 1 - tid * per - q;
+      const int c = hist[bb];
+      offs[bb] = run;
+      if (run < K && K <= run + c) s_bstar = bb;
+      run += c;
+    }
+    __syncthreads();
+    bstar = s_bstar;
+    above = offs[bstar];
+    in_bin = hist[bstar];
+    fallback = in_bin > RS_TIE_CAP;
+    __syncthreads();   // every thread has read hist[bstar] before hist becomes the cursors
+  }
+  if (!fallback) {
+    // scatter: bins above the cut go to their bin's range of sel, the cut bin to tie
+    for (int i = tid; i < RS_NBIN; i += bd) hist[i] = offs[i];
+    if (tid == 0) s_tie = 0;
+    __syncthreads();
+    for (int i = tid; i < L; i += bd) {
+      const uint32_t v = okey[i];
+      const uint32_t bb = bins(v);
+      if ((int)bb > bstar) sel[atomicAdd(&hist[bb], 1)] = comp_of(i);
+      else if ((int)bb == bstar) tie[atomicAdd(&s_tie, 1)] = comp_of(i);
+    }
+    const int P2 = next_pow2(in_bin);
+    __syncthreads();
+    for (int i = in_bin + tid; i < P2; i += bd) tie[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(tie, P2);
+    for (int r = tid; r < K - above; r += bd) put(above + r, tie[r]);
+    // entries above the cut: final index = bin start + rank inside the bin
+    for (int i = tid; i < above; i += bd) {
+      const uint64_t v = sel[i];
+      const int bb = (int)bins((uint32_t)(v >> 32));
+      const int lo = offs[bb], hi = offs[bb - 1];
+      int rank = 0;
+      for (int j = lo; j < hi; ++j) rank += sel[j] > v;
+      put(lo + rank, v);
+    }
+    return;
+  }
+  // ---- fallback: exact radix select (all keys equal, or a crowded cut bin) ----
+  const uint32_t thr = radix_select32_desc(okey, L, K, sc);
+  const int above_r = sc.above;
+  const int need = K - above_r;
+  const int n_eq = sc.hist[thr & 255u];
+  __syncthreads();
+  for (int i = tid; i < L; i += bd) {
+    const uint32_t v = okey[i];
+    if (v > thr || (v == thr && n_eq == need)) sel[atomicAdd(&s_cnt, 1)] = comp_of(i);
+  }
+  __syncthreads();
+  if (n_eq != need) {
+    // more candidates share the k-th score than slots remain: lowest positions win
+    for (int i = tid; i < L; i += bd) okey[i] = (okey[i] == thr) ? ~(uint32_t)cand[i] : 0u;
+    __syncthreads();
+    const uint32_t t2 = radix_select32_desc(okey, L, need, sc);
+    for (int i = tid; i < L; i += bd) {
+      const uint32_t v = okey[i];
+      if (v != 0u && v >= t2) sel[atomicAdd(&s_cnt, 1)] = ((uint64_t)thr << 32) | (uint64_t)v;
+    }
+    __syncthreads();
   }
   for (int i = K + tid; i < k_pow2; i += bd) sel[i] = 0ull;
   __syncthreads();
@@ -340,11 +461,11 @@ template <int DT, int D, int HT>
 static hipError_t launch_rescore_topk_t(const RouteParams& p, int cand_cap, hipStream_t s) {
   const int cap_pow2 = next_pow2(cand_cap);
   const int k_pow2 = next_pow2(p.k);
-  const size_t lds = (size_t)(cap_pow2 + k_pow2) * sizeof(uint64_t);
+  const size_t lds = (size_t)(k_pow2 + RS_TIE_CAP) * sizeof(uint64_t) + (size_t)cap_pow2 * sizeof(uint32_t);
   hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT>), dim3(p.T), dim3(512), lds, s, p, cap_pow2, k_pow2);
+  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT>), dim3(p.T), dim3(256), lds, s, p, cap_pow2, k_pow2);
   return hipGetLastError();
 }
 

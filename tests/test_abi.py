@@ -53,7 +53,7 @@ def _cfg(**over):
     (dict(dtype=1, dim=32), -7), (dict(window=1000), -1), (dict(cluster_size=64), -7),
     (dict(seal_cap=100), -1), (dict(seal_iters=0), -1), (dict(refit_every=1000), -1),
     (dict(max_k=5000), -1), (dict(max_budget=100), -1), (dict(max_keys=0), -1),
-    (dict(max_keys=1 << 21), -6), (dict(max_budget=16384, max_k=4096), -6),
+    (dict(max_keys=1 << 21), -6), (dict(max_budget=32768, max_k=4096), -6),
 ])
 def test_create_rejects_bad_config(lib, over, code):
     h = ctypes.c_void_p()

@@ -20,7 +20,7 @@ from oracle.score import indexer_scores, score_error_scale
 pytestmark = pytest.mark.gpu
 
 
-def route_parity(name, budget=None, k=None, T=None, q_pos0=None, **over):
+def route_parity(name, budget=None, k=None, T=None, q_pos0=None, list_cap=0, **over):
     import torch
     import ivf_top_key_amd as ivf
     ensure_built()
@@ -44,10 +44,11 @@ def route_parity(name, budget=None, k=None, T=None, q_pos0=None, **over):
         cand_cap = max(budget, cfg.n_sink + cfg.window) + 32
         n_slots = ((q_pos0 + T - cfg.n_sink) // cfg.window) * cfg.n_clusters
         dbg = ivf.make_route_debug(T, cand_cap, max(n_slots, 1), max(n_slots, 1))
+        dbg["list_cap"] = list_cap
         idx, sc = ivf.idx_route_topk(gix, q, qs, w, q_pos0, k, budget, debug=dbg)
         torch.cuda.synchronize()
         idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
-        d = {kk: v.cpu().numpy() for kk, v in dbg.items()}
+        d = {kk: v.cpu().numpy() for kk, v in dbg.items() if hasattr(v, "cpu")}
         qraw = inp["q"][:T]
         qsc = None if inp["q_scale"] is None else inp["q_scale"][:T]
         ridx, rsc, odbg = oix.route(qraw, qsc, inp["w"][:T], q_pos0, k, budget, debug=True)
@@ -94,6 +95,11 @@ def route_parity(name, budget=None, k=None, T=None, q_pos0=None, **over):
                 cand, used = fill_budget(oix.base_candidates(od["n"]), [vis[s] for s in g_order], budget)
                 assert [s for s, _ in used] == g_order and [x for _, x in used] == g_take
                 assert np.array_equal(g_cand, cand), f"query {t}: fill with the GPU order differs"
+            # the selection itself, exactly: top k of the GPU's own candidate scores
+            gs = d["cand_scores"][t, :L]
+            order = np.lexsort((g_cand, -gs.astype(np.float64)))[:k]
+            assert np.array_equal(idx[t][:min(k, L)], g_cand[order]), f"query {t}: selection differs from " \
+                f"the exact top-k of the GPU's own scores"
             ok, ex = topk_matches(idx[t], g_cand, qv, wv, oix.kv, t, k, dt)
             assert ok, f"query {t}: top-k is not a top-k of the candidates"
             stats["topk_exempt"] += ex
@@ -134,6 +140,12 @@ def test_route_queries_straddling_windows_and_epochs():
     route_parity("c1r", q_pos0=900, T=3300, budget=1200)
 
 
+def test_route_full_cut_kernel():
+    """A tiny list capacity sends most queries to the full (radix-select) cut kernel."""
+    route_parity("c1r", list_cap=3)
+    route_parity("e4m3_small", list_cap=5)
+
+
 def test_route_sinks_and_open_window_exceed_budget():
     route_parity("c1r", budget=96, k=64, q_pos0=5000, T=200)
 
@@ -154,5 +166,42 @@ def test_route_budget_covering_prefix_is_exhaustive_bit_exact():
         torch.cuda.synchronize()
         assert torch.equal(idx, eidx)
         assert torch.equal(sc.view(torch.int32), esc.view(torch.int32))
+    finally:
+        ivf.idx_destroy(gix)
+
+
+@pytest.mark.parametrize("zero_queries", [False, True])
+def test_route_exact_ties(zero_queries):
+    """Integer-valued fp32 keys and queries give exactly equal scores (all zero when
+    the queries are zero): GPU and oracle must then agree exactly, ties going to the
+    lower position (the crowded-cut-bin and all-equal paths of the top-k)."""
+    import torch
+    import ivf_top_key_amd as ivf
+    from oracle import OracleConfig, OracleIndex
+    ensure_built()
+    rng = np.random.default_rng(11)
+    N, T, H, d, k, budget = 6000, 200, 4, 32, 300, 1500
+    keys = rng.integers(-1, 2, (N, d)).astype(np.float32)
+    q = np.zeros((T, H, d), np.float32) if zero_queries else rng.integers(0, 2, (T, H, d)).astype(np.float32)
+    w = np.ones((T, H), np.float32)
+    cfg = dict(heads=H, dim=d, dtype="f32", n_sink=4, window=1024, cluster_size=128, seal_cap=256,
+               seal_iters=3, refit_every=2048)
+    gix = ivf.idx_create(max_keys=N, max_queries=T, max_budget=budget, max_k=k, **cfg)
+    try:
+        kd = to_dev(keys)
+        ivf.idx_build_seal(gix, kd)
+        while ivf.idx_refit(gix):
+            ivf.idx_publish(gix)
+        q_pos0 = N - T
+        idx, sc = ivf.idx_route_topk(gix, to_dev(q), None, to_dev(w), q_pos0, k, budget)
+        torch.cuda.synchronize()
+        oix = OracleIndex(OracleConfig(**cfg))
+        oix.append(keys)
+        while oix.refit_due():
+            oix.refit()
+            oix.publish()
+        ridx, rsc = oix.route(q, None, w, q_pos0, k, budget)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)
     finally:
         ivf.idx_destroy(gix)
