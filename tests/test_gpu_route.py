@@ -12,7 +12,8 @@ GPU's exhaustive output (same scores through the same score tile)."""
 import numpy as np
 import pytest
 
-from gpu_common import (RTOL, ensure_built, gpu_index, oracle_index, say, to_dev, topk_matches, workload)
+from gpu_common import (RTOL, check_routed_query, ensure_built, gpu_index, oracle_index, say, to_dev,
+                        topk_matches, workload)
 from oracle import fill_budget
 from oracle.index import query_values
 from oracle.score import indexer_scores, score_error_scale
@@ -49,6 +50,7 @@ def route_parity(name, budget=None, k=None, T=None, q_pos0=None, list_cap=0, **o
         torch.cuda.synchronize()
         idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
         d = {kk: v.cpu().numpy() for kk, v in dbg.items() if hasattr(v, "cpu")}
+        d["topk_idx"], d["topk_score"] = idx, sc
         qraw = inp["q"][:T]
         qsc = None if inp["q_scale"] is None else inp["q_scale"][:T]
         ridx, rsc, odbg = oix.route(qraw, qsc, inp["w"][:T], q_pos0, k, budget, debug=True)
@@ -56,62 +58,7 @@ def route_parity(name, budget=None, k=None, T=None, q_pos0=None, list_cap=0, **o
         wv = inp["w"][:T].astype(np.float64)
         stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
         for t in range(T):
-            od = odbg[t]
-            r, m = od["epoch"], od["windows"]
-            assert d["version"][t].tolist() == [r, m, m * cfg.n_clusters, cfg.n_sink + m * cfg.window], \
-                f"query {t}: version {d['version'][t].tolist()} vs ({r}, {m})"
-            vis = {c.slot: c for c in oix.visible(od["n"])}
-            # representative scores of visible live slots
-            if vis:
-                slots = np.array(sorted(vis))
-                reps = np.stack([vis[s].rep_value for s in slots])
-                ref = indexer_scores(qv[t:t + 1], wv[t:t + 1], reps)[0]
-                sig = score_error_scale(qv[t:t + 1], wv[t:t + 1], reps)[0]
-                err = np.abs(d["rep_scores"][t, slots].astype(np.float64) - ref)
-                assert np.all(err <= RTOL[dt] * sig + 1e-30), f"query {t}: representative score error"
-                srep = dict(zip(slots.tolist(), ref.tolist()))
-                ssig = dict(zip(slots.tolist(), sig.tolist()))
-            n_ord = int(d["n_order"][t])
-            g_order = d["order"][t, :n_ord].tolist()
-            g_take = d["order_take"][t, :n_ord].tolist()
-            o_used = od["used"]
-            L = int(d["cand_len"][t])
-            g_cand = d["cand"][t, :L]
-            if [s for s, _ in o_used] == g_order:
-                assert [tk for _, tk in o_used] == g_take, f"query {t}: takes differ"
-                assert np.array_equal(g_cand, od["cand"]), f"query {t}: candidate list differs"
-            else:
-                # near ties only: a valid ranking under the tolerance, and the oracle's
-                # fill with this order reproduces the GPU's list exactly
-                stats["order_swaps"] += 1
-                tol = lambda a, b: 2 * RTOL[dt] * max(ssig[a], ssig[b])
-                for a, b in zip(g_order, g_order[1:]):
-                    assert srep[a] >= srep[b] - tol(a, b), f"query {t}: clusters {a},{b} out of order"
-                chosen = set(g_order)
-                last = g_order[-1]
-                for u in vis:
-                    if u not in chosen:
-                        assert srep[u] <= srep[last] + tol(u, last), f"query {t}: skipped cluster {u}"
-                cand, used = fill_budget(oix.base_candidates(od["n"]), [vis[s] for s in g_order], budget)
-                assert [s for s, _ in used] == g_order and [x for _, x in used] == g_take
-                assert np.array_equal(g_cand, cand), f"query {t}: fill with the GPU order differs"
-            # the selection itself, exactly: top k of the GPU's own candidate scores
-            gs = d["cand_scores"][t, :L]
-            order = np.lexsort((g_cand, -gs.astype(np.float64)))[:k]
-            assert np.array_equal(idx[t][:min(k, L)], g_cand[order]), f"query {t}: selection differs from " \
-                f"the exact top-k of the GPU's own scores"
-            ok, ex = topk_matches(idx[t], g_cand, qv, wv, oix.kv, t, k, dt)
-            assert ok, f"query {t}: top-k is not a top-k of the candidates"
-            stats["topk_exempt"] += ex
-            valid = idx[t] >= 0
-            assert valid.sum() == min(k, L)
-            gj = idx[t][valid]
-            ref = indexer_scores(qv[t:t + 1], wv[t:t + 1], oix.kv[gj])[0]
-            sig = score_error_scale(qv[t:t + 1], wv[t:t + 1], oix.kv[gj])[0]
-            err = np.abs(sc[t][valid].astype(np.float64) - ref)
-            assert np.all(err <= RTOL[dt] * sig + 1e-30), f"query {t}: candidate score error"
-            if err.size:
-                stats["max_err"] = max(stats["max_err"], float(np.max(err / np.maximum(sig, 1e-300))))
+            check_routed_query(t, d, odbg[t], oix, qv, wv, k, budget, dt, stats)
         say(f"  ok {stats}")
         return stats
     finally:

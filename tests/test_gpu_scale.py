@@ -1,0 +1,175 @@
+"""GPU parity at the full benchmark sizes, on outputs the oracle can compute one by one.
+
+1M-token prefix, E4M3 (the benchmark's workload, index built by streaming 16384 keys
+at a time with every refit published, 4096 tail queries routed in one call, k=2048,
+budget 8192), and 32K bf16 (4096 queries).  Checked:
+* exhaustive top-k of sampled queries against the oracle's float64 top-k;
+* sampled sealed windows recomputed by the oracle, bit for bit;
+* sampled clusters of the newest epoch: centroid = exact-order mean of its
+  members, members ascending, representative = the oracle's quantisation;
+* the newest refit's assignment of sampled keys = nearest warm-start centroid
+  (epoch r-1's centroids and the newer seal centroids, fp32 exact order);
+* routed top-k of sampled queries = the oracle's routing over the published
+  clusters (a property of the routing step: the clusters come from the library,
+  everything after them is recomputed by the oracle).
+"""
+import numpy as np
+import pytest
+
+from gpu_common import RTOL, ensure_built, say, to_dev, topk_matches, workload
+from oracle import OracleConfig, OracleIndex
+from oracle.index import exhaustive_topk, key_values, make_cluster, query_values
+from oracle.kmeans import mean_exact, nearest, seal_window, sqdist_exact
+from oracle import codec
+
+pytestmark = pytest.mark.gpu
+
+
+def _build(wl, inp, ivf, chunk):
+    import torch
+    N = wl["N"]
+    ix = ivf.idx_create(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], max_keys=N, n_sink=wl["n_sink"],
+                        window=wl["window"], cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"],
+                        seal_iters=wl["seal_iters"], refit_every=wl["refit_every"], max_queries=wl["T"],
+                        max_budget=16384, max_k=wl["k"])
+    keys = to_dev(inp["keys"])
+    ks = to_dev(inp["k_scale"]) if inp["k_scale"] is not None else None
+    for a in range(0, N, chunk):
+        ivf.idx_build_seal(ix, keys[a:a + chunk], None if ks is None else ks[a:a + chunk])
+        while ivf.idx_refit(ix):
+            ivf.idx_publish(ix)
+    torch.cuda.synchronize()
+    return ix, keys, ks
+
+
+def _clusters(exp, dtype):
+    out = []
+    for s in range(exp["sizes"].shape[0]):
+        sz, off = int(exp["sizes"][s]), int(exp["offsets"][s])
+        out.append(make_cluster(s, exp["members"][off:off + sz].astype(np.int64), exp["centroids"][s], dtype))
+    return out
+
+
+def _scale_case(name, n_exh, n_route, n_windows, n_slots, n_keys_assign, seed):
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload(name)
+    dt, T, k, q_pos0, N = wl["dtype"], wl["T"], wl["k"], wl["q_pos0"], wl["N"]
+    say(f"scale {name}: N={N} dtype={dt} T={T}")
+    ix, keys, ks = _build(wl, inp, ivf, wl["refit_every"])
+    rng = np.random.default_rng(seed)
+    try:
+        q = to_dev(inp["q"])
+        qs = to_dev(inp["q_scale"]) if inp["q_scale"] is not None else None
+        w = to_dev(inp["w"])
+        Cs = wl["window"] // wl["cluster_size"]
+        vis_slots = ((q_pos0 + T - wl["n_sink"]) // wl["window"]) * Cs
+        cand_cap = wl["budget"] + 32
+        dbg = ivf.make_route_debug(T, cand_cap, vis_slots, vis_slots)
+        idx, sc = ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, wl["budget"], debug=dbg)
+        ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(N, 256) // 4, dtype=torch.float32, device="cuda")
+        eidx, esc = ivf.idx_exhaustive_topk(keys, ks, dt, wl["H"], q, qs, w, q_pos0, k, workspace=ws)
+        torch.cuda.synchronize()
+        idx, sc, eidx, esc = idx.cpu().numpy(), sc.cpu().numpy(), eidx.cpu().numpy(), esc.cpu().numpy()
+        info = ivf.idx_get_info(ix)
+        P = info["published_epoch"]
+        kv = key_values(inp["keys"], inp["k_scale"], dt)
+        X = codec.dequantize(inp["keys"], inp["k_scale"], dt)
+        qv = query_values(inp["q"], inp["q_scale"], dt)
+        wv = inp["w"].astype(np.float64)
+
+        # exhaustive: sampled queries against float64
+        pick = np.sort(rng.choice(T, n_exh, replace=False))
+        for t in pick:
+            n = q_pos0 + t + 1
+            ok, ex = topk_matches(eidx[t], np.arange(n), qv, wv, kv, t, k, dt)
+            assert ok, f"exhaustive query {t}"
+        say(f"  exhaustive: {n_exh} sampled queries match")
+
+        # sealed windows recomputed by the oracle
+        seal = ivf.idx_export(ix, -1)
+        Cs = wl["window"] // wl["cluster_size"]
+        S, W = wl["n_sink"], wl["window"]
+        for wi in rng.choice(info["sealed_windows"], n_windows, replace=False):
+            lo = S + wi * W
+            a, C, alive = seal_window(X[lo:lo + W], Cs, wl["seal_cap"], wl["seal_iters"])
+            for c in range(Cs):
+                s = wi * Cs + c
+                mem = lo + np.nonzero(a == c)[0]
+                off, sz = int(seal["offsets"][s]), int(seal["sizes"][s])
+                assert sz == mem.size and np.array_equal(seal["members"][off:off + sz], mem), f"window {wi}"
+                assert np.array_equal(seal["centroids"][s].view(np.uint32), C[c].view(np.uint32)), f"window {wi}"
+        say(f"  seal: {n_windows} sampled windows bit-exact")
+
+        # newest epoch: sampled clusters are exact means; sampled keys are nearest warm centroids
+        if P >= 1:
+            ep = ivf.idx_export(ix, P)
+            live = np.nonzero(ep["sizes"] > 0)[0]
+            for s in rng.choice(live, n_slots, replace=False):
+                off, sz = int(ep["offsets"][s]), int(ep["sizes"][s])
+                mem = ep["members"][off:off + sz].astype(np.int64)
+                assert np.all(np.diff(mem) > 0)
+                assert np.array_equal(ep["centroids"][s].view(np.uint32), mean_exact(X[mem]).view(np.uint32))
+                raw, rs = codec.quantize_rep(ep["centroids"][s], dt)
+                assert np.array_equal(ep["reps"][s], raw) and np.float32(ep["rep_scale"][s]) == rs
+            Q = ep["sizes"].shape[0] // P
+            if P >= 2:
+                prev = ivf.idx_export(ix, P - 1)
+                warm_c = np.concatenate([prev["centroids"], seal["centroids"][(P - 1) * Q:P * Q]])
+                warm_alive = np.concatenate([prev["sizes"] > 0, seal["sizes"][(P - 1) * Q:P * Q] > 0])
+            else:
+                warm_c = seal["centroids"][:Q]
+                warm_alive = seal["sizes"][:Q] > 0
+            owner = np.full(N, -1)
+            for s in range(ep["sizes"].shape[0]):
+                off, sz = int(ep["offsets"][s]), int(ep["sizes"][s])
+                owner[ep["members"][off:off + sz]] = s
+            B = S + P * wl["refit_every"]
+            assert np.all(owner[S:B] >= 0) and np.all(owner[B:] == -1)
+            alive_ids = np.nonzero(warm_alive)[0]
+            xs = rng.choice(np.arange(S, B), n_keys_assign, replace=False)
+            D = sqdist_exact(X[xs], warm_c[alive_ids])
+            assert np.array_equal(owner[xs], alive_ids[nearest(D)]), "refit assignment is not the nearest centroid"
+            say(f"  epoch {P}: {n_slots} clusters exact means, {n_keys_assign} keys nearest")
+
+        # routing of sampled queries over the published clusters
+        cfg = OracleConfig(heads=wl["H"], dim=wl["d"], dtype=dt, n_sink=S, window=W,
+                           cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"],
+                           seal_iters=wl["seal_iters"], refit_every=wl["refit_every"])
+        oix = OracleIndex(cfg)
+        oix.kv = kv
+        oix.X = X
+        sc_all = _clusters(seal, dt)
+        oix.seals = [sc_all[i:i + Cs] for i in range(0, len(sc_all), Cs)]
+        if P >= 1:
+            oix.epochs[P] = _clusters(ep, dt)
+        oix.computed = oix.published = P
+        from gpu_common import check_routed_query
+        picks = np.sort(rng.choice(T, n_route, replace=False))
+        rows = torch.from_numpy(picks).cuda()
+        d = {}
+        for kk, v in dbg.items():
+            if hasattr(v, "cpu"):
+                full = np.zeros(tuple(v.shape), dtype=v[:1].cpu().numpy().dtype)   # only sampled rows filled
+                full[picks] = v.index_select(0, rows).cpu().numpy()
+                d[kk] = full
+        d["topk_idx"], d["topk_score"] = idx, sc
+        stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
+        for t in picks:
+            _, _, od = oix.route(inp["q"][t:t + 1], None if inp["q_scale"] is None else inp["q_scale"][t:t + 1],
+                                 inp["w"][t:t + 1], q_pos0 + int(t), k, wl["budget"], debug=True)
+            check_routed_query(int(t), d, od[0], oix, qv, wv, k, wl["budget"], dt, stats)
+        say(f"  routed: {n_route} sampled queries match the oracle's routing over the published clusters {stats}")
+        rec = np.mean([np.intersect1d(a[a >= 0], b[b >= 0]).size / k for a, b in zip(idx, eidx)])
+        say(f"  recall vs exhaustive {rec:.4f}")
+    finally:
+        ivf.idx_destroy(ix)
+
+
+def test_scale_1m_e4m3():
+    _scale_case("c4", n_exh=6, n_route=24, n_windows=3, n_slots=64, n_keys_assign=400, seed=1)
+
+
+def test_scale_32k_bf16():
+    _scale_case("c2", n_exh=16, n_route=48, n_windows=4, n_slots=64, n_keys_assign=1000, seed=2)
