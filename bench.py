@@ -35,6 +35,37 @@ BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 
 
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "rescore_topk_c4_e4m3_pmc.md")
+PMC_SOURCES = ("score.hip", "dev.h", "params.h")
+
+
+def kernel_source_hash():
+    """First 16 hex digits of the sha256 over the sources the rescoring kernel is built from."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in PMC_SOURCES:
+        with open(os.path.join(ROOT, "ivf_top_key_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload, budget):
+    """HBM bytes per k_rescore_topk launch from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None when the summary
+    is for another workload or the kernel's sources changed since it was taken."""
+    if workload != "c4" or budget != 8192 or not os.path.exists(PMC_SUMMARY):
+        return None
+    vals = {}
+    with open(PMC_SUMMARY) as fh:
+        for line in fh:
+            if ":" in line and line.split(":")[0] in ("traffic_bytes_per_launch", "source_sha256_16"):
+                key, v = line.split(":", 1)
+                vals[key] = v.strip()
+    if vals.get("source_sha256_16") != kernel_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
+
+
 def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -182,7 +213,8 @@ def main():
     resc_gbs = rescore_bytes / (kern["rescore_topk"] * 1e-3) / 1e9
     if kern["rescore_topk"] >= kern["rep_score"]:
         roof = dict(kernel="rescore_topk", bound="hbm", achieved=round(resc_gbs, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(resc_gbs / HBM_PEAK_GBS, 4), traffic=None,
+                    unit="GB/s", frac=round(resc_gbs / HBM_PEAK_GBS, 4),
+                    traffic=measured_traffic(args.workload, budget),
                     algorithmic_bytes=rescore_bytes, avg_launch_ms=round(kern["rescore_topk"], 4))
     else:
         ach = rep_flops / (kern["rep_score"] * 1e-3) / 1e12
