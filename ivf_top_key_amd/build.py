@@ -23,10 +23,13 @@ SOURCES = ["score.hip", "route.hip", "seal.hip", "refit.hip", "runtime.cpp"]
 #   (no fused multiply-add); the score epilogue calls fmaf explicitly.
 # correctly rounded fp32 divide/sqrt: centroid means and representative scales.
 # packed fp32 ops are disabled for every kernel.
+# MFMA accumulators in ordinary VGPRs: the score epilogue reads all of them, and
+# the accumulation-register form would add one copy per accumulator.
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=true",
     "-I", INCLUDE, "-I", CSRC,
 ]
 

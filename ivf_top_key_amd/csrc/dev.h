@@ -16,6 +16,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#ifndef IVFTK_SWZ8
+#define IVFTK_SWZ8(r) ((r) >> 1)
+#endif
+
 namespace ivftk {
 
 enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
@@ -23,6 +27,7 @@ enum { DT_F32 = 0, DT_BF16 = 1, DT_E4M3 = 2 };
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 template <int DT>
 struct Elem;
@@ -423,10 +428,13 @@ __device__ __forceinline__ void load_half_row(uint32_t* r, const uint8_t* row) {
   }
 }
 
-// One query's A operands: HT tiles of 32 heads (rows beyond H are zero).
+// One query's A operands: HT tiles of 32 heads (rows beyond H are zero), and the
+// head weights of the accumulator rows this lane holds: w[ht][4j + e] is the
+// weight of head ht*32 + 8j + 4g + e (g = lane >> 5).
 template <int DT, int D, int HT>
 struct QueryFrag {
   uint32_t a[HT][Geo<DT, D>::HW];
+  float w[HT][16];
 };
 
 // q_t: the query's [H][RB] rows.
@@ -453,11 +461,33 @@ __device__ __forceinline__ void load_query_weights(float* wq, const float* w_t, 
   for (int h = lane; h < HT * 32; h += 64) wq[h] = (h < H) ? (qs_t ? w_t[h] * qs_t[h] : w_t[h]) : 0.0f;
 }
 
-// Score of this lane's column (key) against the query, before the key scale.
-// wq: the query's LDS head weights.  Lanes l and l+32 return the same value.
+// This lane's head weights from the query's LDS weights (after a barrier).
 template <int DT, int D, int HT>
-__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const float* wq, const uint32_t* b) {
+__device__ __forceinline__ void load_query_wregs(QueryFrag<DT, D, HT>& f, const float* wq) {
   const int g = (threadIdx.x >> 5) & 1;
+#pragma unroll
+  for (int ht = 0; ht < HT; ++ht) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 w4 = *reinterpret_cast<const float4*>(wq + ht * 32 + 8 * j + 4 * g);
+      f.w[ht][4 * j + 0] = w4.x;
+      f.w[ht][4 * j + 1] = w4.y;
+      f.w[ht][4 * j + 2] = w4.z;
+      f.w[ht][4 * j + 3] = w4.w;
+    }
+  }
+}
+
+// ReLU as one integer max on the bit pattern: every negative float (and -0) has
+// the sign bit set, so it is below 0 as an int32 and becomes +0; non-negative
+// values pass unchanged.  Accumulators are never NaN here.  A float max would
+// also quiet signalling NaNs first, which costs a second instruction.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// Score of this lane's column (key) against the query, before the key scale.
+// Lanes l and l+32 return the same value.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
   v16f acc[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -470,15 +500,9 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
   float p = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
+    // rows 8j + 4g + e of this head tile, in the order j, e
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // rows 8j + 4g + 0..3 of this head tile
-      const float4 w4 = *reinterpret_cast<const float4*>(wq + ht * 32 + 8 * j + 4 * g);
-      p = __builtin_fmaf(w4.x, __builtin_fmaxf(acc[ht][4 * j + 0], 0.0f), p);
-      p = __builtin_fmaf(w4.y, __builtin_fmaxf(acc[ht][4 * j + 1], 0.0f), p);
-      p = __builtin_fmaf(w4.z, __builtin_fmaxf(acc[ht][4 * j + 2], 0.0f), p);
-      p = __builtin_fmaf(w4.w, __builtin_fmaxf(acc[ht][4 * j + 3], 0.0f), p);
-    }
+    for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.w[ht][v], relu(acc[ht][v]), p);
   }
   const float o = __shfl_xor(p, 32);
   return p + o;
@@ -489,8 +513,8 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
 // block i is contracted.  fetch(blk, buf, scale) issues this lane's loads for a
 // block; sink(blk, score) consumes the score of this lane's column.
 template <int DT, int D, int HT, int DEPTH, class Fetch, class Sink>
-__device__ __forceinline__ void score_blocks(const QueryFrag<DT, D, HT>& f, const float* wq, int first, int step,
-                                             int nblk, Fetch fetch, Sink sink) {
+__device__ __forceinline__ void score_blocks(const QueryFrag<DT, D, HT>& f, int first, int step, int nblk, Fetch fetch,
+                                             Sink sink) {
   uint32_t buf[DEPTH][Geo<DT, D>::HW];
   float sc[DEPTH];
 #pragma unroll
@@ -503,12 +527,122 @@ __device__ __forceinline__ void score_blocks(const QueryFrag<DT, D, HT>& f, cons
     for (int d = 0; d < DEPTH; ++d) {
       const int blk = base + d * step;
       if (blk < nblk) {
-        const float x = score_tile<DT, D, HT>(f, wq, buf[d]) * sc[d];
+        const float x = score_tile<DT, D, HT>(f, buf[d]) * sc[d];
         sink(blk, x);
         const int nxt = blk + DEPTH * step;
         if (nxt < nblk) fetch(nxt, buf[d], sc[d]);
       }
     }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// block-cooperative scoring of a shared run of rows
+// ---------------------------------------------------------------------------
+//
+// When every wave of a block scores the same rows (representatives, or a chunk of
+// keys) against its own query, each row is read from memory once per block: a
+// stage of SR rows is loaded with row-contiguous 16-byte chunks (a row is one or
+// more whole cache lines per group of lanes), written to LDS with an XOR swizzle
+// of the chunk index, and every wave reads its MFMA operand layout from there.
+// Two LDS buffers alternate; the loads of stage s+1 are in flight while stage s is
+// contracted, and one barrier per stage separates reuse of a buffer.
+
+template <int DT, int D>
+struct Stage {
+  static constexpr int RB = Geo<DT, D>::RB;
+  static constexpr int CPR = RB / 16;                          // 16-byte chunks per row
+  static constexpr int SR = (8192 / RB) < 32 ? 32 : 8192 / RB;  // rows per stage
+  static constexpr int CHUNKS = SR * CPR;                      // chunks per stage
+};
+
+// LDS slot of chunk ch of stage row r.  Rows of 128 bytes pair up in a 256-byte
+// bank line, so their swizzle key steps every second row; longer rows use the row.
+template <int CPR>
+__device__ __forceinline__ int stage_slot(int r, int ch) {
+  const int key = (CPR == 8) ? (IVFTK_SWZ8(r)) : r;
+  return r * CPR + (ch ^ (key & (CPR - 1)));
+}
+
+// Loads this thread's chunks of stage st (rows clamped to nrows - 1) into reg,
+// and for threads below SR the scale of stage row tid.
+template <class S, int NT, int CPT, class Row>
+__device__ __forceinline__ void stage_gload(u32x4 (&reg)[CPT], float& rsc, int st, int nrows, Row& row) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = k * NT + tid;
+    int i = st * S::SR + c / S::CPR;
+    i = i < nrows ? i : nrows - 1;
+    const uint8_t* rp;
+    float sc;
+    row(i, rp, sc);
+    reg[k] = *reinterpret_cast<const u32x4*>(rp + (c % S::CPR) * 16);
+  }
+  if (tid < S::SR) {
+    int i = st * S::SR + tid;
+    i = i < nrows ? i : nrows - 1;
+    const uint8_t* rp;
+    row(i, rp, rsc);
+  }
+}
+
+template <class S, int NT, int CPT>
+__device__ __forceinline__ void stage_lstore(const u32x4 (&reg)[CPT], float rsc, int b, u32x4* tile, float* tsc) {
+  const int tid = threadIdx.x;
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = k * NT + tid;
+    tile[b * S::CHUNKS + stage_slot<S::CPR>(c / S::CPR, c % S::CPR)] = reg[k];
+  }
+  if (tid < S::SR) tsc[b * S::SR + tid] = rsc;
+}
+
+// Scores rows [0, nrows) (nrows uniform over the block; every thread of the block
+// calls).  NW waves of 64 lanes.  row(i, &ptr, &scale): address of row i's bytes
+// and its scale.  sink(i, x): score of row i for this lane's column (i may be
+// >= nrows; lanes 32..63 repeat lanes 0..31).  tile: 2 * CHUNKS 16-byte vectors of LDS,
+// tsc: 2 * SR floats of LDS.
+template <int DT, int D, int HT, int NW, class Row, class Sink>
+__device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, int nrows, u32x4* tile, float* tsc, Row row,
+                                             Sink sink) {
+  using S = Stage<DT, D>;
+  using G = Geo<DT, D>;
+  constexpr int NT = NW * 64;
+  constexpr int CPT = S::CHUNKS / NT;
+  static_assert(S::CHUNKS % NT == 0, "stage chunks must split evenly over the block");
+  static_assert(S::SR <= NT, "one scale per thread");
+  const int tid = threadIdx.x, col = tid & 31, g = (tid >> 5) & 1;
+  const int nst = (nrows + S::SR - 1) / S::SR;
+  if (nst == 0) return;
+  u32x4 reg[CPT];
+  float rsc = 1.0f;
+  stage_gload<S, NT, CPT>(reg, rsc, 0, nrows, row);
+  stage_lstore<S, NT, CPT>(reg, rsc, 0, tile, tsc);
+  __syncthreads();
+  for (int st = 0; st < nst; ++st) {
+    const int b = st & 1;
+    if (st + 1 < nst) stage_gload<S, NT, CPT>(reg, rsc, st + 1, nrows, row);
+#pragma unroll
+    for (int tt = 0; tt < S::SR / 32; ++tt) {
+      const int r0 = st * S::SR + tt * 32;
+      if (r0 < nrows) {
+        const int r = tt * 32 + col;
+        uint32_t bf[G::HW];
+#pragma unroll
+        for (int i = 0; i < G::HW / 4; ++i) {
+          const u32x4 v = tile[b * S::CHUNKS + stage_slot<S::CPR>(r, g * (S::CPR / 2) + i)];
+          bf[4 * i + 0] = v.x;
+          bf[4 * i + 1] = v.y;
+          bf[4 * i + 2] = v.z;
+          bf[4 * i + 3] = v.w;
+        }
+        const float x = score_tile<DT, D, HT>(f, bf) * tsc[b * S::SR + r];
+        sink(r0 + col, x);
+      }
+    }
+    if (st + 1 < nst) stage_lstore<S, NT, CPT>(reg, rsc, b ^ 1, tile, tsc);
+    __syncthreads();
   }
 }
 

@@ -18,35 +18,38 @@ namespace ivftk {
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
   using G = Geo<DT, D>;
+  using S = Stage<DT, D>;
   __shared__ float wq_s[4][HT * 32];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
+  __shared__ u32x4 tile[2 * S::CHUNKS];
+  __shared__ float tsc[2 * S::SR];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tl = blockIdx.x * 4 + wave;
-  const int t = p.t0 + tl;
   const bool active = tl < p.Tb;
-  if (active)
-    load_query_weights<HT>(wq_s[wave], p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr,
-                           p.H);
-  __syncthreads();
-  if (!active) return;
-  const int64_t n = p.q_pos0 + t + 1;
+  const int tc = p.t0 + (active ? tl : p.Tb - 1);   // idle waves still stage rows
+  load_query_weights<HT>(wq_s[wave], p.w + (size_t)tc * p.H, p.qscale ? p.qscale + (size_t)tc * p.H : nullptr, p.H);
+  // the block's rows: keys [j0, j1) with j1 bounded by its longest prefix
+  const int t_last = p.t0 + min(blockIdx.x * 4 + 3, p.Tb - 1);
   const int64_t j0 = (int64_t)blockIdx.y * p.kchunk;
-  const int64_t j1 = (j0 + p.kchunk < n) ? j0 + p.kchunk : n;
+  const int64_t n_max = p.q_pos0 + t_last + 1;
+  const int64_t j1 = (j0 + p.kchunk < n_max) ? j0 + p.kchunk : n_max;
+  __syncthreads();
   if (j0 >= j1) return;
+  const int64_t n_own = p.q_pos0 + tc + 1;
+  const int64_t j_end = active ? (j1 < n_own ? j1 : n_own) : j0;
   QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-  float* out = p.ws + (size_t)tl * p.ld;
-  const int nblk = (int)((j1 - j0 + 31) >> 5);
-  score_blocks<DT, D, HT, 3>(
-      f, wq_s[wave], 0, 1, nblk,
-      [&](int blk, uint32_t* buf, float& sc) {
-        int64_t j = j0 + blk * 32 + col;
-        j = j < j1 ? j : j1 - 1;
-        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
+  load_query<DT, D, HT>(f, p.q + (size_t)tc * p.H * G::RB, p.H);
+  load_query_wregs<DT, D, HT>(f, wq_s[wave]);
+  float* out = p.ws + (size_t)(active ? tl : 0) * p.ld;
+  score_staged<DT, D, HT, 4>(
+      f, (int)(j1 - j0), tile, tsc,
+      [&](int i, const uint8_t*& rp, float& sc) {
+        const int64_t j = j0 + i;
+        rp = p.keys + (size_t)j * G::RB;
         sc = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
       },
-      [&](int blk, float x) {
-        const int64_t j = j0 + blk * 32 + col;
-        if (lane < 32 && j < j1) out[j] = x;
+      [&](int i, float x) {
+        const int64_t j = j0 + i;
+        if (lane < 32 && j < j_end) out[j] = x;
       });
 }
 
@@ -249,26 +252,71 @@ __device__ __forceinline__ StoreView epoch_store(const RouteParams& p, int r) { 
 template <int DT, int D, int HT>
 __global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
   using G = Geo<DT, D>;
+  using S = Stage<DT, D>;
   __shared__ float wq_s[4][HT * 32];
+  __shared__ u32x4 tile[2 * S::CHUNKS];
+  __shared__ float tsc[2 * S::SR];
+  __shared__ int s_r[4], s_cvis[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
   const int t = blockIdx.x * 4 + wave;
   const bool active = t < p.T;
-  if (active)
-    load_query_weights<HT>(wq_s[wave], p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr,
-                           p.H);
+  const int tc = active ? t : p.T - 1;
+  load_query_weights<HT>(wq_s[wave], p.w + (size_t)tc * p.H, p.qscale ? p.qscale + (size_t)tc * p.H : nullptr, p.H);
+  const QVer v = query_version(p, tc);
+  if (lane == 0) {
+    s_r[wave] = active ? v.r : -1;
+    s_cvis[wave] = active ? v.cvis : 0;
+  }
   __syncthreads();
-  if (!active) return;
-  const QVer v = query_version(p, t);
+  // The block shares one staged pass when its queries use the same epoch (then a
+  // slot's representative is the same row for all of them); otherwise each wave
+  // scores its own slots.
+  int r_all = -1, cmax = 0;
+  bool same = true;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int rw = s_r[w];
+    if (rw >= 0) {
+      if (r_all < 0) r_all = rw;
+      else if (rw != r_all) same = false;
+      cmax = max(cmax, s_cvis[w]);
+    }
+  }
   const int s0 = blockIdx.y * chunk;
+  float* out = p.srep + (size_t)tc * p.srep_ld;
+  if (same) {
+    const int s1 = min(cmax, s0 + chunk);
+    if (s0 >= s1) return;
+    const int own_end = active ? min(v.cvis, s1) : s0;
+    const StoreView ep = epoch_store(p, r_all);
+    const int split = v.split;
+    QueryFrag<DT, D, HT> f;
+    load_query<DT, D, HT>(f, p.q + (size_t)tc * p.H * G::RB, p.H);
+    load_query_wregs<DT, D, HT>(f, wq_s[wave]);
+    score_staged<DT, D, HT, 4>(
+        f, s1 - s0, tile, tsc,
+        [&](int i, const uint8_t*& rp, float& sc) {
+          const int s = s0 + i;
+          const bool from_epoch = s < split;
+          rp = (from_epoch ? ep.rep : p.seal.rep) + (size_t)s * G::RB;
+          sc = (DT == DT_E4M3) ? (from_epoch ? ep.rsc : p.seal.rsc)[s] : 1.0f;
+        },
+        [&](int i, float x) {
+          const int s = s0 + i;
+          if (lane < 32 && s < own_end) out[s] = x;
+        });
+    return;
+  }
+  if (!active) return;
   const int s1 = min(v.cvis, s0 + chunk);
   if (s0 >= s1) return;
   const StoreView ep = epoch_store(p, v.r);
   QueryFrag<DT, D, HT> f;
   load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-  float* out = p.srep + (size_t)t * p.srep_ld;
+  load_query_wregs<DT, D, HT>(f, wq_s[wave]);
   const int nblk = (s1 - s0 + 31) >> 5;
   score_blocks<DT, D, HT, 3>(
-      f, wq_s[wave], 0, 1, nblk,
+      f, 0, 1, nblk,
       [&](int blk, uint32_t* buf, float& sc) {
         int s = s0 + blk * 32 + col;
         s = s < s1 ? s : s1 - 1;
@@ -330,9 +378,10 @@ __global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow
   QueryFrag<DT, D, HT> f;
   load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
   __syncthreads();
+  load_query_wregs<DT, D, HT>(f, wq_s);
   const int nb = (L + 31) >> 5;
   score_blocks<DT, D, HT, 3>(
-      f, wq_s, wave, nw, nb,
+      f, wave, nw, nb,
       [&](int blk, uint32_t* buf, float& sc) {
         const int i = blk * 32 + col;
         int j = cand[i < L ? i : L - 1];
