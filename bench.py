@@ -36,6 +36,7 @@ FP32_PEAK_TFLOPS = 157.3
 
 
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rescore_topk_c4_e4m3_pmc.md")
+PMC_KERNEL = "rescore_topk"
 PMC_SOURCES = ("score.hip", "dev.h", "params.h")
 
 
@@ -49,11 +50,11 @@ def kernel_source_hash():
     return h.hexdigest()[:16]
 
 
-def measured_traffic(workload, budget):
-    """HBM bytes per k_rescore_topk launch from the committed counter summary
+def measured_traffic(kernel, workload, budget):
+    """HBM bytes per launch of `kernel` from the committed counter summary
     (FETCH_SIZE and WRITE_SIZE, scaled by a 1 GiB copy), or None when the summary
-    is for another workload or the kernel's sources changed since it was taken."""
-    if workload != "c4" or budget != 8192 or not os.path.exists(PMC_SUMMARY):
+    is for another kernel or workload or the kernel's sources changed since."""
+    if kernel != PMC_KERNEL or workload != "c4" or budget != 8192 or not os.path.exists(PMC_SUMMARY):
         return None
     vals = {}
     with open(PMC_SUMMARY) as fh:
@@ -179,7 +180,7 @@ def main():
     for _ in range(args.warmup):
         ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc)
     torch.cuda.synchronize()
-    evs = [[hip.event() for _ in range(6)] for _ in range(args.steps)]
+    evs = [[hip.event() for _ in range(8)] for _ in range(args.steps)]
     start, stop = hip.event(), hip.event()
     torch.cuda.synchronize()
     hip.h.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream.cuda_stream))
@@ -189,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     total_ms = hip.elapsed(start, stop)
     ms_per_step = total_ms / args.steps
-    names = ["rep_score", "route_select", "rescore_topk"]
+    names = ["rep_score", "route_select", "cluster_score", "rescore_topk"]
     kern = {n: float(np.mean([hip.elapsed(e[2 * i], e[2 * i + 1]) for e in evs])) for i, n in enumerate(names)}
     value = T / (ms_per_step / 1e3)
     log(f"routed: {ms_per_step:.3f} ms/step, {value:.0f} q/s, kernels {kern}")
@@ -201,26 +202,42 @@ def main():
     m_t = (n_t - S) // W
     c_vis = m_t * Cs
     open_t = n_t - S - m_t * W
-    cand_t = np.minimum(n_t, np.maximum(budget, S + open_t))
+    base_t = np.minimum(n_t, S) + open_t                      # sinks + open window
+    cand_t = np.minimum(n_t, np.maximum(budget, base_t))
+    clus_t = cand_t - base_t                                  # candidates from selected clusters
     rb = d * {"f32": 4, "bf16": 2, "e4m3": 1}[dt]
     scale_b = 4 if dt == "e4m3" else 0
-    rep_flops = float(2 * H * d * c_vis.sum())
-    rescore_bytes = float(cand_t.sum() * (rb + scale_b + 4) + T * H * (rb + 8) + T * k * 8)
+    peak_mfma = {"e4m3": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS, "f32": FP32_PEAK_TFLOPS}[dt]
+    work = {
+        # contractions: flops against the MFMA peak of the format
+        "rep_score": ("mfma", float(2 * H * d * c_vis.sum())),
+        "cluster_score": ("mfma", float(2 * H * d * clus_t.sum())),
+        # cut + fill: read each query's representative scores and cluster sizes, write its list
+        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 4)),
+        # sink / open-window rows gathered and scored, cluster scores and positions read, top-k written
+        "rescore_topk": ("hbm", float(base_t.sum() * (rb + scale_b + 4) + clus_t.sum() * 8
+                                      + T * H * (rb + 8) + T * k * 8)),
+    }
     rescore_flops = float(2 * H * d * cand_t.sum())
     keys_scored = float((c_vis + cand_t).sum())
-    peak_mfma = {"e4m3": FP8_PEAK_TFLOPS, "bf16": BF16_PEAK_TFLOPS, "f32": FP32_PEAK_TFLOPS}[dt]
-    rep_frac = rep_flops / (kern["rep_score"] * 1e-3) / 1e12 / peak_mfma
-    resc_gbs = rescore_bytes / (kern["rescore_topk"] * 1e-3) / 1e9
-    if kern["rescore_topk"] >= kern["rep_score"]:
-        roof = dict(kernel="rescore_topk", bound="hbm", achieved=round(resc_gbs, 1), peak=HBM_PEAK_GBS,
-                    unit="GB/s", frac=round(resc_gbs / HBM_PEAK_GBS, 4),
-                    traffic=measured_traffic(args.workload, budget),
-                    algorithmic_bytes=rescore_bytes, avg_launch_ms=round(kern["rescore_topk"], 4))
-    else:
-        ach = rep_flops / (kern["rep_score"] * 1e-3) / 1e12
-        roof = dict(kernel="rep_score", bound="mfma", achieved=round(ach, 2), peak=peak_mfma, unit="TFLOP/s",
-                    frac=round(rep_frac, 4), traffic=None, algorithmic_flops=rep_flops,
-                    avg_launch_ms=round(kern["rep_score"], 4))
+
+    def roof_of(name):
+        bound, amount = work[name]
+        sec = kern[name] * 1e-3
+        if bound == "mfma":
+            ach = amount / sec / 1e12
+            return dict(kernel=name, bound="mfma", achieved=round(ach, 2), peak=peak_mfma, unit="TFLOP/s",
+                        frac=round(ach / peak_mfma, 4), traffic=None, algorithmic_flops=amount,
+                        avg_launch_ms=round(kern[name], 4))
+        ach = amount / sec / 1e9
+        return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=measured_traffic(name, args.workload, budget),
+                    algorithmic_bytes=amount, avg_launch_ms=round(kern[name], 4))
+
+    dominant = max(kern, key=kern.get)
+    roof = roof_of(dominant)
+    kernel_roofs = {n: {kk: v for kk, v in roof_of(n).items() if kk in ("bound", "achieved", "unit", "frac")}
+                    for n in names}
 
     # ---- exhaustive baseline + recall ----
     extra = {}
@@ -291,9 +308,9 @@ def main():
         "cpu_baseline": cpu,
         "keys_scored_per_s": round(keys_scored / (ms_per_step * 1e-3), 1),
         "kernels_ms": {kk: round(v, 4) for kk, v in kern.items()},
-        "rep_score_mfma_frac": round(rep_frac, 4),
-        "rescore_hbm_gbs": round(resc_gbs, 1),
-        "rescore_tflops": round(rescore_flops / (kern["rescore_topk"] * 1e-3) / 1e12, 1),
+        "kernel_rooflines": kernel_roofs,
+        "candidate_scoring_tflops": round(rescore_flops / ((kern["cluster_score"] + kern["rescore_topk"]) * 1e-3)
+                                          / 1e12, 1),
         "maintenance": {
             "build_s": round(build_s, 3),
             "seal_ms_per_window_last_chunk": round(seal_ms[-1][0] / max(1, seal_ms[-1][1]), 4),

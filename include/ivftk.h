@@ -88,8 +88,19 @@ typedef struct {
   int32_t max_queries;   /* largest T of one idx_route_topk call                               */
   int32_t max_budget;    /* largest budget of one idx_route_topk call (max(budget, S+W) <= 16384) */
   int32_t max_k;         /* largest k of one idx_route_topk call (<= 4096)                     */
+  int32_t rescore_mode;  /* how idx_route_topk scores the selected clusters' candidates:
+                            IDX_RESCORE_AUTO, IDX_RESCORE_QUERY or IDX_RESCORE_CLUSTER      */
   int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1)                       */
 } idx_config;
+
+/* Candidate rescoring of idx_route_topk.  Both give bit-identical results.
+ *   QUERY:   each query gathers and scores all of its candidates' key rows.
+ *   CLUSTER: the (query, cluster) selections are grouped by cluster; each selected
+ *            cluster's key rows are read once and scored against every query that
+ *            selected it (pays off when many queries of a call share clusters).
+ *   AUTO:    the library's choice; currently QUERY, which is the faster one on the
+ *            measured workloads (1M-key E4M3 prefill chunk of 4096 queries). */
+enum { IDX_RESCORE_AUTO = 0, IDX_RESCORE_QUERY = 1, IDX_RESCORE_CLUSTER = 2 };
 
 /* Snapshot of the host-side index state (no device wait). */
 typedef struct {
@@ -115,8 +126,10 @@ typedef struct {
   float* rep_scores;     /* [T, rep_cap]: representative score of each visible slot     */
   int32_t rep_cap;
   int32_t* version;      /* [T, 4]: epoch r, sealed windows m, visible slots, open start */
-  void** events;         /* host array of 6 hipEvent_t: recorded before and after each of the
-                            three kernels (representative scores, cut + fill, rescore + top-k) */
+  void** events;         /* host array of 8 hipEvent_t, recorded in pairs around the four
+                            stages: representative scores; cluster cut + fill + grouping of
+                            the selections by cluster; cluster-by-cluster candidate scores;
+                            sink and open-window scores + top-k                            */
   int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut kernel at this
                             size so the full cut kernel takes over sooner (testing)        */
   float* cand_scores;    /* [T, cand_cap]: exact score of each candidate, fill order      */

@@ -143,6 +143,22 @@ __device__ inline void bitonic_sort_desc(uint64_t* a, int n) {
   }
 }
 
+// Sort v (one entry per lane, 64 lanes) into descending order across the wave.
+__device__ __forceinline__ uint64_t wave_sort_desc(uint64_t v) {
+  const int lane = threadIdx.x & 63;
+  for (int k = 2; k <= 64; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)v, j), hi = __shfl_xor((uint32_t)(v >> 32), j);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      // segments of k lanes alternate direction; the last pass (k = 64) is descending
+      const bool desc = (lane & k) == 0;
+      const bool low = (lane & j) == 0;
+      v = (low == desc) ? (v > o ? v : o) : (v < o ? v : o);
+    }
+  }
+  return v;
+}
+
 // Sort a[0..n) (n a power of two) into ascending order.
 __device__ inline void bitonic_sort_asc(uint64_t* a, int n) {
   for (int k = 2; k <= n; k <<= 1) {
@@ -532,6 +548,42 @@ __device__ __forceinline__ void score_blocks(const QueryFrag<DT, D, HT>& f, int 
         const int nxt = blk + DEPTH * step;
         if (nxt < nblk) fetch(nxt, buf[d], sc[d]);
       }
+    }
+  }
+}
+
+// score_blocks for gathered rows: index(blk) loads this lane's row index for block
+// blk, row(j, buf, scale) issues the loads of row j.  Loads retire in issue order,
+// so a row load that needs an index issued just before it would also wait for
+// every row load in flight; instead each index is loaded DEPTH blocks before its
+// row (a second ring), and the row loads of DEPTH blocks stay in flight.  Every
+// load is unconditional (block numbers past the end are clamped to the last
+// block) so that the compiler can count the loads in flight exactly; tiles past
+// the end are computed and dropped (sink is not called for them).
+template <int DT, int D, int HT, int DEPTH, class Index, class Row, class Sink>
+__device__ __forceinline__ void score_gather(const QueryFrag<DT, D, HT>& f, int first, int step, int nblk,
+                                             Index index, Row row, Sink sink) {
+  if (first >= nblk) return;
+  const int last = nblk - 1;
+  uint32_t buf[DEPTH][Geo<DT, D>::HW];
+  float sc[DEPTH];
+  int jx[DEPTH];   // row index of the block DEPTH blocks after the one in buf[d]
+  int j0[DEPTH];
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) j0[d] = index(min(first + d * step, last));
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) jx[d] = index(min(first + (DEPTH + d) * step, last));
+#pragma unroll
+  for (int d = 0; d < DEPTH; ++d) row(j0[d], buf[d], sc[d]);
+  for (int base = first; base < nblk; base += DEPTH * step) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int blk = base + d * step;
+      const float x = score_tile<DT, D, HT>(f, buf[d]) * sc[d];
+      if (blk < nblk) sink(blk, x);
+      const int jn = jx[d];
+      jx[d] = index(min(blk + 2 * DEPTH * step, last));
+      row(jn, buf[d], sc[d]);
     }
   }
 }

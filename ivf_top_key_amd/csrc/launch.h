@@ -12,7 +12,12 @@ hipError_t launch_exh_score(const ExhParams& p, int dtype, int dim, int ht, int6
 hipError_t launch_topk_rows(const ExhParams& p, hipStream_t s);
 hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s);
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s);
+hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s);
+hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s);
+hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s);
 hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
+// True if one rescoring block holds cand_cap candidates and k winners.
+bool rescore_fits(int cand_cap, int k);
 hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, hipStream_t s);
 hipError_t launch_refit(const RefitParams& p, int dtype, int dim, hipStream_t s);
 

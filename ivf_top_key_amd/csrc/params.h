@@ -56,6 +56,25 @@ struct RouteParams {
   int list_cap;        // > 0: smaller cluster-list capacity of the fast cut kernel (tests)
   float* dbg_cand_scores;  // [T, dbg_cand_ld]
   int dbg_cand_ld;
+  // Cluster-major rescoring (cluster_major = 1; otherwise the final kernel gathers
+  // and scores every candidate).  A cluster is named by a unified id: ids
+  // [0, id_seal) are seal slots, id_seal + e * id_ep + s is slot s of epoch store e.
+  int cluster_major;
+  int id_seal, id_ep, n_ids;
+  int* sel_id;         // [T, sel_ld] ids of the query's selected clusters in rank order
+  int* sel_dst;        // [T, sel_ld] list index of each selected cluster's first candidate
+  int* n_sel;          // [T]
+  int64_t sel_ld;
+  int* pc_cnt;         // [n_ids] selections per id, then the scatter cursors
+  int* pair_t;         // [pair_cap] (query, list index, members taken), grouped by id
+  int* pair_dst;
+  int* pair_take;
+  int* item_id;        // [item_cap] work items: up to CS_PAIRS pairs of one id
+  int* item_first;
+  int* item_n;
+  int64_t item_cap;
+  int* ctr;            // [2] next work item, number of work items
+  float* sbuf;         // [T, cand_ld] scores of the cluster candidates
 };
 
 struct ExhParams {

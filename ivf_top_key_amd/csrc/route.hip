@@ -35,6 +35,28 @@ __device__ __forceinline__ QV qversion(const RouteParams& p, int t) {
   return v;
 }
 
+// Unified id of visible slot `slot` for a query of version v (see RouteParams).
+__device__ __forceinline__ int unified_id(const RouteParams& p, const QV& v, int slot) {
+  return slot < v.split ? p.id_seal + (v.r % 3) * p.id_ep + slot : slot;
+}
+
+// Records the query's selected clusters (rank order) for the cluster-major
+// rescoring and counts one selection per cluster id.  first[i] = the list index of
+// cluster i's first candidate.  All threads call.
+__device__ inline void record_selection(const RouteParams& p, const QV& v, int t, const uint64_t* comp,
+                                        const int* pre, int base_len, int nsel) {
+  if (!p.cluster_major) return;
+  int* sid = p.sel_id + (size_t)t * p.sel_ld;
+  int* sdst = p.sel_dst + (size_t)t * p.sel_ld;
+  for (int i = threadIdx.x; i < nsel; i += blockDim.x) {
+    const int id = unified_id(p, v, (int)comp_id(comp[i]));
+    sid[i] = id;
+    sdst[i] = base_len + pre[i];
+    atomicAdd(&p.pc_cnt[id], 1);
+  }
+  if (threadIdx.x == 0) p.n_sel[t] = nsel;
+}
+
 // Full version: every visible cluster in LDS, weighted radix select over composite
 // keys.  Runs only for queries the fast kernel handed over (redo[t] = 1).
 __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_pow2) {
@@ -67,6 +89,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   if (room <= 0 || v.cvis == 0) {
     if (tid == 0) {
       p.cand_len[t] = base_len;
+      if (p.cluster_major) p.n_sel[t] = 0;
       if (p.dbg_n_order) p.dbg_n_order[t] = 0;
     }
     return;
@@ -130,6 +153,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   if (tid == 0) s_total = chunk_base;
   __syncthreads();
   const int used = min(room, s_total);
+  record_selection(p, v, t, comp, wt, base_len, nsel);
 
   // fill: candidate c -> cluster i with wt[i] <= c < wt[i+1]
   for (int c = tid; c < used; c += bd) {
@@ -163,7 +187,8 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
 // that bin or above (the selected ones plus the cut bin's other members) are
 // gathered and sorted exactly.  If that list would exceed LIST_CAP the query is
 // left to the full kernel.
-constexpr int LIST_CAP = 2048;
+constexpr int LIST_CAP = 1024;
+constexpr int SF_NBIN = 2048;   // value bins of the cluster-cut histogram
 
 __device__ inline void find_bin_desc(const int* hist, int nbins, int need, int* wtmp, int* o_digit) {
   const int tid = threadIdx.x, bd = blockDim.x;
@@ -190,14 +215,19 @@ __device__ inline void find_bin_desc(const int* hist, int nbins, int need, int* 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(512) void k_route_select_fast(RouteParams p) {
-  __shared__ int hist[4096];
+constexpr int SF_THREADS = 512;
+constexpr int SF_PT = 16;   // visible slots per thread: SF_THREADS * SF_PT >= the 8192 routed slots
+
+__global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p) {
+  __shared__ int hist[SF_NBIN];
   __shared__ uint64_t list[LIST_CAP];
-  __shared__ int pre[LIST_CAP];
+  __shared__ int pre[LIST_CAP + 1];
+  __shared__ int moff[LIST_CAP];   // first member index; epoch store if >= 0, else seal store at ~moff
   __shared__ int wtmp[16];
   __shared__ uint32_t mm_tmp[16];
   __shared__ int s_digit, s_cnt, s_nsel;
-  const int tid = threadIdx.x, bd = blockDim.x;
+  const int tid = threadIdx.x, bd = SF_THREADS;
+  const int wave = tid >> 6, lane = tid & 63, nw = bd >> 6;
   const int t = blockIdx.x;
   const QV v = qversion(p, t);
   const StoreView ep = p.ep[v.r % 3];
@@ -218,51 +248,62 @@ __global__ __launch_bounds__(512) void k_route_select_fast(RouteParams p) {
     if (tid == 0) {
       p.cand_len[t] = base_len;
       p.redo[t] = 0;
+      if (p.cluster_major) p.n_sel[t] = 0;
       if (p.dbg_n_order) p.dbg_n_order[t] = 0;
     }
     return;
   }
   const float* srep = p.srep + (size_t)t * p.srep_ld;
-  for (int i = tid; i < 4096; i += bd) hist[i] = 0;
+  // this thread's slots s = u * bd + tid: score order key and size (0 = dead or not visible)
+  uint32_t ks[SF_PT];
+  int szs[SF_PT];
+#pragma unroll
+  for (int u = 0; u < SF_PT; ++u) {
+    const int s = u * bd + tid;
+    szs[u] = 0;
+    ks[u] = 0u;
+    if (s < v.cvis) {
+      szs[u] = (s < v.split ? ep.size : p.seal.size)[s];
+      ks[u] = order_bits(srep[s]);
+    }
+  }
+  for (int i = tid; i < SF_NBIN; i += bd) hist[i] = 0;
   if (tid == 0) {
     s_cnt = 0;
     s_digit = 0;
     s_nsel = 0;
   }
-  __syncthreads();
-  // linear bins over [min, max] of the live clusters' score keys
+  // value bins over [min, max] of the live clusters' scores
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int s = tid; s < v.cvis; s += bd) {
-    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
-    if (sz > 0) {
-      const uint32_t o = order_bits(srep[s]);
-      mn = o < mn ? o : mn;
-      mx = o > mx ? o : mx;
+#pragma unroll
+  for (int u = 0; u < SF_PT; ++u) {
+    if (szs[u] > 0) {
+      mn = ks[u] < mn ? ks[u] : mn;
+      mx = ks[u] > mx ? ks[u] : mx;
     }
   }
   block_minmax(mn, mx, mm_tmp);
-  const ValBins bins = make_bins(mn, mx < mn ? mn : mx, 4096);
+  const ValBins bins = make_bins(mn, mx < mn ? mn : mx, SF_NBIN);
+  int bn[SF_PT];
   int mine = 0;
-  for (int s = tid; s < v.cvis; s += bd) {
-    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
-    if (sz > 0) {
-      atomicAdd(&hist[bins(order_bits(srep[s]))], sz);
-      mine += sz;
+#pragma unroll
+  for (int u = 0; u < SF_PT; ++u) {
+    bn[u] = (int)bins(ks[u]);
+    if (szs[u] > 0) {
+      atomicAdd(&hist[bn[u]], szs[u]);
+      mine += szs[u];
     }
   }
   int total;
   block_exclusive_scan(mine, wtmp, &total);
   // total <= room: every live cluster is taken (bin 0 and up)
-  if (total > room) find_bin_desc(hist, 4096, room, wtmp, &s_digit);
+  if (total > room) find_bin_desc(hist, SF_NBIN, room, wtmp, &s_digit);
   const uint32_t cut_bin = (uint32_t)s_digit;
-  for (int s = tid; s < v.cvis; s += bd) {
-    const int sz = (s < v.split ? ep.size : p.seal.size)[s];
-    if (sz > 0) {
-      const float x = srep[s];
-      if (bins(order_bits(x)) >= cut_bin) {
-        const int i = atomicAdd(&s_cnt, 1);
-        if (i < LIST_CAP) list[i] = make_comp(x, (uint32_t)s);
-      }
+#pragma unroll
+  for (int u = 0; u < SF_PT; ++u) {
+    if (szs[u] > 0 && (uint32_t)bn[u] >= cut_bin) {
+      const int i = atomicAdd(&s_cnt, 1);
+      if (i < LIST_CAP) list[i] = ((uint64_t)ks[u] << 32) | (uint64_t)(~(uint32_t)(u * bd + tid));
     }
   }
   __syncthreads();
@@ -271,47 +312,78 @@ __global__ __launch_bounds__(512) void k_route_select_fast(RouteParams p) {
     if (tid == 0) p.redo[t] = 1;
     return;
   }
-  const int P2 = next_pow2(cnt);
-  for (int i = cnt + tid; i < P2; i += bd) list[i] = 0ull;
-  __syncthreads();
-  bitonic_sort_desc(list, P2);
-  // prefix sums of member counts in rank order
+  if (cnt <= 64) {
+    if (tid < 64) list[tid] = wave_sort_desc(tid < cnt ? list[tid] : 0ull);
+    __syncthreads();
+  } else {
+    const int P2 = next_pow2(cnt);
+    for (int i = cnt + tid; i < P2; i += bd) list[i] = 0ull;
+    __syncthreads();
+    bitonic_sort_desc(list, P2);
+  }
+  // prefix sums of member counts in rank order; pre[cnt] = total of the list
   int run = 0;
   for (int b0 = 0; b0 < cnt; b0 += bd) {
     const int i = b0 + tid;
-    int sz = 0;
+    int sz = 0, mo = 0;
     if (i < cnt) {
       const int s = (int)comp_id(list[i]);
-      sz = (s < v.split ? ep.size : p.seal.size)[s];
+      const bool from_epoch = s < v.split;
+      sz = (from_epoch ? ep.size : p.seal.size)[s];
+      const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
+      mo = from_epoch ? off : ~off;
     }
     int tot;
     const int ex = block_exclusive_scan(sz, wtmp, &tot);
-    if (i < cnt) pre[i] = run + ex;
+    if (i < cnt) {
+      pre[i] = run + ex;
+      moff[i] = mo;
+    }
     run += tot;
     __syncthreads();
   }
+  if (tid == 0) pre[cnt] = run;
   const int used = min(room, run);
   for (int i = tid; i < cnt; i += bd)
     if (pre[i] < used && (i == cnt - 1 || pre[i + 1] >= used)) s_nsel = i + 1;
   __syncthreads();
   const int nsel = s_nsel;
-  for (int c = tid; c < used; c += bd) {
-    int lo = 0, hi = nsel - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= c) lo = mid; else hi = mid - 1;
+  record_selection(p, v, t, list, pre, base_len, nsel);
+  // fill: one wave per selected cluster copies its first `take` members, two
+  // clusters per step so that their loads are in flight together
+  for (int i0 = wave; i0 < nsel; i0 += 2 * nw) {
+    int start[2], take[2], mo[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int i = i0 + h * nw;
+      start[h] = i < nsel ? pre[i] : 0;
+      take[h] = i < nsel ? min(pre[i + 1], used) - start[h] : 0;
+      mo[h] = i < nsel ? moff[i] : 0;
     }
-    const int s = (int)comp_id(list[lo]);
-    const bool from_epoch = s < v.split;
-    const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
-    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[off + (c - pre[lo])];
+    const int most = max(take[0], take[1]);
+    for (int m0 = 0; m0 < most; m0 += 128) {
+      int val[2][2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int m = m0 + r * 64 + lane;
+          if (m < take[h]) val[h][r] = mo[h] >= 0 ? ep.members[mo[h] + m] : p.seal.members[~mo[h] + m];
+        }
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+          const int m = m0 + r * 64 + lane;
+          if (m < take[h]) cand[base_len + start[h] + m] = val[h][r];
+        }
+    }
   }
   if (p.dbg_order) {
     for (int i = tid; i < nsel && i < p.dbg_order_cap; i += bd) {
       const int s = (int)comp_id(list[i]);
-      const int sz = (s < v.split ? ep.size : p.seal.size)[s];
       p.dbg_order[(size_t)t * p.dbg_order_cap + i] = s;
-      if (p.dbg_take) p.dbg_take[(size_t)t * p.dbg_order_cap + i] = min(sz, room - pre[i]);
+      if (p.dbg_take) p.dbg_take[(size_t)t * p.dbg_order_cap + i] = min(pre[i + 1], used) - pre[i];
     }
   }
   if (tid == 0) {
@@ -321,8 +393,81 @@ __global__ __launch_bounds__(512) void k_route_select_fast(RouteParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// grouping of (query, cluster) selections by cluster for the cluster-major rescoring
+// ---------------------------------------------------------------------------
+constexpr int CS_PAIRS = 32;   // selections per work item of the cluster-major scorer
+
+__global__ void k_pairs_zero(RouteParams p) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < p.n_ids; i += gridDim.x * blockDim.x) p.pc_cnt[i] = 0;
+}
+
+// One block: exclusive scan of the per-id counts into pair offsets (left in pc_cnt
+// as scatter cursors) and the work items (id, first pair, pairs) in id order.
+__global__ __launch_bounds__(1024) void k_pairs_scan(RouteParams p) {
+  __shared__ int wtmp[16];
+  const int tid = threadIdx.x, bd = blockDim.x;
+  const int per = (p.n_ids + bd - 1) / bd;
+  const int i0 = min(tid * per, p.n_ids), i1 = min(i0 + per, p.n_ids);
+  int cnt = 0, nit = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int c = p.pc_cnt[i];
+    cnt += c;
+    nit += (c + CS_PAIRS - 1) / CS_PAIRS;
+  }
+  int tot_pairs, tot_items;
+  int start = block_exclusive_scan(cnt, wtmp, &tot_pairs);
+  int item = block_exclusive_scan(nit, wtmp, &tot_items);
+  for (int i = i0; i < i1; ++i) {
+    const int c = p.pc_cnt[i];
+    for (int j = 0; j * CS_PAIRS < c; ++j, ++item) {
+      if (item < p.item_cap) {
+        p.item_id[item] = i;
+        p.item_first[item] = start + j * CS_PAIRS;
+        p.item_n[item] = min(CS_PAIRS, c - j * CS_PAIRS);
+      }
+    }
+    p.pc_cnt[i] = start;
+    start += c;
+  }
+  if (tid == 0) {
+    p.ctr[0] = 0;
+    p.ctr[1] = (int)min((int64_t)tot_items, p.item_cap);
+  }
+}
+
+// One block per query: its selections go to their cluster's range of the pair arrays.
+__global__ __launch_bounds__(256) void k_pairs_scatter(RouteParams p) {
+  const int t = blockIdx.x;
+  const int n = p.n_sel[t];
+  const int* sid = p.sel_id + (size_t)t * p.sel_ld;
+  const int* sdst = p.sel_dst + (size_t)t * p.sel_ld;
+  const int end = p.cand_len[t];
+  for (int i = threadIdx.x; i < n; i += blockDim.x) {
+    const int id = sid[i], dst = sdst[i];
+    const int nx = i + 1 < n ? sdst[i + 1] : end;
+    const int pos = atomicAdd(&p.pc_cnt[id], 1);
+    p.pair_t[pos] = t;
+    p.pair_dst[pos] = dst;
+    p.pair_take[pos] = nx - dst;
+  }
+}
+
+hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_pairs_zero, dim3((p.n_ids + 1023) / 1024), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_pairs_scan, dim3(1), dim3(1024), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_pairs_scatter, dim3(p.T), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_select_fast, dim3(p.T), dim3(512), 0, s, p);
+  hipLaunchKernelGGL(k_route_select_fast, dim3(p.T), dim3(SF_THREADS), 0, s, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);

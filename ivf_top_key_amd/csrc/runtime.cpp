@@ -66,6 +66,7 @@ struct EpochStore {
 };
 
 constexpr int TILE = 1024;
+constexpr int CS_PAIRS_HOST = 32;   // selections per work item of the cluster-major scorer
 constexpr size_t LDS_BYTES = 163840;
 
 }  // namespace
@@ -95,6 +96,13 @@ struct idx_index {
   int* cand = nullptr;
   int* cand_len = nullptr;
   int* redo = nullptr;
+  // cluster-major rescoring: selections per query, pairs grouped by cluster, work items
+  int64_t sel_cap = 0, pair_cap = 0, item_cap = 0;
+  int n_ids = 0;
+  int *sel_id = nullptr, *sel_dst = nullptr, *n_sel = nullptr, *pc_cnt = nullptr;
+  int *pair_t = nullptr, *pair_dst = nullptr, *pair_take = nullptr;
+  int *item_id = nullptr, *item_first = nullptr, *item_n = nullptr, *ctr = nullptr;
+  float* sbuf = nullptr;
   std::vector<void*> allocs;
   int64_t bytes = 0;
   int64_t n_keys = 0;
@@ -173,6 +181,8 @@ int idx_create(const idx_config* cfg, idx_index** out) {
   if (c.max_queries < 1) return fail(IDX_EINVAL, "max_queries must be >= 1");
   if (c.max_k < 1 || c.max_k > 4096) return fail(IDX_EINVAL, "max_k must be 1..4096");
   if (c.max_budget < c.max_k) return fail(IDX_EINVAL, "max_budget must be >= max_k");
+  if (c.rescore_mode < IDX_RESCORE_AUTO || c.rescore_mode > IDX_RESCORE_CLUSTER)
+    return fail(IDX_EINVAL, "rescore_mode must be IDX_RESCORE_AUTO, _QUERY or _CLUSTER");
   if (c.max_keys < 1 || c.max_keys > (int64_t)1 << 30) return fail(IDX_EINVAL, "max_keys must be 1..2^30");
 
   idx_index* ix = new (std::nothrow) idx_index();
@@ -196,15 +206,14 @@ int idx_create(const idx_config* cfg, idx_index** out) {
     delete ix;
     return fail(IDX_ECAPACITY, "max_keys allows %lld clusters; at most 8192 are routed", (long long)(ix->slot_cap));
   }
-  {
-    auto p2 = [](int64_t n) { int64_t p = 1; while (p < n) p <<= 1; return p; };
-    // rescore block: winners + cut-bin buffer (8 B each), score keys (4 B), ~20 KB static
-    const int64_t lds = (p2(c.max_k) + 1024) * 8 + p2(ix->cand_cap) * 4 + 20480;
-    if (lds > (int64_t)LDS_BYTES) {
-      delete ix;
-      return fail(IDX_ECAPACITY, "max(budget, n_sink + window) and max_k do not fit one block's LDS");
-    }
+  if (!rescore_fits(ix->cand_cap, c.max_k)) {
+    delete ix;
+    return fail(IDX_ECAPACITY, "max(budget, n_sink + window) and max_k do not fit one rescoring block");
   }
+  ix->sel_cap = std::min<int64_t>(ix->cand_cap, std::max<int64_t>(ix->slot_cap, 1));
+  ix->pair_cap = (int64_t)c.max_queries * ix->sel_cap;
+  ix->n_ids = (int)(ix->slot_cap + (ix->wpr ? 3 * ix->ep_slot_cap : 0));
+  ix->item_cap = ix->pair_cap / CS_PAIRS_HOST + ix->n_ids;
   bool ok = ix->alloc(&ix->keys, c.max_keys * ix->RB) &&
             (c.dtype != IDX_E4M3 || ix->alloc(&ix->kscale, c.max_keys)) &&
             ix->alloc(&ix->sl_size, ix->slot_cap) && ix->alloc(&ix->sl_off, ix->slot_cap) &&
@@ -213,6 +222,14 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
             ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
             ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries);
+  if (ok && c.rescore_mode == IDX_RESCORE_CLUSTER)
+    ok = ix->alloc(&ix->sel_id, (int64_t)c.max_queries * ix->sel_cap) &&
+            ix->alloc(&ix->sel_dst, (int64_t)c.max_queries * ix->sel_cap) && ix->alloc(&ix->n_sel, c.max_queries) &&
+            ix->alloc(&ix->pc_cnt, std::max(ix->n_ids, 1)) && ix->alloc(&ix->pair_t, ix->pair_cap) &&
+            ix->alloc(&ix->pair_dst, ix->pair_cap) && ix->alloc(&ix->pair_take, ix->pair_cap) &&
+            ix->alloc(&ix->item_id, ix->item_cap) && ix->alloc(&ix->item_first, ix->item_cap) &&
+            ix->alloc(&ix->item_n, ix->item_cap) && ix->alloc(&ix->ctr, 2) &&
+            ix->alloc(&ix->sbuf, (int64_t)c.max_queries * ix->cand_cap);
   if (ok && ix->wpr) {
     for (int i = 0; i < 3 && ok; ++i) {
       EpochStore& e = ix->ep[i];
@@ -439,6 +456,24 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
   p.redo = ix->redo;
   p.topk_idx = topk_idx;
   p.topk_score = topk_score;
+  p.cluster_major = c.rescore_mode == IDX_RESCORE_CLUSTER;
+  p.id_seal = (int)ix->slot_cap;
+  p.id_ep = (int)ix->ep_slot_cap;
+  p.n_ids = ix->n_ids;
+  p.sel_id = ix->sel_id;
+  p.sel_dst = ix->sel_dst;
+  p.n_sel = ix->n_sel;
+  p.sel_ld = ix->sel_cap;
+  p.pc_cnt = ix->pc_cnt;
+  p.pair_t = ix->pair_t;
+  p.pair_dst = ix->pair_dst;
+  p.pair_take = ix->pair_take;
+  p.item_id = ix->item_id;
+  p.item_first = ix->item_first;
+  p.item_n = ix->item_n;
+  p.item_cap = ix->item_cap;
+  p.ctr = ix->ctr;
+  p.sbuf = ix->sbuf;
   if (dbg) {
     p.dbg_order = dbg->order;
     p.dbg_take = dbg->order_take;
@@ -459,12 +494,17 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
   if (max_slots > 0 && e == hipSuccess) e = launch_rep_score(p, c.dtype, c.dim, ix->HT, max_slots, s);
   mark(1);
   mark(2);
+  if (p.cluster_major && e == hipSuccess) e = launch_pairs_zero(p, s);
   if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
+  if (p.cluster_major && e == hipSuccess) e = launch_pairs_group(p, s);
   mark(3);
-  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
   mark(4);
-  if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
+  if (p.cluster_major && e == hipSuccess) e = launch_cluster_score(p, c.dtype, c.dim, ix->HT, s);
   mark(5);
+  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
+  mark(6);
+  if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
+  mark(7);
   if (e != hipSuccess) return device_error(ix, e, "route launch");
   if (dbg) {
     if (dbg->cand && dbg->cand_cap > 0) {

@@ -343,30 +343,237 @@ hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, in
 }
 
 // ---------------------------------------------------------------------------
-// candidate rescoring + top-k: one block per query
+// cluster-major scoring of the selected clusters' candidates
 // ---------------------------------------------------------------------------
-// Scores of the candidates stay in LDS as 32-bit order keys; a 32-bit radix select
-// finds the k-th score, ties at that score go to the lowest positions, and the k
-// winners are sorted by (score desc, position asc).  Key rows are gathered one
-// block of 32 ahead of the MFMA work so a wave always has loads in flight.
-constexpr int RS_NBIN = 2048;      // linear bins of the top-k histogram
-constexpr int RS_TIE_CAP = 1024;   // largest cut bin resolved by a local sort
+// Work item = one cluster and up to 16 of the queries that selected it.  The block
+// gathers the cluster's member rows into LDS once (row-contiguous loads, swizzled
+// like the staged scorer), then each wave scores the members against its queries
+// and writes the scores to the queries' candidate rows of sbuf.  Blocks take items
+// from a counter until none is left.
+template <int DT, int D, int HT>
+struct ClusterStage {
+  static constexpr int RB = Geo<DT, D>::RB;
+  static constexpr int CPR = RB / 16;
+  // member rows per LDS chunk: 32 KB of rows, 32 to 256 rows
+  static constexpr int CR = (32768 / RB) < 32 ? 32 : ((32768 / RB) > 256 ? 256 : 32768 / RB);
+  // queries go through a per-wave LDS buffer (row-contiguous loads) when one fits in 16 KB
+  static constexpr bool QLDS = HT * 32 * RB <= 16384;
+  static constexpr int QCH = QLDS ? HT * 32 * CPR / 64 : 1;         // 16-byte chunks per lane
+  static constexpr int QBUF = QLDS ? HT * 32 * CPR : 1;             // chunks per wave buffer
+};
 
 template <int DT, int D, int HT>
-__global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow2, int k_pow2) {
+__global__ __launch_bounds__(256) void k_cluster_score(RouteParams p) {
+  using G = Geo<DT, D>;
+  using C = ClusterStage<DT, D, HT>;
+  __shared__ u32x4 tile[C::CR * C::CPR];
+  __shared__ u32x4 qbuf[4][C::QBUF];
+  __shared__ float tsc[C::CR];
+  __shared__ float wq_s[4][128];
+  __shared__ int s_item;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, g = (lane >> 5) & 1;
+  const int nk1 = (int)(p.n_keys - 1);
+  for (;;) {
+    if (tid == 0) s_item = atomicAdd(&p.ctr[0], 1);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= p.ctr[1]) break;
+    const int id = p.item_id[item], first = p.item_first[item], n = p.item_n[item];
+    StoreView st;
+    int slot;
+    if (id < p.id_seal) {
+      st = p.seal;
+      slot = id;
+    } else {
+      const int e = (id - p.id_seal) / p.id_ep;
+      st = p.ep[e];
+      slot = id - p.id_seal - e * p.id_ep;
+    }
+    const int* mem = st.members + max(st.off[slot], 0);
+    // members any query of the item takes (n <= 32 pairs: one per lane, wave maximum)
+    int mt = lane < n ? p.pair_take[first + lane] : 0;
+    for (int off = 32; off > 0; off >>= 1) mt = max(mt, __shfl_xor(mt, off));
+    for (int m0 = 0; m0 < mt; m0 += C::CR) {
+      const int nr = min(C::CR, mt - m0);
+      __syncthreads();   // the previous chunk's readers are done
+      {
+        // member positions first, then all row chunks, then the LDS writes, so that
+        // each thread's loads are in flight together
+        constexpr int SPT = C::CR * C::CPR / 256;   // 16-byte chunks per thread
+        static_assert(C::CR * C::CPR % 256 == 0 && C::CR <= 256, "chunk rows must split over the block");
+        int jr[SPT];
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+          const int r = (k * 256 + tid) / C::CPR;
+          jr[k] = mem[m0 + (r < nr ? r : nr - 1)];
+        }
+        const int js = mem[m0 + (tid < nr ? tid : nr - 1)];
+        u32x4 vv[SPT];
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+          const int j = jr[k] < 0 ? 0 : (jr[k] > nk1 ? nk1 : jr[k]);
+          vv[k] = *reinterpret_cast<const u32x4*>(p.keys + (size_t)j * G::RB + ((k * 256 + tid) % C::CPR) * 16);
+        }
+        float scl = 1.0f;
+        if (DT == DT_E4M3) scl = p.kscale[js < 0 ? 0 : (js > nk1 ? nk1 : js)];
+#pragma unroll
+        for (int k = 0; k < SPT; ++k) {
+          const int c = k * 256 + tid;
+          tile[stage_slot<C::CPR>(c / C::CPR, c % C::CPR)] = vv[k];
+        }
+        if (tid < C::CR) tsc[tid] = scl;
+      }
+      __syncthreads();
+      // each wave scores pairs wave + 4j, j < np; lane j holds pair j's metadata.
+      // The next pair's query rows and head weights are loaded while the current
+      // pair is contracted; loads are unconditional (clamped) so that the ones in
+      // flight are counted exactly.
+      const int np = n > wave ? (n - wave + 3) / 4 : 0;
+      int m_t = 0, m_d = 0, m_k = 0;
+      if (lane < np) {
+        const int pi = first + wave + 4 * lane;
+        m_t = p.pair_t[pi];
+        m_d = p.pair_dst[pi];
+        m_k = p.pair_take[pi];
+      }
+      u32x4 qr[2][C::QCH];
+      QueryFrag<DT, D, HT> fd[C::QLDS ? 1 : 2];   // two for direct loads (prefetch), else one
+      float wv[2][2];                             // head weights of heads lane and 64 + lane
+      auto fetch = [&](int j, int h) {
+        const int t = __shfl(m_t, j);
+        const uint8_t* q_t = p.q + (size_t)t * p.H * G::RB;
+        if constexpr (C::QLDS) {
+#pragma unroll
+          for (int c = 0; c < C::QCH; ++c) {
+            const int ci = c * 64 + lane, row = ci / C::CPR;
+            const int cs = row < p.H ? ci : ci % C::CPR;   // rows past H read row 0 and are zeroed
+            const u32x4 v = *reinterpret_cast<const u32x4*>(q_t + (size_t)cs * 16);
+            qr[h][c] = row < p.H ? v : u32x4{0u, 0u, 0u, 0u};
+          }
+        } else {
+          load_query<DT, D, HT>(fd[C::QLDS ? 0 : h], q_t, p.H);
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const int hd = u * 64 + lane;
+          const size_t wi = (size_t)t * p.H + min(hd, p.H - 1);
+          const float wx = p.qscale ? p.w[wi] * p.qscale[wi] : p.w[wi];
+          wv[h][u] = hd < p.H ? wx : 0.0f;
+        }
+      };
+      if (np > 0) fetch(0, 0);
+      for (int j = 0; j < np; j += 2) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int jj = j + h;
+          fetch(min(jj + 1, np - 1), h ^ 1);
+          if (jj < np) {
+            const int t = __shfl(m_t, jj), dst = __shfl(m_d, jj), take = __shfl(m_k, jj);
+            const int rows = min(take - m0, nr);
+            QueryFrag<DT, D, HT>& f = fd[C::QLDS ? 0 : h];
+            wq_s[wave][lane] = wv[h][0];
+            wq_s[wave][64 + lane] = wv[h][1];
+            if constexpr (C::QLDS) {
+#pragma unroll
+              for (int c = 0; c < C::QCH; ++c) {
+                const int ci = c * 64 + lane;
+                qbuf[wave][stage_slot<C::CPR>(ci / C::CPR, ci % C::CPR)] = qr[h][c];
+              }
+            }
+            __builtin_amdgcn_wave_barrier();
+            if constexpr (C::QLDS) {
+#pragma unroll
+              for (int ht = 0; ht < HT; ++ht)
+#pragma unroll
+                for (int i = 0; i < G::HW / 4; ++i) {
+                  const u32x4 v4 = qbuf[wave][stage_slot<C::CPR>(ht * 32 + col, g * (C::CPR / 2) + i)];
+                  f.a[ht][4 * i + 0] = v4.x;
+                  f.a[ht][4 * i + 1] = v4.y;
+                  f.a[ht][4 * i + 2] = v4.z;
+                  f.a[ht][4 * i + 3] = v4.w;
+                }
+            }
+            load_query_wregs<DT, D, HT>(f, wq_s[wave]);
+            __builtin_amdgcn_wave_barrier();
+            float* out = p.sbuf + (size_t)t * p.cand_ld + dst + m0;
+            for (int r0 = 0; r0 < rows; r0 += 32) {
+              const int r = r0 + col;
+              uint32_t bf[G::HW];
+#pragma unroll
+              for (int i = 0; i < G::HW / 4; ++i) {
+                const u32x4 v4 = tile[stage_slot<C::CPR>(r, g * (C::CPR / 2) + i)];
+                bf[4 * i + 0] = v4.x;
+                bf[4 * i + 1] = v4.y;
+                bf[4 * i + 2] = v4.z;
+                bf[4 * i + 3] = v4.w;
+              }
+              const float x = score_tile<DT, D, HT>(f, bf) * tsc[r];
+              if (lane < 32 && r < rows) out[r] = x;
+            }
+          }
+        }
+      }
+    }
+    __syncthreads();   // every thread has read s_item
+  }
+}
+
+template <int DT, int D, int HT>
+static hipError_t launch_cluster_score_t(const RouteParams& p, hipStream_t s) {
+  int dev = 0, n_cu = 256;
+  (void)hipGetDevice(&dev);
+  (void)hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_cluster_score<DT, D, HT>, 256, 0) != hipSuccess ||
+      per_cu < 1)
+    per_cu = 1;
+  hipLaunchKernelGGL((k_cluster_score<DT, D, HT>), dim3(n_cu * per_cu), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s) {
+  IVFTK_DISPATCH(launch_cluster_score_t, dtype, dim, ht, p, s);
+}
+
+// ---------------------------------------------------------------------------
+// candidate rescoring + top-k: one block per query
+// ---------------------------------------------------------------------------
+// The candidates' scores go to LDS as 32-bit order keys while the waves gather
+// and score key rows (ring of row loads in flight per wave).  Then every thread
+// takes its PT keys and candidate ids into registers, which frees the LDS for the
+// selection: a value-binned histogram between the block's min and max score
+// finds the bin holding the k-th score; entries in higher bins are placed by bin
+// offset plus rank inside their bin, the cut bin is sorted exactly.  Ties at the
+// k-th score go to the lowest positions; the k winners come out sorted by
+// (score desc, position asc).  Degenerate cases (all scores equal, a crowded cut
+// bin) use an exact radix select.
+constexpr int RS_NBIN = 1024;     // value bins of the top-k histogram
+constexpr int RS_TIE_CAP = 512;   // largest cut bin resolved by a local sort
+constexpr int RS_THREADS = 256;
+constexpr int RS_KPT = 4096 / RS_THREADS;   // winners per thread at the largest k
+
+// LDS bytes of the selection region for a candidate capacity and k (both powers of two).
+__host__ __device__ constexpr size_t rescore_region_bytes(int cap_pow2, int k_pow2) {
+  return (size_t)cap_pow2 * 4 > (size_t)(k_pow2 + RS_TIE_CAP) * 8 + (size_t)RS_NBIN * 8
+             ? (size_t)cap_pow2 * 4
+             : (size_t)(k_pow2 + RS_TIE_CAP) * 8 + (size_t)RS_NBIN * 8;
+}
+
+template <int DT, int D, int HT, int PT>
+__global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int k_pow2) {
   using G = Geo<DT, D>;
   extern __shared__ uint64_t lds[];
   __shared__ float wq_s[HT * 32];
-  uint64_t* sel = lds;                                                     // [k_pow2] winners
-  uint64_t* tie = lds + k_pow2;                                            // [RS_TIE_CAP] cut bin
-  uint32_t* okey = reinterpret_cast<uint32_t*>(lds + k_pow2 + RS_TIE_CAP);  // [cap_pow2] score keys
   __shared__ Select32Scratch sc;
-  __shared__ int hist[RS_NBIN];
-  __shared__ int offs[RS_NBIN];
   __shared__ uint32_t mm_tmp[16];
   __shared__ int wtmp[16];
   __shared__ int s_cnt, s_tie, s_bstar;
-  const int tid = threadIdx.x, bd = blockDim.x;
+  uint32_t* okey = reinterpret_cast<uint32_t*>(lds);   // scoring: [L] score keys
+  uint64_t* sel = lds;                                 // selection: [k_pow2] winners
+  uint64_t* tie = lds + k_pow2;                        // [RS_TIE_CAP] cut bin
+  int* hist = reinterpret_cast<int*>(lds + k_pow2 + RS_TIE_CAP);   // [RS_NBIN]
+  int* offs = hist + RS_NBIN;                                      // [RS_NBIN]
+  const int tid = threadIdx.x, bd = RS_THREADS;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
   const int t = blockIdx.x;
   const int L = p.cand_len[t];
@@ -379,46 +586,96 @@ __global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow
   load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
   __syncthreads();
   load_query_wregs<DT, D, HT>(f, wq_s);
-  const int nb = (L + 31) >> 5;
-  score_blocks<DT, D, HT, 3>(
+  // the sinks and the open window are scored here, and with cluster-major rescoring
+  // the selected clusters' candidates [base_len, L) were scored into sbuf; otherwise
+  // every candidate is gathered and scored here
+  const QVer qv = query_version(p, t);
+  const int n_sink = (int)(qv.n < p.S ? qv.n : p.S);
+  const int base_len =
+      p.cluster_major ? min(L, n_sink + (qv.n > qv.open_lo ? (int)(qv.n - qv.open_lo) : 0)) : L;
+  const int nb = (base_len + 31) >> 5;
+  score_gather<DT, D, HT, 3>(
       f, wave, nw, nb,
-      [&](int blk, uint32_t* buf, float& sc) {
+      [&](int blk) -> int {
         const int i = blk * 32 + col;
-        int j = cand[i < L ? i : L - 1];
+        return cand[i < base_len ? i : base_len - 1];
+      },
+      [&](int j, uint32_t* buf, float& scl) {
         j = j < 0 ? 0 : (j > nk1 ? nk1 : j);
         load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
-        sc = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
+        scl = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
       },
       [&](int blk, float x) {
         const int i = blk * 32 + col;
-        if (lane < 32 && i < L) {
+        if (lane < 32 && i < base_len) {
           okey[i] = order_bits(x);
           if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x;
         }
       });
-  if (tid == 0) s_cnt = 0;
+  {
+    const float* sb = p.sbuf + (size_t)t * p.cand_ld;
+    for (int i = base_len + tid; i < L; i += bd) {
+      const float x = sb[i];
+      okey[i] = order_bits(x);
+      if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x;
+    }
+  }
   __syncthreads();
+  // this thread's entries: groups of four consecutive list entries, ent(u) below,
+  // with their score keys and candidate positions (16-byte loads)
+  auto ent = [&](int u) { return 4 * ((u >> 2) * bd + tid) + (u & 3); };
+  uint32_t kv[PT];
+  uint32_t cv[PT];
+#pragma unroll
+  for (int u4 = 0; u4 < PT / 4; ++u4) {
+    const int i0 = 4 * (u4 * bd + tid);
+    if (i0 + 3 < L) {
+      const uint4 k4 = *reinterpret_cast<const uint4*>(okey + i0);
+      const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
+      kv[4 * u4 + 0] = k4.x;
+      kv[4 * u4 + 1] = k4.y;
+      kv[4 * u4 + 2] = k4.z;
+      kv[4 * u4 + 3] = k4.w;
+      cv[4 * u4 + 0] = (uint32_t)c4.x;
+      cv[4 * u4 + 1] = (uint32_t)c4.y;
+      cv[4 * u4 + 2] = (uint32_t)c4.z;
+      cv[4 * u4 + 3] = (uint32_t)c4.w;
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = i0 + e;
+        kv[4 * u4 + e] = i < L ? okey[i] : 0u;
+        cv[4 * u4 + e] = i < L ? (uint32_t)cand[i] : 0u;
+      }
+    }
+  }
+  if (tid == 0) {
+    s_cnt = 0;
+    s_tie = 0;
+  }
+  __syncthreads();   // the LDS region is free from here on
   int* oi = p.topk_idx + (size_t)t * K;
   float* os = p.topk_score ? p.topk_score + (size_t)t * K : nullptr;
-  auto comp_of = [&](int i) -> uint64_t { return ((uint64_t)okey[i] << 32) | (uint64_t)(~(uint32_t)cand[i]); };
-  auto put = [&](int idx, uint64_t v) {
-    oi[idx] = (int)comp_id(v);
-    if (os) os[idx] = comp_score(v);
-  };
+  auto comp = [](uint32_t key, uint32_t pos) -> uint64_t { return ((uint64_t)key << 32) | (uint64_t)(~pos); };
   if (L <= K) {
     const int P2 = next_pow2(L > 0 ? L : 1);
-    for (int i = tid; i < P2; i += bd) sel[i] = i < L ? comp_of(i) : 0ull;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = ent(u);
+      if (i < P2) sel[i] = i < L ? comp(kv[u], cv[u]) : 0ull;
+    }
     __syncthreads();
     bitonic_sort_desc(sel, P2);
     write_topk(sel, L, K, oi, os);
     return;
   }
-  // ---- linear-bin histogram over [min, max] of the score keys ----
   uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-  for (int i = tid; i < L; i += bd) {
-    const uint32_t v = okey[i];
-    mn = v < mn ? v : mn;
-    mx = v > mx ? v : mx;
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    if (ent(u) < L) {
+      mn = kv[u] < mn ? kv[u] : mn;
+      mx = kv[u] > mx ? kv[u] : mx;
+    }
   }
   block_minmax(mn, mx, mm_tmp);
   bool fallback = (mn == mx);
@@ -428,14 +685,18 @@ __global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow
     bins = make_bins(mn, mx, RS_NBIN);
     for (int i = tid; i < RS_NBIN; i += bd) hist[i] = 0;
     __syncthreads();
-    for (int i = tid; i < L; i += bd) atomicAdd(&hist[bins(okey[i])], 1);
+#pragma unroll
+    for (int u = 0; u < PT; ++u)
+      if (ent(u) < L) atomicAdd(&hist[bins(kv[u])], 1);
     __syncthreads();
     // offs[b] = entries in bins above b (descending order); the bin holding the K-th
-    const int per = RS_NBIN / bd;
+    constexpr int per = RS_NBIN / RS_THREADS;
     int sum = 0;
+#pragma unroll
     for (int q = 0; q < per; ++q) sum += hist[RS_NBIN - 1 - tid * per - q];
     int tot;
     int run = block_exclusive_scan(sum, wtmp, &tot);
+#pragma unroll
     for (int q = 0; q < per; ++q) {
       const int bb = RS_NBIN - 1 - tid * per - q;
       const int c = hist[bb];
@@ -453,73 +714,116 @@ __global__ __launch_bounds__(256) void k_rescore_topk(RouteParams p, int cap_pow
   if (!fallback) {
     // scatter: bins above the cut go to their bin's range of sel, the cut bin to tie
     for (int i = tid; i < RS_NBIN; i += bd) hist[i] = offs[i];
-    if (tid == 0) s_tie = 0;
     __syncthreads();
-    for (int i = tid; i < L; i += bd) {
-      const uint32_t v = okey[i];
-      const uint32_t bb = bins(v);
-      if ((int)bb > bstar) sel[atomicAdd(&hist[bb], 1)] = comp_of(i);
-      else if ((int)bb == bstar) tie[atomicAdd(&s_tie, 1)] = comp_of(i);
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      if (ent(u) < L) {
+        const int bb = (int)bins(kv[u]);
+        if (bb > bstar) sel[atomicAdd(&hist[bb], 1)] = comp(kv[u], cv[u]);
+        else if (bb == bstar) tie[atomicAdd(&s_tie, 1)] = comp(kv[u], cv[u]);
+      }
     }
     const int P2 = next_pow2(in_bin);
     __syncthreads();
-    for (int i = in_bin + tid; i < P2; i += bd) tie[i] = 0ull;
-    __syncthreads();
-    bitonic_sort_desc(tie, P2);
-    for (int r = tid; r < K - above; r += bd) put(above + r, tie[r]);
-    // entries above the cut: final index = bin start + rank inside the bin
-    for (int i = tid; i < above; i += bd) {
-      const uint64_t v = sel[i];
-      const int bb = (int)bins((uint32_t)(v >> 32));
-      const int lo = offs[bb], hi = offs[bb - 1];
-      int rank = 0;
-      for (int j = lo; j < hi; ++j) rank += sel[j] > v;
-      put(lo + rank, v);
+    if (P2 <= 64) {
+      if (tid < 64) tie[tid] = wave_sort_desc(tid < in_bin ? tie[tid] : 0ull);
+    } else {
+      for (int i = in_bin + tid; i < P2; i += bd) tie[i] = 0ull;
+      __syncthreads();
+      bitonic_sort_desc(tie, P2);
     }
+    // entries above the cut move to bin start + rank inside the bin (ranks are taken
+    // before any entry moves), the cut bin's winners follow them
+    uint64_t pv[RS_KPT];
+    int pp[RS_KPT];
+#pragma unroll
+    for (int q = 0; q < RS_KPT; ++q) {
+      const int i = q * bd + tid;
+      pp[q] = -1;
+      if (i < above) {
+        const uint64_t v = sel[i];
+        const int bb = (int)bins((uint32_t)(v >> 32));
+        const int lo = offs[bb], hi = offs[bb - 1];
+        int rank = 0;
+        for (int j = lo; j < hi; ++j) rank += sel[j] > v;
+        pv[q] = v;
+        pp[q] = lo + rank;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < RS_KPT; ++q)
+      if (pp[q] >= 0) sel[pp[q]] = pv[q];
+    for (int r = tid; r < K - above; r += bd) sel[above + r] = tie[r];
+    __syncthreads();
+    write_topk(sel, K, K, oi, os);
     return;
   }
   // ---- fallback: exact radix select (all keys equal, or a crowded cut bin) ----
-  const uint32_t thr = radix_select32_desc(okey, L, K, sc);
-  const int above_r = sc.above;
-  const int need = K - above_r;
-  const int n_eq = sc.hist[thr & 255u];
   __syncthreads();
-  for (int i = tid; i < L; i += bd) {
-    const uint32_t v = okey[i];
-    if (v > thr || (v == thr && n_eq == need)) sel[atomicAdd(&s_cnt, 1)] = comp_of(i);
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    const int i = ent(u);
+    if (i < L) okey[i] = kv[u];
   }
+  __syncthreads();
+  const uint32_t thr = radix_select32_desc(okey, L, K, sc);
+  const int need = K - sc.above;
+  const int n_eq = sc.hist[thr & 255u];
+  uint32_t t2 = 0u;
   __syncthreads();
   if (n_eq != need) {
     // more candidates share the k-th score than slots remain: lowest positions win
-    for (int i = tid; i < L; i += bd) okey[i] = (okey[i] == thr) ? ~(uint32_t)cand[i] : 0u;
-    __syncthreads();
-    const uint32_t t2 = radix_select32_desc(okey, L, need, sc);
-    for (int i = tid; i < L; i += bd) {
-      const uint32_t v = okey[i];
-      if (v != 0u && v >= t2) sel[atomicAdd(&s_cnt, 1)] = ((uint64_t)thr << 32) | (uint64_t)v;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = ent(u);
+      if (i < L) okey[i] = (kv[u] == thr) ? ~cv[u] : 0u;
     }
     __syncthreads();
+    t2 = radix_select32_desc(okey, L, need, sc);
+    __syncthreads();
   }
+#pragma unroll
+  for (int u = 0; u < PT; ++u) {
+    if (ent(u) < L) {
+      const uint32_t v = kv[u];
+      if (v > thr || (v == thr && (n_eq == need || ~cv[u] >= t2))) sel[atomicAdd(&s_cnt, 1)] = comp(v, cv[u]);
+    }
+  }
+  __syncthreads();
   for (int i = K + tid; i < k_pow2; i += bd) sel[i] = 0ull;
   __syncthreads();
   bitonic_sort_desc(sel, k_pow2);
   write_topk(sel, K, K, oi, os);
 }
 
+template <int DT, int D, int HT, int PT>
+static hipError_t launch_rescore_pt(const RouteParams& p, int cap_pow2, int k_pow2, hipStream_t s) {
+  const size_t lds = rescore_region_bytes(cap_pow2, k_pow2);
+  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT, PT>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT, PT>), dim3(p.T), dim3(RS_THREADS), lds, s, p, k_pow2);
+  return hipGetLastError();
+}
+
 template <int DT, int D, int HT>
 static hipError_t launch_rescore_topk_t(const RouteParams& p, int cand_cap, hipStream_t s) {
   const int cap_pow2 = next_pow2(cand_cap);
   const int k_pow2 = next_pow2(p.k);
-  const size_t lds = (size_t)(k_pow2 + RS_TIE_CAP) * sizeof(uint64_t) + (size_t)cap_pow2 * sizeof(uint32_t);
-  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT>), dim3(p.T), dim3(256), lds, s, p, cap_pow2, k_pow2);
-  return hipGetLastError();
+  if (cap_pow2 <= 32 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 32>(p, cap_pow2, k_pow2, s);
+  if (cap_pow2 <= 64 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 64>(p, cap_pow2, k_pow2, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s) {
   IVFTK_DISPATCH(launch_rescore_topk_t, dtype, dim, ht, p, cand_cap, s);
+}
+
+bool rescore_fits(int cand_cap, int k) {
+  const int cap_pow2 = next_pow2(cand_cap), k_pow2 = next_pow2(k);
+  // the region plus the kernel's static LDS (head weights, radix scratch, a few words)
+  return cap_pow2 <= 64 * RS_THREADS && rescore_region_bytes(cap_pow2, k_pow2) + 4096 <= 163840;
 }
 
 }  // namespace ivftk

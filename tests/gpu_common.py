@@ -69,13 +69,13 @@ def to_dev(a, device="cuda"):
     return torch.from_numpy(np.ascontiguousarray(a)).to(device)
 
 
-def gpu_index(wl, inp, n_keys=None, chunk=None, max_queries=None, max_budget=None, max_k=None):
+def gpu_index(wl, inp, n_keys=None, chunk=None, max_queries=None, max_budget=None, max_k=None, rescore="auto"):
     """Insert keys (in chunks) and run every due refit, published at once."""
     import ivf_top_key_amd as ivf
     n = wl["N"] if n_keys is None else n_keys
     ix = ivf.idx_create(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], max_keys=wl["N"],
                         max_queries=max_queries or wl["T"], max_budget=max_budget or max(wl["budget"], wl["N"]),
-                        max_k=max_k or wl["k"], **{k: wl[k] for k in CFG_KEYS})
+                        max_k=max_k or wl["k"], rescore=rescore, **{k: wl[k] for k in CFG_KEYS})
     keys = to_dev(inp["keys"][:n])
     ks = to_dev(inp["k_scale"][:n]) if inp["k_scale"] is not None else None
     chunk = chunk or n

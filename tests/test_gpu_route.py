@@ -152,3 +152,39 @@ def test_route_exact_ties(zero_queries):
         assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)
     finally:
         ivf.idx_destroy(gix)
+
+
+@pytest.mark.parametrize("name,over", [
+    ("c1", {}),
+    ("bf16_small", {}),
+    ("e4m3_small", dict(T=300, q_pos0=11000)),
+])
+def test_route_rescore_modes_bit_identical(name, over):
+    """Query-major and cluster-major rescoring give the same candidates, scores and top-k bits."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload(name, **over)
+    T, k, budget = wl["T"], wl["k"], wl["budget"]
+    q = to_dev(inp["q"])
+    qs = to_dev(inp["q_scale"]) if inp["q_scale"] is not None else None
+    w = to_dev(inp["w"])
+    out = {}
+    for mode in ("query", "cluster"):
+        ix = gpu_index(wl, inp, rescore=mode)
+        try:
+            dbg = ivf.make_route_debug(T, budget + wl["window"] + 64, 8, 8)
+            idx, sc = ivf.idx_route_topk(ix, q, qs, w, wl["q_pos0"], k, budget, debug=dbg)
+            torch.cuda.synchronize()
+            out[mode] = (idx.cpu().numpy(), sc.cpu().numpy(), dbg["cand"].cpu().numpy(),
+                         dbg["cand_scores"].cpu().numpy(), dbg["cand_len"].cpu().numpy())
+        finally:
+            ivf.idx_destroy(ix)
+    a, b = out["query"], out["cluster"]
+    assert np.array_equal(a[4], b[4])
+    for t in range(T):
+        L = int(a[4][t])
+        assert np.array_equal(a[2][t, :L], b[2][t, :L]), f"query {t}: candidate lists differ"
+        assert np.array_equal(a[3][t, :L].view(np.uint32), b[3][t, :L].view(np.uint32)), f"query {t}: scores differ"
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    say(f"  {name}: {T} queries, query-major and cluster-major bit-identical")
