@@ -102,6 +102,8 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-exhaustive", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--rescore", default="auto", choices=["auto", "query", "cluster"],
+                    help="candidate rescoring: query-major gathers (auto) or cluster-major")
     ap.add_argument("--cpu-sample", type=int, default=1024)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one 1 GiB elementwise copy (reference for HBM counters)")
@@ -139,7 +141,7 @@ def main():
     # ---- build the index by streaming the prefix, R keys at a time ----
     ix = ivf.idx_create(heads=H, dim=d, dtype=dt, max_keys=N, n_sink=wl["n_sink"], window=W,
                         cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"], seal_iters=wl["seal_iters"],
-                        refit_every=R, max_queries=T, max_budget=16384, max_k=k)
+                        refit_every=R, max_queries=T, max_budget=16384, max_k=k, rescore=args.rescore)
     stream = torch.cuda.current_stream()
     side = torch.cuda.Stream()
     torch.cuda.synchronize()
@@ -214,10 +216,15 @@ def main():
         "cluster_score": ("mfma", float(2 * H * d * clus_t.sum())),
         # cut + fill: read each query's representative scores and cluster sizes, write its list
         "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 4)),
-        # sink / open-window rows gathered and scored, cluster scores and positions read, top-k written
-        "rescore_topk": ("hbm", float(base_t.sum() * (rb + scale_b + 4) + clus_t.sum() * 8
-                                      + T * H * (rb + 8) + T * k * 8)),
     }
+    if args.rescore == "cluster":
+        # sink / open-window rows gathered and scored, cluster scores and positions read, top-k written
+        work["rescore_topk"] = ("hbm", float(base_t.sum() * (rb + scale_b + 4) + clus_t.sum() * 8
+                                             + T * H * (rb + 8) + T * k * 8))
+    else:
+        # every candidate's key row (+ scale) and position gathered, query read, top-k written
+        work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b + 4) + T * H * (rb + 8) + T * k * 8))
+        work["cluster_score"] = ("mfma", 0.0)
     rescore_flops = float(2 * H * d * cand_t.sum())
     keys_scored = float((c_vis + cand_t).sum())
 
@@ -303,7 +310,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"1M-token prefix ({N} keys), {dt} keys+queries with fp32 scales, H={H}, d={d}, "
                                f"{T} tail queries, k={k}, budget {budget}",
-                   "global_batch": T, "seq_len": N, "parallelism": "single GPU"},
+                   "global_batch": T, "seq_len": N, "parallelism": "single GPU",
+                   "rescore": "query-major" if args.rescore != "cluster" else "cluster-major"},
         "roofline": roof,
         "cpu_baseline": cpu,
         "keys_scored_per_s": round(keys_scored / (ms_per_step * 1e-3), 1),
