@@ -142,6 +142,13 @@ struct RefitParams {
   int* tile_cnt;
   int tile;            // keys per tile
   int n_tiles;
+  // screening of the work keys with bf16 matrix products (see refit.hip)
+  uint16_t* cbf;       // [2, r*Q, d] split bf16 copies (hi, lo) of the warm centroids
+  float* cnrm;         // [r*Q] squared norm of each warm centroid, -1 for empty slots
+  unsigned* tile_cmax; // [ceil(r*Q / 32)] largest squared norm per 32-slot tile (float bits)
+  int* ovf;            // keys whose candidate list overflowed: exact brute force
+  int* ovf_count;
+  int brute_ovf;       // 1: the brute-force kernel takes its keys from ovf
 };
 
 }  // namespace ivftk

@@ -88,8 +88,10 @@ __device__ __forceinline__ bool warm_alive(const RefitParams& p, int s) {
 __global__ void k_refit_begin(RefitParams p) {
   if (threadIdx.x == 0) {
     *p.work_count = 0;
+    *p.ovf_count = 0;
     *p.drift_max = 0.0f;
   }
+  if (threadIdx.x == 0) p.tile_cmax[0] = 0u;
 }
 
 // keys that were assigned by epoch r-1: test the bounds against the new centres
@@ -153,8 +155,10 @@ template <int DT, int D>
 __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
   __shared__ float tile[REFIT_TILE_SLOTS * D];
   __shared__ int alive[REFIT_TILE_SLOTS];
-  const int64_t n_new = p.B_r - p.B_prev;
-  const int64_t total = n_new + *p.work_count;
+  // keys: new keys then the work list, or (brute_ovf) the screening's overflow list
+  const int64_t n_new = p.brute_ovf ? 0 : p.B_r - p.B_prev;
+  const int64_t total = p.brute_ovf ? (int64_t)*p.ovf_count : n_new + *p.work_count;
+  const int* list = p.brute_ovf ? p.ovf : p.work;
   const int nslots = p.r * p.Q;
   for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < total; base += (int64_t)gridDim.x * blockDim.x) {
     const int64_t item = base + threadIdx.x;
@@ -162,7 +166,7 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
     int64_t x = 0;
     float xv[D];
     if (active) {
-      x = item < n_new ? p.B_prev + item : (int64_t)p.work[item - n_new];
+      x = item < n_new ? p.B_prev + item : (int64_t)list[item - n_new];
       x = min(max(x, (int64_t)p.S), p.B_r - 1);
       load_key_f32<DT, D>(xv, p, x);
     }
@@ -196,6 +200,215 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
       p.assign[x] = best;
       p.ub[x] = __builtin_sqrtf(b1) * (1.0f + EPS_B);
       p.lb[x] = (b2 < __builtin_inff()) ? __builtin_sqrtf(b2) * (1.0f - EPS_B) : __builtin_inff();
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// screening: the nearest warm centroid of the new keys and the work list
+// ---------------------------------------------------------------------------
+// The exact answer is the fixed-order fp32 nearest centroid.  Matrix cores give an
+// approximate squared distance A(x,c) = |x|^2 + |c|^2 - 2 <x, c>' where <x, c>' is
+// accumulated in fp32 from split bf16 values, v = v_hi + v_lo + e with v_hi =
+// bf16(v), v_lo = bf16(v - v_hi), |e| <= 2^-16 |v|, as hi.hi + hi.lo + lo.hi (the
+// products are exact).  |A - D| for the fixed-order distance D is at most
+//   E(x) = 2.5e-4 |x| cmax + 6e-5 (|x| + cmax)^2 + 1e-30   (cmax >= every |c|):
+// the split drops lo.lo and e terms (< 3.1 * 2^-16 |x||c| per dot product), the
+// fp32 sums of 3d products add < 384 * 2^-23 * 1.01 |x||c|, both doubled by the
+// factor 2, and the norms, the final operations and the fixed-order evaluation's
+// own error stay below 4e-5 (|x|+|c|)^2 for d <= 128.  The exact nearest c* has
+// A(c*) - E <= D(c*) <= D(c_min) <= Amin + E, so only slots with A <= Amin + 2E can
+// be it; those are evaluated in the fixed order, and the result equals the brute
+// force.  The cut carries 1% slack on E against fp32 rounding of the comparison.  A
+// key whose survivor list overflows goes to the brute-force kernel.
+
+// split bf16 copies (hi rows [0, r*Q), lo rows [r*Q, 2*r*Q)) and squared norm of the
+// warm centroids (+inf for empty slots), and the largest squared norm (tile_cmax[0])
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_refit_prep(RefitParams p) {
+  const int nslots = p.r * p.Q;
+  const int s = blockIdx.x * blockDim.x + threadIdx.x;
+  if (s >= nslots) return;
+  const float* c = warm_cent(p, s, D);
+  float nrm = 0.0f;
+  for (int i = 0; i < D; ++i) {
+    const float v = c[i];
+    nrm = nrm + v * v;
+    p.cbf[(size_t)s * D + i] = (uint16_t)f32_to_bf16(v);
+  }
+  for (int i = 0; i < D; ++i) {
+    const float v = c[i];
+    const float hi = __uint_as_float(f32_to_bf16(v) << 16);
+    p.cbf[(size_t)(p.r * p.Q + s) * D + i] = (uint16_t)f32_to_bf16(v - hi);
+  }
+  const bool alive = warm_alive(p, s);
+  p.cnrm[s] = alive ? nrm : __builtin_inff();
+  if (alive) atomicMax(&p.tile_cmax[0], __float_as_uint(nrm));
+}
+
+constexpr int SCR_LIST = 8;   // candidate entries per lane (each half-wave sees half the slots)
+
+// Per key (one column of a wave's 32), each lane keeps the smallest approximate
+// distance Amin of its half of the slots and the slots with A <= Amin + 2E; at the
+// end the halves merge, the survivors are evaluated exactly, and the bounds for the
+// next refit are ub = exact best, lb = min(second-best exact survivor, Amin + E)
+// (every other slot has A - E > Amin + E).
+template <int DT, int D>
+__global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
+  using GB = Geo<DT_BF16, D>;
+  constexpr int CPR = GB::RB / 16;
+  __shared__ u32x4 ctile[2][32 * CPR];   // hi and lo rows of 32 slots
+  __shared__ float cn[32];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, g = (lane >> 5) & 1;
+  const int64_t n_new = p.B_r - p.B_prev;
+  const int64_t total = n_new + *p.work_count;
+  const int nslots = p.r * p.Q;
+  const int ntl = (nslots + 31) / 32;
+  const float cmr = __builtin_sqrtf(__uint_as_float(p.tile_cmax[0])) * (1.0f + 1e-6f);
+  for (int64_t base = (int64_t)blockIdx.x * 128; base < total; base += (int64_t)gridDim.x * 128) {
+    const int64_t item = base + wave * 32 + col;
+    const bool active = item < total;
+    int64_t x = p.S;
+    if (item < n_new) x = p.B_prev + item;
+    else if (item < total) x = (int64_t)p.work[item - n_new];
+    x = min(max(x, (int64_t)p.S), p.B_r - 1);
+    // this lane's half of the key as bf16 (B operand), and the squared norm
+    uint32_t bx[GB::HW], bl[GB::HW];   // split bf16 of this lane's half of the key
+    float nh = 0.0f;
+    {
+      const uint8_t* row = p.keys + (size_t)x * (D * Elem<DT>::bytes) + (size_t)g * (D / 2) * Elem<DT>::bytes;
+      const float sk = (DT == DT_E4M3) ? p.kscale[x] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < GB::HW; ++i) {
+        float a = load_elem<DT>(row, 2 * i), b = load_elem<DT>(row, 2 * i + 1);
+        if constexpr (DT == DT_E4M3) {
+          a = a * sk;
+          b = b * sk;
+        }
+        const uint32_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
+        bx[i] = ah | (bh << 16);
+        bl[i] = f32_to_bf16(a - __uint_as_float(ah << 16)) | (f32_to_bf16(b - __uint_as_float(bh << 16)) << 16);
+        nh = nh + a * a;
+        nh = nh + b * b;
+      }
+    }
+    const float nx = nh + __shfl_xor(nh, 32);
+    const float nxr = __builtin_sqrtf(nx) * (1.0f + 1e-6f);
+    const float sum = nxr + cmr;
+    const float E = (2.5e-4f * nxr * cmr + 6e-5f * sum * sum + 1e-30f) * (1.0f + 1e-5f);
+    const float E2 = 2.02f * E;   // the cut Amin + 2E with 1% slack
+    float amin = __builtin_inff();
+    int ls[SCR_LIST];
+    float la[SCR_LIST];
+#pragma unroll
+    for (int q = 0; q < SCR_LIST; ++q) {
+      ls[q] = -1;
+      la[q] = 0.0f;
+    }
+    bool ovf = false;
+    for (int tl = 0; tl < ntl; ++tl) {
+      const int t0 = tl * 32;
+      __syncthreads();
+      for (int c = tid; c < 2 * 32 * CPR; c += 256) {
+        const int h = c / (32 * CPR), cc = c % (32 * CPR);
+        const int r = cc / CPR, ch = cc % CPR;
+        const int sl = min(t0 + r, nslots - 1) + h * nslots;
+        ctile[h][stage_slot<CPR>(r, ch)] = *reinterpret_cast<const u32x4*>(
+            reinterpret_cast<const uint8_t*>(p.cbf) + (size_t)sl * GB::RB + ch * 16);
+      }
+      if (tid < 32) cn[tid] = t0 + tid < nslots ? p.cnrm[t0 + tid] : __builtin_inff();
+      __syncthreads();
+      v16f acc;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < GB::HW / 4; ++i) {
+        const u32x4 a4 = ctile[0][stage_slot<CPR>(col, g * (CPR / 2) + i)];
+        const u32x4 l4 = ctile[1][stage_slot<CPR>(col, g * (CPR / 2) + i)];
+        const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w};
+        const uint32_t al[4] = {l4.x, l4.y, l4.z, l4.w};
+        mfma_step<DT_BF16>(acc, a, &bx[4 * i]);
+        mfma_step<DT_BF16>(acc, a, &bl[4 * i]);
+        mfma_step<DT_BF16>(acc, al, &bx[4 * i]);
+      }
+      float A[16];
+      float tmin = __builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float4 c4 = *reinterpret_cast<const float4*>(cn + 8 * j + 4 * g);
+        const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int v = 4 * j + e;
+          A[v] = (nx + cv[e]) - 2.0f * acc[v];
+          tmin = __builtin_fminf(tmin, A[v]);
+        }
+      }
+      if (tmin <= amin + E2) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          if (A[v] <= amin + E2) {
+            amin = __builtin_fminf(amin, A[v]);
+            const float cut = amin + E2;
+            bool placed = false;
+#pragma unroll
+            for (int q = 0; q < SCR_LIST; ++q) {
+              if (ls[q] >= 0 && la[q] > cut) ls[q] = -1;
+              if (!placed && ls[q] < 0) {
+                ls[q] = t0 + 8 * (v >> 2) + 4 * g + (v & 3);
+                la[q] = A[v];
+                placed = true;
+              }
+            }
+            ovf = ovf || !placed;
+          }
+        }
+      }
+    }
+    // both halves of the wave hold the same key: final cut, then exact distances of
+    // this lane's survivors
+    amin = __builtin_fminf(amin, __shfl_xor(amin, 32));
+    ovf = ovf || __shfl_xor((int)ovf, 32);
+    const float cut = amin + E2;
+    float e1 = __builtin_inff(), e2 = __builtin_inff();
+    int s1 = 0x7fffffff;
+    float xv[D];
+    load_key_f32<DT, D>(xv, p, x);
+#pragma unroll
+    for (int q = 0; q < SCR_LIST; ++q) {
+      if (ls[q] < 0 || la[q] > cut) continue;
+      const float de = sqdist<D>(xv, warm_cent(p, ls[q], D));
+      if (de < e1 || (de == e1 && ls[q] < s1)) {
+        e2 = e1;
+        e1 = de;
+        s1 = ls[q];
+      } else {
+        e2 = __builtin_fminf(e2, de);
+      }
+    }
+    const float pe1 = __shfl_xor(e1, 32), pe2 = __shfl_xor(e2, 32);
+    const int ps1 = __shfl_xor(s1, 32);
+    float b1, b2;
+    int best;
+    if (e1 < pe1 || (e1 == pe1 && s1 < ps1)) {
+      b1 = e1;
+      best = s1;
+      b2 = __builtin_fminf(__builtin_fminf(e2, pe2), pe1);
+    } else {
+      b1 = pe1;
+      best = ps1;
+      b2 = __builtin_fminf(__builtin_fminf(e2, pe2), e1);
+    }
+    b2 = __builtin_fminf(b2, amin + 0.99f * E);   // every non-survivor has D > Amin + E
+    if (active && g == 0) {
+      if (ovf || best == 0x7fffffff) {
+        p.ovf[atomicAdd(p.ovf_count, 1)] = (int)x;
+      } else {
+        p.assign[x] = best;
+        p.ub[x] = __builtin_sqrtf(b1) * (1.0f + EPS_B);
+        p.lb[x] = (b2 < __builtin_inff()) ? __builtin_sqrtf(__builtin_fmaxf(b2, 0.0f)) * (1.0f - EPS_B)
+                                          : __builtin_inff();
+      }
     }
   }
 }
@@ -362,7 +575,12 @@ static hipError_t launch_refit_t(const RefitParams& p, hipStream_t s) {
   if (n_old > 0) {
     hipLaunchKernelGGL((k_refit_old<DT, D>), dim3((unsigned)((n_old + 255) / 256)), dim3(256), 0, s, p);
   }
-  hipLaunchKernelGGL((k_refit_brute<DT, D>), dim3(2048), dim3(256), 0, s, p);
+  const int nslots_ = p.r * p.Q;
+  hipLaunchKernelGGL((k_refit_prep<DT, D>), dim3((nslots_ + 255) / 256), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_refit_screen<DT, D>), dim3(2048), dim3(256), 0, s, p);
+  RefitParams po = p;
+  po.brute_ovf = 1;
+  hipLaunchKernelGGL((k_refit_brute<DT, D>), dim3(256), dim3(256), 0, s, po);
   const size_t hist_lds = (size_t)nslots * sizeof(int);
   hipError_t e = hipFuncSetAttribute((const void*)k_tile_hist, hipFuncAttributeMaxDynamicSharedMemorySize,
                                      (int)hist_lds);

@@ -92,6 +92,11 @@ struct idx_index {
   int* work = nullptr;
   int* work_count = nullptr;
   int* tile_cnt = nullptr;
+  uint16_t* cbf = nullptr;       // refit screening: bf16 warm centroids, norms, tile maxima
+  float* cnrm = nullptr;
+  unsigned* tile_cmax = nullptr;
+  int* ovf = nullptr;
+  int* ovf_count = nullptr;
   float* srep = nullptr;
   int* cand = nullptr;
   int* cand_len = nullptr;
@@ -240,7 +245,11 @@ int idx_create(const idx_config* cfg, idx_index** out) {
     }
     ok = ok && ix->alloc(&ix->assign, c.max_keys) && ix->alloc(&ix->ub, c.max_keys) &&
          ix->alloc(&ix->lb, c.max_keys) && ix->alloc(&ix->work, c.max_keys) && ix->alloc(&ix->work_count, 1) &&
-         ix->alloc(&ix->tile_cnt, (int64_t)ix->n_tiles_cap * std::max<int64_t>(ix->ep_slot_cap, 1));
+         ix->alloc(&ix->tile_cnt, (int64_t)ix->n_tiles_cap * std::max<int64_t>(ix->ep_slot_cap, 1)) &&
+         ix->alloc(&ix->cbf, 2 * std::max<int64_t>(ix->ep_slot_cap, 1) * c.dim) &&
+         ix->alloc(&ix->cnrm, std::max<int64_t>(ix->ep_slot_cap, 1)) &&
+         ix->alloc(&ix->tile_cmax, std::max<int64_t>((ix->ep_slot_cap + 31) / 32, 1)) &&
+         ix->alloc(&ix->ovf, c.max_keys) && ix->alloc(&ix->ovf_count, 1);
   }
   if (!ok) {
     ix->release();
@@ -368,6 +377,12 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   p.drift = out.drift;
   p.drift_max = out.drift_max;
   p.tile_cnt = ix->tile_cnt;
+  p.cbf = ix->cbf;
+  p.cnrm = ix->cnrm;
+  p.tile_cmax = ix->tile_cmax;
+  p.ovf = ix->ovf;
+  p.ovf_count = ix->ovf_count;
+  p.brute_ovf = 0;
   p.tile = TILE;
   p.n_tiles = (int)((p.B_r - p.S + TILE - 1) / TILE);
   e = launch_refit(p, c.dtype, c.dim, side);
