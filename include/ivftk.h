@@ -90,6 +90,8 @@ typedef struct {
   int32_t max_k;         /* largest k of one idx_route_topk call (<= 4096)                     */
   int32_t rescore_mode;  /* how idx_route_topk scores the selected clusters' candidates:
                             IDX_RESCORE_AUTO, IDX_RESCORE_QUERY or IDX_RESCORE_CLUSTER      */
+  int32_t cluster_mode;  /* IDX_CLUSTERS_CONTENT (size-capped k-means seal + refits) or
+                            IDX_CLUSTERS_POSITIONAL (position blocks; refit_every must be 0) */
   int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1)                       */
 } idx_config;
 
@@ -101,6 +103,15 @@ typedef struct {
  *   AUTO:    the library's choice; currently QUERY, which is the faster one on the
  *            measured workloads (1M-key E4M3 prefill chunk of 4096 queries). */
 enum { IDX_RESCORE_AUTO = 0, IDX_RESCORE_QUERY = 1, IDX_RESCORE_CLUSTER = 2 };
+
+/* How sealed windows are grouped.
+ *   CONTENT:    size-capped k-means (the method of the pages).
+ *   POSITIONAL: window w's cluster i is the contiguous block of cluster_size keys
+ *               [S + w*W + i*cluster_size, ...), represented by its mean: the
+ *               position-block grouping of the comparison method the paper-daily
+ *               explainer calls HiSA ("它到底在解决什么问题？"), routed by the same
+ *               kernels as a baseline. */
+enum { IDX_CLUSTERS_CONTENT = 0, IDX_CLUSTERS_POSITIONAL = 1 };
 
 /* Snapshot of the host-side index state (no device wait). */
 typedef struct {

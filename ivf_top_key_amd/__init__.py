@@ -16,6 +16,7 @@ import torch
 from . import _lib
 
 RESCORE = {"auto": 0, "query": 1, "cluster": 2}
+CLUSTERS = {"content": 0, "positional": 1}
 DTYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
 IDX_OK, IDX_EINVAL, IDX_ENOMEM, IDX_EDEVICE, IDX_ECAUSAL, IDX_ESTATE, IDX_ECAPACITY, IDX_ENOTIMPL = \
@@ -76,12 +77,13 @@ class Index:
 def idx_create(heads: int, dim: int, dtype: str, max_keys: int, n_sink: int = 4, window: int = 1024,
                cluster_size: int = 128, seal_cap: int = 256, seal_iters: int = 10, refit_every: int = 16384,
                max_queries: int = 4096, max_budget: int = 8192, max_k: int = 2048,
-               rescore: str = "auto") -> Index:
+               rescore: str = "auto", clusters: str = "content") -> Index:
     cfg = dict(heads=heads, dim=dim, dtype=dtype, n_sink=n_sink, window=window, cluster_size=cluster_size,
                seal_cap=seal_cap, seal_iters=seal_iters, refit_every=refit_every, max_queries=max_queries,
-               max_budget=max_budget, max_k=max_k, rescore=rescore, max_keys=max_keys)
+               max_budget=max_budget, max_k=max_k, rescore=rescore, clusters=clusters, max_keys=max_keys)
     c = _lib.idx_config(heads, dim, DTYPES[dtype], n_sink, window, cluster_size, seal_cap, seal_iters,
-                        refit_every, max_queries, max_budget, max_k, RESCORE[rescore], max_keys)
+                        refit_every, max_queries, max_budget, max_k, RESCORE[rescore], CLUSTERS[clusters],
+                        max_keys)
     h = ctypes.c_void_p()
     _check(lib().idx_create(ctypes.byref(c), ctypes.byref(h)))
     return Index(h, cfg)

@@ -15,7 +15,7 @@ c_vp = ctypes.c_void_p
 class idx_config(ctypes.Structure):
     _fields_ = [("heads", c_i32), ("dim", c_i32), ("dtype", c_i32), ("n_sink", c_i32), ("window", c_i32),
                 ("cluster_size", c_i32), ("seal_cap", c_i32), ("seal_iters", c_i32), ("refit_every", c_i32),
-                ("max_queries", c_i32), ("max_budget", c_i32), ("max_k", c_i32), ("rescore_mode", c_i32),
+                ("max_queries", c_i32), ("max_budget", c_i32), ("max_k", c_i32), ("rescore_mode", c_i32), ("cluster_mode", c_i32),
                 ("max_keys", c_i64)]
 
 

@@ -100,6 +100,7 @@ struct SealParams {
   const uint8_t* keys;
   const float* kscale;
   int S, W, Cs, cap, iters;
+  int positional;     // 1: cluster i of a window = its keys [i*W/Cs, (i+1)*W/Cs), one pass
   int w0;
   int* size;          // seal store, indexed by slot w*Cs + c
   int* off;

@@ -188,6 +188,10 @@ int idx_create(const idx_config* cfg, idx_index** out) {
   if (c.max_budget < c.max_k) return fail(IDX_EINVAL, "max_budget must be >= max_k");
   if (c.rescore_mode < IDX_RESCORE_AUTO || c.rescore_mode > IDX_RESCORE_CLUSTER)
     return fail(IDX_EINVAL, "rescore_mode must be IDX_RESCORE_AUTO, _QUERY or _CLUSTER");
+  if (c.cluster_mode != IDX_CLUSTERS_CONTENT && c.cluster_mode != IDX_CLUSTERS_POSITIONAL)
+    return fail(IDX_EINVAL, "cluster_mode must be IDX_CLUSTERS_CONTENT or IDX_CLUSTERS_POSITIONAL");
+  if (c.cluster_mode == IDX_CLUSTERS_POSITIONAL && c.refit_every != 0)
+    return fail(IDX_EINVAL, "positional blocks are never refitted: refit_every must be 0");
   if (c.max_keys < 1 || c.max_keys > (int64_t)1 << 30) return fail(IDX_EINVAL, "max_keys must be 1..2^30");
 
   idx_index* ix = new (std::nothrow) idx_index();
@@ -319,7 +323,8 @@ int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_
     p.W = c.window;
     p.Cs = ix->Cs;
     p.cap = c.seal_cap;
-    p.iters = c.seal_iters;
+    p.positional = c.cluster_mode == IDX_CLUSTERS_POSITIONAL;
+    p.iters = p.positional ? 1 : c.seal_iters;
     p.w0 = ix->sealed;
     p.size = ix->sl_size;
     p.off = ix->sl_off;

@@ -59,114 +59,120 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   __syncthreads();
 
   for (int it = 0; it < p.iters; ++it) {
-    // ---- distances to every centroid, nearest ----
-    float acc[CS];
+    if (p.positional) {
+      // ---- position blocks: no distances, the means below are the centroids ----
+      if (tid < W) asg[tid] = tid / (W / CS);
+      __syncthreads();
+    } else {
+      // ---- distances to every centroid, nearest ----
+      float acc[CS];
 #pragma unroll
-    for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
-    int best = 0;
-    if (tid < W) {
-      const uint8_t* row = p.keys + (size_t)(base + tid) * RB;
-      float sk = 1.0f;
-      if constexpr (DT == DT_E4M3) sk = p.kscale[base + tid];
-      for (int i0 = 0; i0 < D; i0 += EPC) {
-        const uint4 raw = *reinterpret_cast<const uint4*>(row + i0 * Elem<DT>::bytes);
-        const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+      for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
+      int best = 0;
+      if (tid < W) {
+        const uint8_t* row = p.keys + (size_t)(base + tid) * RB;
+        float sk = 1.0f;
+        if constexpr (DT == DT_E4M3) sk = p.kscale[base + tid];
+        for (int i0 = 0; i0 < D; i0 += EPC) {
+          const uint4 raw = *reinterpret_cast<const uint4*>(row + i0 * Elem<DT>::bytes);
+          const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-          float xi;
-          if constexpr (DT == DT_F32) {
-            xi = __uint_as_float(wds[e]);
-          } else if constexpr (DT == DT_BF16) {
-            xi = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-          } else {
-            xi = e4m3_to_f32((wds[e >> 2] >> (8 * (e & 3))) & 0xFFu) * sk;
-          }
+          for (int e = 0; e < EPC; ++e) {
+            float xi;
+            if constexpr (DT == DT_F32) {
+              xi = __uint_as_float(wds[e]);
+            } else if constexpr (DT == DT_BF16) {
+              xi = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+            } else {
+              xi = e4m3_to_f32((wds[e >> 2] >> (8 * (e & 3))) & 0xFFu) * sk;
+            }
 #pragma unroll
-          for (int c = 0; c < CS; ++c) {
-            const float t = xi - cent[c * D + i0 + e];
-            acc[c] = acc[c] + t * t;
+            for (int c = 0; c < CS; ++c) {
+              const float t = xi - cent[c * D + i0 + e];
+              acc[c] = acc[c] + t * t;
+            }
           }
         }
-      }
 #pragma unroll
-      for (int c = 1; c < CS; ++c)
-        if (acc[c] < acc[best]) best = c;
-    }
-    if (tid < CS) cnt[tid] = 0;
-    if (tid == 0) s_over = 0;
-    __syncthreads();
-    if (tid < W) atomicAdd(&cnt[best], 1);
-    __syncthreads();
-    if (tid < CS && cnt[tid] > cap) s_over = 1;
-    __syncthreads();
-
-    if (!s_over) {
-      if (tid < W) asg[tid] = best;
-    } else {
-      // ---- greedy walk over all (D, key, cluster) triples ----
-      const int ntr = W * CS;
-      const int P2 = next_pow2(ntr);
-      if (tid < W) {
-#pragma unroll
-        for (int c = 0; c < CS; ++c)
-          sortbuf[tid * CS + c] = ((uint64_t)__float_as_uint(acc[c]) << 32) | (uint32_t)(tid * CS + c);
-      }
-      for (int i = ntr + tid; i < P2; i += bd) sortbuf[i] = ~0ull;
-      for (int j = tid; j < W; j += bd) {
-        asg[j] = -1;
-        first_lane[j] = 64;
+        for (int c = 1; c < CS; ++c)
+          if (acc[c] < acc[best]) best = c;
       }
       if (tid < CS) cnt[tid] = 0;
+      if (tid == 0) s_over = 0;
       __syncthreads();
-      bitonic_sort_asc(sortbuf, P2);
-      if (tid < 64) {
-        int placed = 0;
-        for (int st = 0; st < ntr && placed < W; st += 64) {
-          const int ti = st + lane;
-          const bool valid = ti < ntr;
-          const uint32_t id = valid ? (uint32_t)sortbuf[ti] : 0u;
-          const int j = (int)(id / CS), c = (int)(id % CS);
-          const bool elig = valid && asg[j] < 0 && cnt[c] < cap;
-          bool conflict = false;
+      if (tid < W) atomicAdd(&cnt[best], 1);
+      __syncthreads();
+      if (tid < CS && cnt[tid] > cap) s_over = 1;
+      __syncthreads();
+
+      if (!s_over) {
+        if (tid < W) asg[tid] = best;
+      } else {
+        // ---- greedy walk over all (D, key, cluster) triples ----
+        const int ntr = W * CS;
+        const int P2 = next_pow2(ntr);
+        if (tid < W) {
 #pragma unroll
-          for (int cc = 0; cc < CS; ++cc) {
-            const int pend = __popcll(__ballot(elig && c == cc));
-            const int have = cnt[cc];
-            if (have < cap && have + pend > cap) conflict = true;
-          }
-          if (!conflict) {
-            if (elig) atomicMin(&first_lane[j], lane);
-            __builtin_amdgcn_wave_barrier();
-            const bool win = elig && first_lane[j] == lane;
-            __builtin_amdgcn_wave_barrier();
-            if (elig) first_lane[j] = 64;
-            if (win) asg[j] = c;
+          for (int c = 0; c < CS; ++c)
+            sortbuf[tid * CS + c] = ((uint64_t)__float_as_uint(acc[c]) << 32) | (uint32_t)(tid * CS + c);
+        }
+        for (int i = ntr + tid; i < P2; i += bd) sortbuf[i] = ~0ull;
+        for (int j = tid; j < W; j += bd) {
+          asg[j] = -1;
+          first_lane[j] = 64;
+        }
+        if (tid < CS) cnt[tid] = 0;
+        __syncthreads();
+        bitonic_sort_asc(sortbuf, P2);
+        if (tid < 64) {
+          int placed = 0;
+          for (int st = 0; st < ntr && placed < W; st += 64) {
+            const int ti = st + lane;
+            const bool valid = ti < ntr;
+            const uint32_t id = valid ? (uint32_t)sortbuf[ti] : 0u;
+            const int j = (int)(id / CS), c = (int)(id % CS);
+            const bool elig = valid && asg[j] < 0 && cnt[c] < cap;
+            bool conflict = false;
 #pragma unroll
             for (int cc = 0; cc < CS; ++cc) {
-              const int add = __popcll(__ballot(win && c == cc));
-              if (lane == 0) cnt[cc] += add;
+              const int pend = __popcll(__ballot(elig && c == cc));
+              const int have = cnt[cc];
+              if (have < cap && have + pend > cap) conflict = true;
             }
-            placed += __popcll(__ballot(win));
-            __builtin_amdgcn_wave_barrier();
-          } else {
-            int add = 0;
-            if (lane == 0) {
-              for (int q = 0; q < 64 && st + q < ntr; ++q) {
-                const uint32_t id2 = (uint32_t)sortbuf[st + q];
-                const int j2 = (int)(id2 / CS), c2 = (int)(id2 % CS);
-                if (asg[j2] < 0 && cnt[c2] < cap) {
-                  asg[j2] = c2;
-                  cnt[c2] += 1;
-                  ++add;
+            if (!conflict) {
+              if (elig) atomicMin(&first_lane[j], lane);
+              __builtin_amdgcn_wave_barrier();
+              const bool win = elig && first_lane[j] == lane;
+              __builtin_amdgcn_wave_barrier();
+              if (elig) first_lane[j] = 64;
+              if (win) asg[j] = c;
+#pragma unroll
+              for (int cc = 0; cc < CS; ++cc) {
+                const int add = __popcll(__ballot(win && c == cc));
+                if (lane == 0) cnt[cc] += add;
+              }
+              placed += __popcll(__ballot(win));
+              __builtin_amdgcn_wave_barrier();
+            } else {
+              int add = 0;
+              if (lane == 0) {
+                for (int q = 0; q < 64 && st + q < ntr; ++q) {
+                  const uint32_t id2 = (uint32_t)sortbuf[st + q];
+                  const int j2 = (int)(id2 / CS), c2 = (int)(id2 % CS);
+                  if (asg[j2] < 0 && cnt[c2] < cap) {
+                    asg[j2] = c2;
+                    cnt[c2] += 1;
+                    ++add;
+                  }
                 }
               }
+              placed += __shfl(add, 0);
+              __builtin_amdgcn_wave_barrier();
             }
-            placed += __shfl(add, 0);
-            __builtin_amdgcn_wave_barrier();
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
 
     // ---- stable member lists: ascending position within each cluster ----

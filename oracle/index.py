@@ -49,7 +49,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import codec
-from .kmeans import mean_exact, nearest, seal_window, sqdist_exact
+from .kmeans import mean_exact, nearest, seal_blocks, seal_window, sqdist_exact
 from .score import indexer_scores
 
 
@@ -68,8 +68,11 @@ class OracleConfig:
     seal_cap: int = 256
     seal_iters: int = 10
     refit_every: int = 16384           # 0 = never refit
+    positional: bool = False           # clusters = contiguous blocks (no k-means, no refit)
 
     def __post_init__(self):
+        if self.positional and self.refit_every:
+            raise ValueError("positional blocks are never refitted (refit_every must be 0)")
         if self.window % self.cluster_size:
             raise ValueError("window must be a multiple of cluster_size")
         if self.refit_every and self.refit_every % self.window:
@@ -221,7 +224,10 @@ class OracleIndex:
         cfg = self.cfg
         lo = cfg.n_sink + w * cfg.window
         X = self.X[lo:lo + cfg.window]
-        assign, C, _ = seal_window(X, cfg.n_clusters, cfg.seal_cap, cfg.seal_iters)
+        if cfg.positional:
+            assign, C, _ = seal_blocks(X, cfg.n_clusters)
+        else:
+            assign, C, _ = seal_window(X, cfg.n_clusters, cfg.seal_cap, cfg.seal_iters)
         clusters = []
         for i in range(cfg.n_clusters):
             members = lo + np.nonzero(assign == i)[0]

@@ -79,6 +79,27 @@ def capped_greedy_assign(D: np.ndarray, cap: int) -> np.ndarray:
     return assign
 
 
+def seal_blocks(X: np.ndarray, n_clusters: int):
+    """Positional clusters of one window (the block-routing baseline): cluster i is
+    the contiguous block of keys [i*b, (i+1)*b), b = W / n_clusters, and its
+    centroid is the exact-order mean of the block.
+
+    This is the position-block grouping of the comparison method the pages call
+    HiSA (paper-daily explainer, "它到底在解决什么问题？": keys cut into contiguous
+    blocks by position, each block represented by its mean, blocks ranked by the
+    representative's score); AttentionIndex replaces the blocks by content clusters.
+    Returns (assign [W] int64, centroids [n_clusters, d] fp32, alive [n_clusters] bool).
+    """
+    X = np.asarray(X, dtype=np.float32)
+    W = X.shape[0]
+    if W % n_clusters:
+        raise ValueError("window must split into equal blocks")
+    b = W // n_clusters
+    assign = np.arange(W) // b
+    C = np.stack([mean_exact(X[i * b:(i + 1) * b]) for i in range(n_clusters)])
+    return assign, C, np.ones(n_clusters, dtype=bool)
+
+
 def seal_window(X: np.ndarray, n_clusters: int, cap: int, iters: int):
     """Size-capped k-means on one window of keys X [W, d] (ascending position).
 

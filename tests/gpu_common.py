@@ -49,7 +49,8 @@ def workload(name, **over):
 
 
 def oracle_cfg(wl):
-    return OracleConfig(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], **{k: wl[k] for k in CFG_KEYS})
+    return OracleConfig(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], positional=wl.get("positional", False),
+                        **{k: wl[k] for k in CFG_KEYS})
 
 
 def oracle_index(wl, inp, n_keys=None):
@@ -75,7 +76,9 @@ def gpu_index(wl, inp, n_keys=None, chunk=None, max_queries=None, max_budget=Non
     n = wl["N"] if n_keys is None else n_keys
     ix = ivf.idx_create(heads=wl["H"], dim=wl["d"], dtype=wl["dtype"], max_keys=wl["N"],
                         max_queries=max_queries or wl["T"], max_budget=max_budget or max(wl["budget"], wl["N"]),
-                        max_k=max_k or wl["k"], rescore=rescore, **{k: wl[k] for k in CFG_KEYS})
+                        max_k=max_k or wl["k"], rescore=rescore,
+                        clusters="positional" if wl.get("positional") else "content",
+                        **{k: wl[k] for k in CFG_KEYS})
     keys = to_dev(inp["keys"][:n])
     ks = to_dev(inp["k_scale"][:n]) if inp["k_scale"] is not None else None
     chunk = chunk or n

@@ -43,7 +43,8 @@ def test_every_declared_function_is_exported(lib):
 def _cfg(**over):
     from ivf_top_key_amd._lib import idx_config
     base = dict(heads=64, dim=128, dtype=2, n_sink=4, window=1024, cluster_size=128, seal_cap=256, seal_iters=10,
-                refit_every=16384, max_queries=4096, max_budget=8192, max_k=2048, rescore_mode=0, max_keys=1 << 20)
+                refit_every=16384, max_queries=4096, max_budget=8192, max_k=2048, rescore_mode=0, cluster_mode=0,
+                max_keys=1 << 20)
     base.update(over)
     return idx_config(*[base[f] for f, _ in idx_config._fields_])
 
@@ -54,6 +55,7 @@ def _cfg(**over):
     (dict(seal_cap=100), -1), (dict(seal_iters=0), -1), (dict(refit_every=1000), -1),
     (dict(max_k=5000), -1), (dict(max_budget=100), -1), (dict(max_keys=0), -1),
     (dict(max_keys=1 << 21), -6), (dict(max_budget=32768, max_k=4096), -6), (dict(rescore_mode=3), -1),
+    (dict(cluster_mode=2), -1), (dict(cluster_mode=1), -1),
 ])
 def test_create_rejects_bad_config(lib, over, code):
     h = ctypes.c_void_p()

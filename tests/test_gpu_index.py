@@ -31,6 +31,24 @@ def test_index_bit_exact(name):
         ivf.idx_destroy(gix)
 
 
+@pytest.mark.parametrize("name", ["c1", "e4m3_small"])
+def test_positional_blocks_bit_exact(name):
+    """Block-routing baseline: every window's clusters are its contiguous blocks with
+    exact-order means, bit for bit."""
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload(name, positional=True, refit_every=0)
+    gix = gpu_index(wl, inp, chunk=1500)
+    try:
+        oix = oracle_index(wl, inp)
+        got = compare_seal_store(ivf, gix, oix, name + " positional")
+        b = wl["cluster_size"]
+        assert np.all(got["sizes"] == b)
+        say(f"  ok: {len(oix.seals)} windows of position blocks")
+    finally:
+        ivf.idx_destroy(gix)
+
+
 def test_index_streamed_in_chunks_matches_one_shot():
     """Keys inserted 700 at a time (windows sealed across calls, refits launched as
     soon as due) give the same index as the oracle."""

@@ -154,6 +154,12 @@ def test_route_exact_ties(zero_queries):
         ivf.idx_destroy(gix)
 
 
+@pytest.mark.parametrize("name", ["bf16_small", "e4m3_small"])
+def test_route_positional_blocks(name):
+    """The same routing over position blocks (the block-routing baseline)."""
+    route_parity(name, positional=True, refit_every=0)
+
+
 @pytest.mark.parametrize("name,over", [
     ("c1", {}),
     ("bf16_small", {}),

@@ -190,3 +190,37 @@ def test_rep_quantisation_is_stored_with_cluster():
     c = make_cluster(3, np.array([1, 2]), np.float32([1.0, -2.0, 0.5]), "e4m3")
     assert c.rep_scale == np.float32(np.float32(2.0) / np.float32(448.0))
     assert np.allclose(c.rep_value, [1.0, -2.0, 0.5], rtol=2 ** -4)
+
+
+def test_positional_index_routes_whole_blocks():
+    """Block routing: clusters are the windows' contiguous 128-key blocks; with a budget of
+    sinks + open window + two blocks, the candidates are exactly the two blocks whose mean
+    representative scores highest, in rank order."""
+    from oracle import OracleConfig, OracleIndex
+    from oracle.index import query_values
+    from oracle.score import indexer_scores
+    import datagen
+    inp = datagen.workload_inputs(7, 4096, 1, 4095, 2, 32, 16, "f32")
+    cfg = OracleConfig(heads=2, dim=32, dtype="f32", n_sink=4, window=1024, cluster_size=128, refit_every=0,
+                       positional=True)
+    ix = OracleIndex(cfg)
+    ix.append(inp["keys"], None)
+    assert len(ix.seals) == 3
+    for w, clusters in enumerate(ix.seals):
+        for i, c in enumerate(clusters):
+            lo = 4 + w * 1024 + i * 128
+            assert np.array_equal(c.members, np.arange(lo, lo + 128))
+    n = 4096
+    open_len = n - (4 + 3 * 1024)
+    budget = 4 + open_len + 256
+    idx, sc, dbg = ix.route(inp["q"], None, inp["w"], 4095, 64, budget, debug=True)
+    d = dbg[0]
+    qv = query_values(inp["q"], None, "f32")
+    reps = np.stack([c.rep_value for w in ix.seals for c in w])
+    s = indexer_scores(qv, inp["w"].astype(np.float64), reps)[0]
+    top2 = np.argsort(-s, kind="stable")[:2]
+    assert [u for u, _ in d["used"]] == top2.tolist()
+    blocks = np.concatenate([np.arange(4 + 128 * b, 4 + 128 * (b + 1)) for b in top2])
+    assert np.array_equal(d["cand"][4 + open_len:], blocks)
+    with pytest.raises(ValueError):
+        OracleConfig(heads=2, dim=32, dtype="f32", refit_every=16384, positional=True)

@@ -125,3 +125,19 @@ def test_seal_capped_result_is_a_greedy_fixed_point():
     for c in range(4):
         if alive[c]:
             assert np.array_equal(C[c], mean_exact(X[a == c]))
+
+
+def test_seal_blocks_are_contiguous_means():
+    """Positional blocks: block i is keys [i*b, (i+1)*b) and its centroid is their mean
+    (the plain mean in float64 agrees to fp32 rounding)."""
+    from oracle.kmeans import seal_blocks
+    rng = np.random.default_rng(3)
+    X = rng.standard_normal((1024, 32)).astype(np.float32)
+    a, C, alive = seal_blocks(X, 8)
+    assert alive.all()
+    assert np.array_equal(a, np.repeat(np.arange(8), 128))
+    for i in range(8):
+        ref = X[i * 128:(i + 1) * 128].astype(np.float64).mean(axis=0)
+        assert np.allclose(C[i], ref, rtol=0, atol=1e-5)
+    with pytest.raises(ValueError):
+        seal_blocks(X[:1001], 8)
