@@ -212,6 +212,19 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
                    int32_t T, int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score,
                    const idx_route_debug* dbg, void* stream);
 
+/* Routed top-k for a decode batch: query t is the token at positions[t] (host array
+ * of T int64, any order, repeats allowed) and sees keys 0 .. positions[t].  This is
+ * the generation phase of the paper-daily explainer ("它到底在解决什么问题？" and the
+ * limitations paragraph on decoding): each generated token's key is inserted with
+ * idx_build_seal (n = 1 per step) and its query routed against the same index.
+ * Everything else as idx_route_topk.  The positions are read during the call
+ * (copied to device memory on `stream`).
+ * Errors: EINVAL (null positions or a negative one), ECAUSAL (a position >= n_keys),
+ * ESTATE, EINVAL / ECAPACITY as idx_route_topk. */
+int idx_route_topk_pos(idx_index* ix, const void* q, const float* q_scale, const float* w,
+                       const int64_t* positions, int32_t T, int32_t k, int32_t budget, int32_t* topk_idx,
+                       float* topk_score, const idx_route_debug* dbg, void* stream);
+
 /* Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass. */
 int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T);
 

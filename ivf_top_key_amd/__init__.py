@@ -132,6 +132,40 @@ def make_route_debug(T: int, cand_cap: int, order_cap: int, rep_cap: int, device
                 cand_scores=torch.full((T, cand_cap), float("nan"), dtype=torch.float32, device=device))
 
 
+def _route_debug(debug: dict | None):
+    if debug is None:
+        return None
+    ev = debug.get("events")
+    if ev is not None:
+        ev = ctypes.cast((ctypes.c_void_p * len(ev))(*ev), ctypes.POINTER(ctypes.c_void_p))
+    return _lib.idx_route_debug(
+        _ptr(debug.get("cand")), debug["cand"].shape[1] if debug.get("cand") is not None else 0,
+        _ptr(debug.get("cand_len")), _ptr(debug.get("order")), _ptr(debug.get("order_take")),
+        debug["order"].shape[1] if debug.get("order") is not None else 0, _ptr(debug.get("n_order")),
+        _ptr(debug.get("rep_scores")),
+        debug["rep_scores"].shape[1] if debug.get("rep_scores") is not None else 0,
+        _ptr(debug.get("version")), ev, int(debug.get("list_cap", 0)), _ptr(debug.get("cand_scores")))
+
+
+def idx_route_topk_pos(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, positions, k: int, budget: int,
+                       topk_idx=None, topk_score=None, debug: dict | None = None, stream=None):
+    """Decode batch: query t at positions[t] (host integers)."""
+    T = q.shape[0]
+    pos = np.ascontiguousarray(np.asarray(positions, dtype=np.int64).reshape(-1))
+    if pos.shape[0] != T:
+        raise ValueError("one position per query")
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=q.device)
+    if topk_score is None:
+        topk_score = torch.empty((T, k), dtype=torch.float32, device=q.device)
+    dbg = _route_debug(debug)
+    _check(lib().idx_route_topk_pos(ix.handle, _ptr(q, ELEM_BYTES[ix.dtype], "q"), _ptr(q_scale, 4, "q_scale"),
+                                    _ptr(w, 4, "w"), pos.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), T, k,
+                                    budget, _ptr(topk_idx, 4, "topk_idx"), _ptr(topk_score, 4, "topk_score"),
+                                    ctypes.byref(dbg) if dbg is not None else None, _stream(stream)))
+    return topk_idx, topk_score
+
+
 def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0: int, k: int, budget: int,
                    topk_idx=None, topk_score=None, debug: dict | None = None, stream=None):
     T = q.shape[0]

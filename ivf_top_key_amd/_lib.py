@@ -48,6 +48,8 @@ SIGNATURES = [
     ("idx_publish", c_i32, [c_vp, c_vp, ctypes.POINTER(c_i32)]),
     ("idx_route_topk", c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,
                                ctypes.POINTER(idx_route_debug), c_vp]),
+    ("idx_route_topk_pos", c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(c_i64), c_i32, c_i32, c_i32, c_vp, c_vp,
+                                   ctypes.POINTER(idx_route_debug), c_vp]),
     ("idx_exhaustive_workspace_bytes", c_i64, [c_i64, c_i32]),
     ("idx_exhaustive_topk", c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32,
                                     c_vp, c_vp, c_vp, c_i64, c_vp]),

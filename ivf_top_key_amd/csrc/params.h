@@ -20,7 +20,8 @@ struct StoreView {
   const float* rsc;
 };
 
-// Everything the routed path needs.  Query t sits at position q_pos0 + t; its
+// Everything the routed path needs.  Query t sits at position qpos[t] when qpos is
+// set (a decode batch), at q_pos0 + t otherwise; its
 // version is computed on the device from (S, W, Cs, wpr, P): m = windows inside
 // the prefix, epoch r = min(P, m / wpr), slots [0, r*wpr*Cs) come from epoch r's
 // store and slots [r*wpr*Cs, m*Cs) from the seal store.
@@ -34,6 +35,7 @@ struct RouteParams {
   int H;
   int T;
   int64_t q_pos0;
+  const int64_t* qpos; // [T] positions of a decode batch, or null
   int k;
   int budget;
   int S, W, Cs, wpr, P;

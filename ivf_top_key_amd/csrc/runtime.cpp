@@ -101,6 +101,7 @@ struct idx_index {
   int* cand = nullptr;
   int* cand_len = nullptr;
   int* redo = nullptr;
+  int64_t* qpos = nullptr;   // positions of a decode batch (idx_route_topk_pos)
   // cluster-major rescoring: selections per query, pairs grouped by cluster, work items
   int64_t sel_cap = 0, pair_cap = 0, item_cap = 0;
   int n_ids = 0;
@@ -230,7 +231,8 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->sl_rep, ix->slot_cap * ix->RB) && ix->alloc(&ix->sl_rsc, ix->slot_cap) &&
             ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
             ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
-            ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries);
+            ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries) &&
+            ix->alloc(&ix->qpos, c.max_queries);
   if (ok && c.rescore_mode == IDX_RESCORE_CLUSTER)
     ok = ix->alloc(&ix->sel_id, (int64_t)c.max_queries * ix->sel_cap) &&
             ix->alloc(&ix->sel_dst, (int64_t)c.max_queries * ix->sel_cap) && ix->alloc(&ix->n_sel, c.max_queries) &&
@@ -411,9 +413,11 @@ int idx_publish(idx_index* ix, void* stream, int32_t* published) {
   return IDX_OK;
 }
 
-int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
-                   int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score, const idx_route_debug* dbg,
-                   void* stream) {
+// Shared body of idx_route_topk (positions == nullptr: q_pos0 + t) and
+// idx_route_topk_pos (host positions, copied to the index's device buffer).
+static int route_common(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
+                        const int64_t* positions, int32_t T, int32_t k, int32_t budget, int32_t* topk_idx,
+                        float* topk_score, const idx_route_debug* dbg, void* stream) {
   g_err.clear();
   if (int e = check_handle(ix)) return e;
   const idx_config& c = ix->cfg;
@@ -424,25 +428,33 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
   if (k < 1 || k > c.max_k) return fail(IDX_ECAPACITY, "k %d outside 1..max_k %d", k, c.max_k);
   if (budget < k) return fail(IDX_EINVAL, "budget %d < k %d", budget, k);
   if (budget > c.max_budget) return fail(IDX_ECAPACITY, "budget %d exceeds max_budget %d", budget, c.max_budget);
-  if (q_pos0 < 0) return fail(IDX_EINVAL, "q_pos0 must be >= 0");
-  if (q_pos0 + T > ix->n_keys)
-    return fail(IDX_ECAUSAL, "query position %lld has no inserted key (%lld keys)", (long long)(q_pos0 + T - 1),
+  int64_t pmin = q_pos0, pmax = q_pos0 + T - 1;
+  if (positions) {
+    pmin = pmax = positions[0];
+    for (int32_t t = 1; t < T; ++t) {
+      pmin = std::min(pmin, positions[t]);
+      pmax = std::max(pmax, positions[t]);
+    }
+  }
+  if (pmin < 0) return fail(IDX_EINVAL, "query positions must be >= 0");
+  if (pmax >= ix->n_keys)
+    return fail(IDX_ECAUSAL, "query position %lld has no inserted key (%lld keys)", (long long)pmax,
                 (long long)ix->n_keys);
   const int P = ix->published;
   auto windows_in = [&](int64_t n) -> int {
     return n >= c.n_sink ? (int)((n - c.n_sink) / c.window) : 0;
   };
   if (ix->wpr) {
-    // epochs used by this call: r_t = min(P, m_t / wpr) grows by at most one per window,
-    // so every epoch between the first and the last query's is used; each must still
-    // be held (the ring keeps three stores and a refit in flight overwrites the oldest)
-    const int r0 = std::min(P, windows_in(q_pos0 + 1) / ix->wpr);
-    const int r1 = std::min(P, windows_in(q_pos0 + T) / ix->wpr);
+    // epochs used by this call: r_t = min(P, m_t / wpr) is monotone in the position,
+    // so the smallest position uses the oldest epoch; every epoch used must still be
+    // held (the ring keeps three stores and a refit in flight overwrites the oldest)
+    const int r0 = std::min(P, windows_in(pmin + 1) / ix->wpr);
+    const int r1 = std::min(P, windows_in(pmax + 1) / ix->wpr);
     const int oldest = std::max(1, ix->computed - 2);
     const int lo = std::max(r0, 1);
     if (r1 >= 1 && lo < oldest)
       return fail(IDX_ESTATE, "queries at %lld..%lld need epoch %d; epochs below %d are no longer held",
-                  (long long)q_pos0, (long long)(q_pos0 + T - 1), lo, oldest);
+                  (long long)pmin, (long long)pmax, lo, oldest);
   }
   (void)hipSetDevice(ix->device);
   hipStream_t s = (hipStream_t)stream;
@@ -456,6 +468,7 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
   p.H = c.heads;
   p.T = T;
   p.q_pos0 = q_pos0;
+  p.qpos = nullptr;
   p.k = k;
   p.budget = budget;
   p.S = c.n_sink;
@@ -504,7 +517,12 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
     p.dbg_cand_scores = dbg->cand_scores;
     p.dbg_cand_ld = dbg->cand_cap;
   }
-  const int max_slots = windows_in(q_pos0 + T) * ix->Cs;
+  const int max_slots = windows_in(pmax + 1) * ix->Cs;
+  if (positions) {
+    hipError_t ec = hipMemcpyAsync(ix->qpos, positions, (size_t)T * sizeof(int64_t), hipMemcpyHostToDevice, s);
+    if (ec != hipSuccess) return device_error(ix, ec, "position copy");
+    p.qpos = ix->qpos;
+  }
   hipEvent_t* ev = (dbg && dbg->events) ? reinterpret_cast<hipEvent_t*>(dbg->events) : nullptr;
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
@@ -542,6 +560,26 @@ int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const flo
     if (e != hipSuccess) return device_error(ix, e, "route debug copy");
   }
   return IDX_OK;
+}
+
+int idx_route_topk(idx_index* ix, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
+                   int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score, const idx_route_debug* dbg,
+                   void* stream) {
+  if (q_pos0 < 0) {
+    g_err.clear();
+    return fail(IDX_EINVAL, "q_pos0 must be >= 0");
+  }
+  return route_common(ix, q, q_scale, w, q_pos0, nullptr, T, k, budget, topk_idx, topk_score, dbg, stream);
+}
+
+int idx_route_topk_pos(idx_index* ix, const void* q, const float* q_scale, const float* w, const int64_t* positions,
+                       int32_t T, int32_t k, int32_t budget, int32_t* topk_idx, float* topk_score,
+                       const idx_route_debug* dbg, void* stream) {
+  if (!positions) {
+    g_err.clear();
+    return fail(IDX_EINVAL, "null positions");
+  }
+  return route_common(ix, q, q_scale, w, 0, positions, T, k, budget, topk_idx, topk_score, dbg, stream);
 }
 
 int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T) {

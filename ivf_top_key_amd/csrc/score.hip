@@ -235,7 +235,7 @@ struct QVer {
 
 __device__ __forceinline__ QVer query_version(const RouteParams& p, int t) {
   QVer v;
-  v.n = p.q_pos0 + t + 1;
+  v.n = (p.qpos ? p.qpos[t] : p.q_pos0 + t) + 1;
   v.m = v.n >= p.S ? (int)((v.n - p.S) / p.W) : 0;
   v.r = p.wpr ? min(p.P, v.m / p.wpr) : 0;
   v.split = v.r * p.wpr * p.Cs;

@@ -308,17 +308,26 @@ class OracleIndex:
     # ---- routing --------------------------------------------------------
     def route(self, q_raw, q_scale, w, q_pos0: int, k: int, budget: int, debug: bool = False):
         """Routed top-k for queries at positions q_pos0 .. q_pos0+T-1."""
+        T = np.asarray(q_raw).shape[0]
+        return self.route_at(q_raw, q_scale, w, q_pos0 + np.arange(T), k, budget, debug)
+
+    def route_at(self, q_raw, q_scale, w, positions, k: int, budget: int, debug: bool = False):
+        """Routed top-k for queries at arbitrary positions (a decode batch: query t is
+        the token at positions[t] and sees keys 0 .. positions[t])."""
         cfg = self.cfg
         qv = query_values(q_raw, q_scale, cfg.dtype)
         w = np.asarray(w, dtype=np.float64)
         T = qv.shape[0]
-        if q_pos0 + T > self.n_keys:
+        positions = np.asarray(positions, dtype=np.int64)
+        if positions.shape != (T,):
+            raise ValueError("one position per query")
+        if T and (positions.min() < 0 or positions.max() >= self.n_keys):
             raise CausalityError("query position beyond the inserted keys")
         idx = np.full((T, k), -1, dtype=np.int64)
         sc = np.full((T, k), -np.inf, dtype=np.float64)
         dbg = []
         for t in range(T):
-            n = q_pos0 + t + 1
+            n = int(positions[t]) + 1
             vis = self.visible(n)
             base = self.base_candidates(n)
             if vis:

@@ -70,6 +70,7 @@ def test_calls_on_null_handle(lib):
     assert lib.idx_refit(None, None, None, None) == -1
     assert lib.idx_publish(None, None, None) == -1
     assert lib.idx_route_topk(None, None, None, None, 0, 1, 1, 1, None, None, None, None) == -1
+    assert lib.idx_route_topk_pos(None, None, None, None, None, 1, 1, 1, None, None, None, None) == -1
     assert lib.idx_export(None, -1, None) == -1
     assert lib.idx_get_info(None, None) == -1
     assert lib.idx_destroy(None) == 0

@@ -224,3 +224,26 @@ def test_positional_index_routes_whole_blocks():
     assert np.array_equal(d["cand"][4 + open_len:], blocks)
     with pytest.raises(ValueError):
         OracleConfig(heads=2, dim=32, dtype="f32", refit_every=16384, positional=True)
+
+
+def test_route_at_positions_matches_single_query_routes():
+    """A decode batch at scattered positions routes each query exactly as a one-query
+    call at that position (the version, candidates and top-k depend only on it)."""
+    from oracle import OracleConfig, OracleIndex
+    import datagen
+    inp = datagen.workload_inputs(11, 6000, 6000, 0, 2, 32, 16, "f32")
+    cfg = OracleConfig(heads=2, dim=32, dtype="f32", n_sink=4, window=1024, cluster_size=128, refit_every=2048)
+    ix = OracleIndex(cfg)
+    ix.append(inp["keys"], None)
+    while ix.refit_due():
+        ix.refit()
+        ix.publish()
+    pos = np.array([5999, 3, 1027, 4100, 2051, 5000])
+    q, w = inp["q"][pos], inp["w"][pos]
+    idx, sc = ix.route_at(q, None, w, pos, 32, 1500)
+    for t, p in enumerate(pos):
+        i1, s1 = ix.route(q[t:t + 1], None, w[t:t + 1], int(p), 32, 1500)
+        assert np.array_equal(idx[t], i1[0]) and np.array_equal(sc[t], s1[0])
+        assert np.all(idx[t][idx[t] >= 0] <= p)
+    with pytest.raises(Exception):
+        ix.route_at(q[:1], None, w[:1], np.array([6000]), 32, 1500)
