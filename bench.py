@@ -100,6 +100,8 @@ def main():
     ap.add_argument("--workload", default="c4")
     ap.add_argument("--budget", type=int, default=8192)
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--ablation", action="store_true",
+                    help="also measure recall vs prefix length for seal-only, refit intervals and position blocks")
     ap.add_argument("--no-exhaustive", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--rescore", default="auto", choices=["auto", "query", "cluster"],
@@ -289,6 +291,31 @@ def main():
             extra["budget_sweep"] = sweep
         del ws
 
+    # ---- decode-shaped routing: batches of queries at scattered positions ----
+    rng = np.random.default_rng(5)
+    dec = {}
+    for B in (1, 64):
+        pos = (N - 1 - rng.integers(0, 32768, size=B)).astype(np.int64)   # the two newest epochs
+        sel = torch.from_numpy(rng.integers(0, T, size=B)).to(dev)
+        qb = q.index_select(0, sel)
+        qsb = qs.index_select(0, sel) if qs is not None else None
+        wb = w.index_select(0, sel)
+        for _ in range(3):
+            ivf.idx_route_topk_pos(ix, qb, qsb, wb, pos, k, budget)
+        d0, d1 = hip.event(), hip.event()
+        hip.h.hipEventRecord(ctypes.c_void_p(d0), ctypes.c_void_p(stream.cuda_stream))
+        for _ in range(20):
+            ivf.idx_route_topk_pos(ix, qb, qsb, wb, pos, k, budget)
+        hip.h.hipEventRecord(ctypes.c_void_p(d1), ctypes.c_void_p(stream.cuda_stream))
+        torch.cuda.synchronize()
+        dms = hip.elapsed(d0, d1) / 20
+        dec[str(B)] = dict(ms_per_call=round(dms, 4), queries_per_s=round(B / (dms * 1e-3), 1))
+    extra["decode_batches"] = dec
+    log(f"decode batches {dec}")
+
+    if args.ablation:
+        extra["ablation"] = ablation(ivf, torch, wl, inp, keys, ks, q, qs, w, dev, budget, k)
+
     # ---- CPU oracle on a bounded sample of the same queries ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -355,6 +382,47 @@ def blas_threads():
     except Exception:
         pass
     return os.cpu_count()
+
+
+def ablation(ivf, torch, wl, inp, keys, ks, q, qs, w, dev, budget, k, n_q=512,
+             lengths=(16384, 65536, 262144, 1048576)):
+    """Recall of routed vs exhaustive top-k (the same n_q queries placed at the end of
+    each prefix length) for: seal-only clustering, refits every 8K / 16K / 32K tokens,
+    and position blocks (the block-routing baseline).  The index is streamed once per
+    configuration; each length is measured when the stream reaches it."""
+    N, H, dt = wl["N"], wl["H"], wl["dtype"]
+    lengths = [L for L in lengths if L <= N]
+    qa, wa = q[:n_q], w[:n_q]
+    qsa = qs[:n_q] if qs is not None else None
+    ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(max(lengths), n_q) // 4, dtype=torch.float32, device=dev)
+    exh = {}
+    for L in lengths:
+        e_idx, _ = ivf.idx_exhaustive_topk(keys, ks, dt, H, qa, qsa, wa, L - n_q, k, workspace=ws, n_keys=L)
+        exh[L] = e_idx.cpu().numpy()
+    out = {}
+    configs = [("seal-only", "content", 0), ("refit every 8K", "content", 8192),
+               ("refit every 16K", "content", 16384), ("refit every 32K", "content", 32768),
+               ("position blocks", "positional", 0)]
+    for name, clusters, R in configs:
+        ix = ivf.idx_create(heads=H, dim=wl["d"], dtype=dt, max_keys=N, n_sink=wl["n_sink"], window=wl["window"],
+                            cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"], seal_iters=wl["seal_iters"],
+                            refit_every=R, max_queries=n_q, max_budget=budget, max_k=k, clusters=clusters)
+        res = {}
+        done = 0
+        chunk = 16384
+        for L in lengths:
+            while done < L:
+                b = min(L, done + chunk)
+                ivf.idx_build_seal(ix, keys[done:b], None if ks is None else ks[done:b])
+                while ivf.idx_refit(ix):
+                    ivf.idx_publish(ix)
+                done = b
+            r_idx, _ = ivf.idx_route_topk(ix, qa, qsa, wa, L - n_q, k, budget)
+            res[str(L)] = summarize(recall_per_query(r_idx.cpu().numpy(), exh[L]))["mean"]
+        ivf.idx_destroy(ix)
+        out[name] = res
+        log(f"ablation {name}: {res}")
+    return dict(budget=budget, k=k, queries=n_q, recall_by_prefix=out)
 
 
 def cpu_baseline(ix, inp, wl, budget, sample):
