@@ -41,6 +41,7 @@ STREAM_KEY_NOISE = 2
 STREAM_QUERY = 3
 STREAM_WEIGHT = 4
 STREAM_ADVERSARIAL = 5
+STREAM_ENCODER = 6
 
 
 def _rng(seed: int, stream: int) -> np.random.Generator:
@@ -120,6 +121,19 @@ def make_adversarial_keys(seed: int, N: int, d: int, M: int, a: float = 1.0,
     s = np.where(rng.random(N) < 0.5, -1.0, 1.0)
     eps = rng.standard_normal((N, d))
     return (mu[z] + (s * a)[:, None] * u[z] + (noise / np.sqrt(d)) * eps).astype(np.float32)
+
+
+def encoder_weights(seed: int, d: int, alpha: float = 0.25, h: int = 128) -> np.ndarray:
+    """Seeded stand-in weights for the learned-representative encoder (packed order:
+    W1 [h, d], b1 [h], W2 [h, h], b2 [h], Wa [h, d + 1 + 2h], ba [h], Wb [d, h], bb [d],
+    alpha), matrices N(0, 1/fan_in), biases zero."""
+    rng = _rng(seed, STREAM_ENCODER)
+    parts = []
+    for rows, cols in ((h, d), (h, h), (h, d + 1 + 2 * h), (d, h)):
+        parts.append((rng.standard_normal((rows, cols)) / np.sqrt(cols)).reshape(-1))
+        parts.append(np.zeros(rows))
+    parts.append(np.array([alpha]))
+    return np.concatenate(parts).astype(np.float32)
 
 
 # --------------------------------------------------------------------------

@@ -156,6 +156,8 @@ typedef struct {
   float* centroids;      /* [n_slots, d] fp32                                           */
   void* reps;            /* [n_slots, d] representatives in the key format              */
   float* rep_scale;      /* [n_slots] (1.0 unless E4M3)                                 */
+  float* rep_f32;        /* [n_slots, d]: representative before quantization (the
+                            centroid, or the learned representative with an encoder)     */
 } idx_export_buf;
 
 /* Create an index on the current HIP device; *out receives the handle. */
@@ -192,6 +194,18 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
  * new epoch for queries whose prefix holds all of its keys.  published: host out,
  * the newest visible epoch (may be NULL). */
 int idx_publish(idx_index* ix, void* stream, int32_t* published);
+
+/* Learned representatives (paper-daily explainer, "代表向量为什么要学？"): clusters
+ * keep their distance-based members and centroid, and the representative that
+ * queries score becomes mean + alpha * tanh(Wb ReLU(Wa z + ba) + bb) with
+ * z = [mean, log n, mean and max over members of W2 ReLU(W1 x + b1) + b2] (128
+ * hidden units).  weights: device array of idx_encoder_floats(dim) fp32 values,
+ * packed W1 [128, d], b1 [128], W2 [128, 128], b2 [128], Wa [128, d + 257],
+ * ba [128], Wb [d, 128], bb [d], alpha; copied on `stream`.  Applies to clusters
+ * created by later seals and refits; NULL returns to mean representatives.
+ * Errors: ESTATE while a refit is launched but not yet published. */
+int64_t idx_encoder_floats(int32_t dim);   /* -1 for an unsupported dim */
+int idx_set_encoder(idx_index* ix, const float* weights, void* stream);
 
 /* Routed top-k for T queries at positions q_pos0 .. q_pos0 + T - 1.
  *   q:       device [T, H, d] in the index dtype.

@@ -226,13 +226,28 @@ def idx_export(ix: Index, which: int) -> dict:
     out = dict(sizes=np.zeros(ns, np.int32), offsets=np.zeros(ns, np.int32), members=np.zeros(nm, np.int32),
                centroids=np.zeros((ns, d), np.float32),
                reps=np.zeros((ns, d), {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[ix.dtype]),
-               rep_scale=np.zeros(ns, np.float32))
+               rep_scale=np.zeros(ns, np.float32), rep_f32=np.zeros((ns, d), np.float32))
     for k in out:
         setattr(buf, k, out[k].ctypes.data if out[k].size else None)
     _check(lib().idx_export(ix.handle, which, ctypes.byref(buf)))
     return out
 
 
+def idx_encoder_floats(dim: int) -> int:
+    return int(lib().idx_encoder_floats(dim))
+
+
+def idx_set_encoder(ix: Index, weights: torch.Tensor | None, stream=None):
+    """Learned representatives from now on (weights: float32 device tensor in the packed
+    layout, idx_encoder_floats(dim) values), or None for mean representatives."""
+    if weights is not None:
+        if weights.dtype != torch.float32 or weights.numel() != idx_encoder_floats(ix.cfg["dim"]):
+            raise ValueError("encoder weights must be float32 with idx_encoder_floats(dim) values")
+        weights = weights.contiguous()
+    _check(lib().idx_set_encoder(ix.handle, _ptr(weights, 4, "weights"), _stream(stream)))
+
+
 __all__ = ["IdxError", "Index", "idx_create", "idx_destroy", "idx_last_error", "idx_get_info", "idx_build_seal",
-           "idx_refit", "idx_publish", "idx_route_topk", "idx_exhaustive_workspace_bytes", "idx_exhaustive_topk",
-           "idx_export", "make_route_debug", "DTYPES"]
+           "idx_refit", "idx_publish", "idx_route_topk", "idx_route_topk_pos", "idx_exhaustive_workspace_bytes",
+           "idx_exhaustive_topk", "idx_export", "idx_encoder_floats", "idx_set_encoder", "make_route_debug",
+           "DTYPES"]

@@ -34,7 +34,7 @@ class idx_route_debug(ctypes.Structure):
 
 class idx_export_buf(ctypes.Structure):
     _fields_ = [("n_slots", c_i32), ("n_members", c_i32), ("sizes", c_vp), ("offsets", c_vp), ("members", c_vp),
-                ("centroids", c_vp), ("reps", c_vp), ("rep_scale", c_vp)]
+                ("centroids", c_vp), ("reps", c_vp), ("rep_scale", c_vp), ("rep_f32", c_vp)]
 
 
 # (name, restype, argtypes) of every exported function
@@ -54,6 +54,8 @@ SIGNATURES = [
     ("idx_exhaustive_topk", c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32,
                                     c_vp, c_vp, c_vp, c_i64, c_vp]),
     ("idx_export", c_i32, [c_vp, c_i32, ctypes.POINTER(idx_export_buf)]),
+    ("idx_encoder_floats", c_i64, [c_i32]),
+    ("idx_set_encoder", c_i32, [c_vp, c_vp, c_vp]),
 ]
 
 _lib = None

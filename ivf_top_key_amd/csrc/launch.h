@@ -20,5 +20,7 @@ hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht,
 bool rescore_fits(int cand_cap, int k);
 hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, hipStream_t s);
 hipError_t launch_refit(const RefitParams& p, int dtype, int dim, hipStream_t s);
+hipError_t launch_encode(const EncParams& p, int dtype, int dim, hipStream_t s);
+int64_t encoder_floats(int dim);
 
 }  // namespace ivftk

@@ -108,6 +108,7 @@ struct SealParams {
   int* off;
   int* members;       // [windows * W], window w's members at [w*W, (w+1)*W)
   float* cent;
+  float* lrep;        // representative before quantization (= centroid; an encoder may replace it)
   uint8_t* rep;
   float* rsc;
 };
@@ -137,6 +138,7 @@ struct RefitParams {
   int* off;
   int* members;
   float* cent;
+  float* lrep;         // representative before quantization (= centroid; an encoder may replace it)
   uint8_t* rep;
   float* rsc;
   float* drift;
@@ -152,6 +154,19 @@ struct RefitParams {
   int* ovf;            // keys whose candidate list overflowed: exact brute force
   int* ovf_count;
   int brute_ovf;       // 1: the brute-force kernel takes its keys from ovf
+};
+
+// Learned representatives of slots [slot0, slot0 + n_slots) of one store.
+struct EncParams {
+  const uint8_t* keys;
+  const float* kscale;
+  int64_t n_keys;
+  StoreView st;        // size, off, members, cent of the store
+  const float* w;      // packed encoder weights
+  float* lrep;         // [slots, d] out: representative before quantization
+  uint8_t* rep;        // [slots, RB] out: representative in the key format
+  float* rsc;          // [slots] out: its scale
+  int slot0, n_slots;
 };
 
 }  // namespace ivftk

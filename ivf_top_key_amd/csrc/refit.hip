@@ -521,6 +521,7 @@ __global__ __launch_bounds__(256) void k_refit_mean(RefitParams p) {
     out = warm_cent(p, s, D)[i];
   }
   p.cent[(size_t)s * D + i] = out;
+  p.lrep[(size_t)s * D + i] = out;
 }
 
 // per slot: representative, drift of the centroid, largest drift

@@ -59,6 +59,7 @@ struct EpochStore {
   int* off = nullptr;
   int* members = nullptr;
   float* cent = nullptr;
+  float* lrep = nullptr;
   uint8_t* rep = nullptr;
   float* rsc = nullptr;
   float* drift = nullptr;
@@ -83,6 +84,9 @@ struct idx_index {
   float* kscale = nullptr;
   int *sl_size = nullptr, *sl_off = nullptr, *sl_members = nullptr;
   float* sl_cent = nullptr;
+  float* sl_lrep = nullptr;
+  float* enc = nullptr;      // learned-representative weights (packed), used when has_enc
+  bool has_enc = false;
   uint8_t* sl_rep = nullptr;
   float* sl_rsc = nullptr;
   EpochStore ep[3];
@@ -229,6 +233,7 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->sl_size, ix->slot_cap) && ix->alloc(&ix->sl_off, ix->slot_cap) &&
             ix->alloc(&ix->sl_members, ix->member_cap) && ix->alloc(&ix->sl_cent, ix->slot_cap * c.dim) &&
             ix->alloc(&ix->sl_rep, ix->slot_cap * ix->RB) && ix->alloc(&ix->sl_rsc, ix->slot_cap) &&
+            ix->alloc(&ix->sl_lrep, ix->slot_cap * c.dim) && ix->alloc(&ix->enc, encoder_floats(c.dim)) &&
             ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
             ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
             ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries) &&
@@ -246,6 +251,7 @@ int idx_create(const idx_config* cfg, idx_index** out) {
       EpochStore& e = ix->ep[i];
       ok = ix->alloc(&e.size, ix->ep_slot_cap) && ix->alloc(&e.off, ix->ep_slot_cap) &&
            ix->alloc(&e.members, ix->ep_member_cap) && ix->alloc(&e.cent, ix->ep_slot_cap * c.dim) &&
+           ix->alloc(&e.lrep, ix->ep_slot_cap * c.dim) &&
            ix->alloc(&e.rep, ix->ep_slot_cap * ix->RB) && ix->alloc(&e.rsc, ix->ep_slot_cap) &&
            ix->alloc(&e.drift, ix->ep_slot_cap) && ix->alloc(&e.drift_max, 1);
     }
@@ -332,9 +338,24 @@ int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_
     p.off = ix->sl_off;
     p.members = ix->sl_members;
     p.cent = ix->sl_cent;
+    p.lrep = ix->sl_lrep;
     p.rep = ix->sl_rep;
     p.rsc = ix->sl_rsc;
     e = launch_seal(p, c.dtype, c.dim, new_windows, s);
+    if (e == hipSuccess && ix->has_enc) {
+      EncParams ep{};
+      ep.keys = ix->keys;
+      ep.kscale = ix->kscale;
+      ep.n_keys = ix->n_keys;
+      ep.st = ix->seal_view();
+      ep.w = ix->enc;
+      ep.lrep = ix->sl_lrep;
+      ep.rep = ix->sl_rep;
+      ep.rsc = ix->sl_rsc;
+      ep.slot0 = ix->sealed * ix->Cs;
+      ep.n_slots = (int)(new_windows * ix->Cs);
+      e = launch_encode(ep, c.dtype, c.dim, s);
+    }
     if (e != hipSuccess) return device_error(ix, e, "seal launch");
     ix->sealed = (int)full;
   }
@@ -379,6 +400,7 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   p.off = out.off;
   p.members = out.members;
   p.cent = out.cent;
+  p.lrep = out.lrep;
   p.rep = out.rep;
   p.rsc = out.rsc;
   p.drift = out.drift;
@@ -393,6 +415,20 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   p.tile = TILE;
   p.n_tiles = (int)((p.B_r - p.S + TILE - 1) / TILE);
   e = launch_refit(p, c.dtype, c.dim, side);
+  if (e == hipSuccess && ix->has_enc) {
+    EncParams ep{};
+    ep.keys = ix->keys;
+    ep.kscale = ix->kscale;
+    ep.n_keys = ix->n_keys;
+    ep.st = StoreView{out.size, out.off, out.members, out.cent, out.rep, out.rsc};
+    ep.w = ix->enc;
+    ep.lrep = out.lrep;
+    ep.rep = out.rep;
+    ep.rsc = out.rsc;
+    ep.slot0 = 0;
+    ep.n_slots = r * ix->Q;
+    e = launch_encode(ep, c.dtype, c.dim, side);
+  }
   if (e == hipSuccess) e = hipEventRecord(ix->ev_refit, side);
   if (e != hipSuccess) return device_error(ix, e, "refit launch");
   ix->computed = r;
@@ -633,27 +669,48 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
   return IDX_OK;
 }
 
+int64_t idx_encoder_floats(int32_t dim) {
+  if (dim != 32 && dim != 64 && dim != 128) return -1;
+  return encoder_floats(dim);
+}
+
+int idx_set_encoder(idx_index* ix, const float* weights, void* stream) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (ix->computed != ix->published) return fail(IDX_ESTATE, "a refit is in flight; publish it first");
+  if (!weights) {
+    ix->has_enc = false;
+    return IDX_OK;
+  }
+  (void)hipSetDevice(ix->device);
+  const hipError_t e = hipMemcpyAsync(ix->enc, weights, (size_t)encoder_floats(ix->cfg.dim) * sizeof(float),
+                                      hipMemcpyDeviceToDevice, (hipStream_t)stream);
+  if (e != hipSuccess) return device_error(ix, e, "encoder copy");
+  ix->has_enc = true;
+  return IDX_OK;
+}
+
 int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
   g_err.clear();
   if (int e = check_handle(ix)) return e;
   if (!buf) return fail(IDX_EINVAL, "null export buffer");
   const idx_config& c = ix->cfg;
   const int *size, *off, *members;
-  const float *cent, *rsc;
+  const float *cent, *rsc, *lrep;
   const uint8_t* rep;
   int64_t n_slots, n_members;
   if (which == -1) {
     n_slots = (int64_t)ix->sealed * ix->Cs;
     n_members = (int64_t)ix->sealed * c.window;
     size = ix->sl_size; off = ix->sl_off; members = ix->sl_members;
-    cent = ix->sl_cent; rep = ix->sl_rep; rsc = ix->sl_rsc;
+    cent = ix->sl_cent; rep = ix->sl_rep; rsc = ix->sl_rsc; lrep = ix->sl_lrep;
   } else {
     if (which < 1 || which > ix->computed || which <= ix->computed - 3)
       return fail(IDX_ESTATE, "epoch %d is not held (computed %d)", which, ix->computed);
     n_slots = (int64_t)which * ix->Q;
     n_members = (int64_t)which * ix->wpr * c.window;
     const EpochStore& e = ix->ep[which % 3];
-    size = e.size; off = e.off; members = e.members; cent = e.cent; rep = e.rep; rsc = e.rsc;
+    size = e.size; off = e.off; members = e.members; cent = e.cent; rep = e.rep; rsc = e.rsc; lrep = e.lrep;
   }
   buf->n_slots = (int32_t)n_slots;
   buf->n_members = (int32_t)n_members;
@@ -669,6 +726,7 @@ int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
   cp(buf->centroids, cent, (size_t)n_slots * c.dim * 4);
   cp(buf->reps, rep, (size_t)n_slots * ix->RB);
   cp(buf->rep_scale, rsc, (size_t)n_slots * 4);
+  cp(buf->rep_f32, lrep, (size_t)n_slots * c.dim * 4);
   if (e != hipSuccess) return device_error(ix, e, "export copy");
   return IDX_OK;
 }

@@ -241,6 +241,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   for (int idx = tid; idx < CS * D; idx += bd) {
     const float x = cent[idx];
     p.cent[(size_t)slot0 * D + idx] = x;
+    p.lrep[(size_t)slot0 * D + idx] = x;
     if constexpr (DT == DT_E4M3) atomicMax(&amax[idx / D], __float_as_uint(__builtin_fabsf(x)));
   }
   __syncthreads();

@@ -24,8 +24,8 @@ Inverted-File Index, Park & Hwu, arXiv:2611.02508; cited by page and section):
   warm-started refits with Elkan/Hamerly-style bounds, versioned publication.
 
 Modules: codec (stored formats), score (fp64 indexer score), kmeans
-(exact-order fp32 seal/refit arithmetic), index (versions, routing,
-exhaustive baseline), recall.
+(exact-order fp32 seal/refit arithmetic), encoder (learned representatives),
+index (versions, routing, exhaustive baseline), recall.
 """
-from . import codec, score, kmeans, index, recall  # noqa: F401
+from . import codec, score, kmeans, encoder, index, recall  # noqa: F401
 from .index import OracleConfig, OracleIndex, exhaustive_topk, fill_budget  # noqa: F401

@@ -49,6 +49,7 @@ from dataclasses import dataclass, field
 import numpy as np
 
 from . import codec
+from .encoder import encode
 from .kmeans import mean_exact, nearest, seal_blocks, seal_window, sqdist_exact
 from .score import indexer_scores
 
@@ -69,6 +70,7 @@ class OracleConfig:
     seal_iters: int = 10
     refit_every: int = 16384           # 0 = never refit
     positional: bool = False           # clusters = contiguous blocks (no k-means, no refit)
+    encoder: object = None             # learned-representative weights (oracle.encoder), or None
 
     def __post_init__(self):
         if self.positional and self.refit_every:
@@ -107,8 +109,9 @@ class Cluster:
         return self.members.size > 0
 
 
-def make_cluster(slot: int, members: np.ndarray, centroid: np.ndarray, dtype: str) -> Cluster:
-    raw, sc = codec.quantize_rep(centroid, dtype)
+def make_cluster(slot: int, members: np.ndarray, centroid: np.ndarray, dtype: str, rep=None) -> Cluster:
+    """rep: the representative before quantization (default: the centroid)."""
+    raw, sc = codec.quantize_rep(centroid if rep is None else np.asarray(rep, dtype=np.float32), dtype)
     value = codec.decode_codes(raw, dtype).astype(np.float64) * np.float64(sc)
     return Cluster(slot, np.asarray(members, dtype=np.int64), np.asarray(centroid, np.float32).copy(),
                    raw, np.float32(sc), value)
@@ -231,8 +234,15 @@ class OracleIndex:
         clusters = []
         for i in range(cfg.n_clusters):
             members = lo + np.nonzero(assign == i)[0]
-            clusters.append(make_cluster(w * cfg.n_clusters + i, members, C[i], cfg.dtype))
+            clusters.append(make_cluster(w * cfg.n_clusters + i, members, C[i], cfg.dtype,
+                                         self._learned(members, C[i])))
         self.seals.append(clusters)
+
+    def _learned(self, members, centroid):
+        """Learned representative (float32) when an encoder is set, else None (the mean)."""
+        if self.cfg.encoder is None or len(members) == 0:
+            return None
+        return encode(self.X[np.asarray(members, dtype=np.int64)], centroid, self.cfg.encoder).astype(np.float32)
 
     # ---- refit + publish ------------------------------------------------
     def refit_due(self) -> bool:
@@ -272,7 +282,7 @@ class OracleIndex:
                 cent = mean_exact(self.X[members])
             else:
                 cent = c.centroid
-            epoch.append(make_cluster(c.slot, members, cent, cfg.dtype))
+            epoch.append(make_cluster(c.slot, members, cent, cfg.dtype, self._learned(members, cent)))
         self.epochs[r] = epoch
         self.computed = r
         return r

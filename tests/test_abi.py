@@ -98,3 +98,11 @@ def test_exhaustive_rejects_bad_arguments(lib):
 def test_workspace_size(lib):
     assert lib.idx_exhaustive_workspace_bytes(1000, 3) == 3 * 1024 * 4
     assert lib.idx_exhaustive_workspace_bytes(0, 3) == 0
+
+
+def test_encoder_size_matches_the_packed_layout(lib):
+    from oracle.encoder import encoder_floats
+    for d in (32, 64, 128):
+        assert lib.idx_encoder_floats(d) == encoder_floats(d)
+    assert lib.idx_encoder_floats(96) == -1
+    assert lib.idx_set_encoder(None, None, None) == -1
