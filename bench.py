@@ -422,7 +422,61 @@ def ablation(ivf, torch, wl, inp, keys, ks, q, qs, w, dev, budget, k, n_q=512,
         ivf.idx_destroy(ix)
         out[name] = res
         log(f"ablation {name}: {res}")
-    return dict(budget=budget, k=k, queries=n_q, recall_by_prefix=out)
+    return dict(budget=budget, k=k, queries=n_q, recall_by_prefix=out,
+                learned_representatives=learned_ablation(ivf, torch, wl, dev, budget, k, n_q))
+
+
+def learned_ablation(ivf, torch, wl, dev, budget, k, n_q, N=524288, lengths=(65536, 131072, 262144, 524288)):
+    """Mean vs learned representatives (seeded stand-in encoder weights) on the mixture
+    whose components hide members of opposite sign along u_m, with queries along u_m;
+    recall vs exhaustive and index build time (seals + refits with publication)."""
+    import datagen
+    H, d, dt, M = wl["H"], wl["d"], wl["dtype"], 4096
+    kf = datagen.make_adversarial_keys(wl["seed"], N, d, M, a=1.0)
+    keys_np, ks_np = datagen.cast_rows(kf, dt)
+    qf = datagen.make_adversarial_queries(wl["seed"], n_q, H, d, M)
+    if dt == "e4m3":
+        qc, qsv = datagen.cast_rows(qf.reshape(n_q, H * d), dt)
+        q_np, qs_np = qc.reshape(n_q, H, d), np.repeat(qsv[:, None], H, axis=1).astype(np.float32)
+    else:
+        q_np, qs_np = datagen.cast_rows(qf, dt)[0], None
+    w_np = datagen.make_weights(wl["seed"], n_q, H)
+    keys = torch.from_numpy(keys_np).to(dev)
+    ks = torch.from_numpy(ks_np).to(dev) if ks_np is not None else None
+    q = torch.from_numpy(np.ascontiguousarray(q_np)).to(dev)
+    qs = torch.from_numpy(qs_np).to(dev) if qs_np is not None else None
+    w = torch.from_numpy(w_np).to(dev)
+    ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(N, n_q) // 4, dtype=torch.float32, device=dev)
+    exh = {}
+    for L in lengths:
+        e_idx, _ = ivf.idx_exhaustive_topk(keys, ks, dt, H, q, qs, w, L - n_q, k, workspace=ws, n_keys=L)
+        exh[L] = e_idx.cpu().numpy()
+    enc = torch.from_numpy(datagen.encoder_weights(wl["seed"], d, alpha=0.25)).to(dev)
+    out = {}
+    for name, use_enc in (("mean representatives", False), ("learned representatives (seeded weights)", True)):
+        ix = ivf.idx_create(heads=H, dim=d, dtype=dt, max_keys=N, n_sink=wl["n_sink"], window=wl["window"],
+                            cluster_size=wl["cluster_size"], seal_cap=wl["seal_cap"], seal_iters=wl["seal_iters"],
+                            refit_every=wl["refit_every"], max_queries=n_q, max_budget=budget, max_k=k)
+        if use_enc:
+            ivf.idx_set_encoder(ix, enc)
+        res, done, build_s = {}, 0, 0.0
+        for L in lengths:
+            torch.cuda.synchronize()
+            t0 = time.time()
+            while done < L:
+                b = min(L, done + 16384)
+                ivf.idx_build_seal(ix, keys[done:b], None if ks is None else ks[done:b])
+                while ivf.idx_refit(ix):
+                    ivf.idx_publish(ix)
+                done = b
+            torch.cuda.synchronize()
+            build_s += time.time() - t0
+            r_idx, _ = ivf.idx_route_topk(ix, q, qs, w, L - n_q, k, budget)
+            res[str(L)] = summarize(recall_per_query(r_idx.cpu().numpy(), exh[L]))["mean"]
+        ivf.idx_destroy(ix)
+        out[name] = dict(recall_by_prefix=res, build_s=round(build_s, 3))
+        log(f"learned-rep ablation {name}: {out[name]}")
+    return out
 
 
 def cpu_baseline(ix, inp, wl, budget, sample):

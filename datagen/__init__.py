@@ -103,6 +103,24 @@ def make_weights(seed: int, T: int, H: int) -> np.ndarray:
     return (rng.standard_normal((T, H)) / np.sqrt(H)).astype(np.float32)
 
 
+def adversarial_directions(seed: int, M: int, d: int) -> np.ndarray:
+    """u_m: a unit direction orthogonal to each centre mu_m."""
+    rng = _rng(seed, STREAM_ADVERSARIAL + 100)
+    mu = centres(seed, M, d)
+    g = rng.standard_normal((M, d))
+    g -= (g * mu).sum(1, keepdims=True) * mu
+    return g / np.linalg.norm(g, axis=1, keepdims=True)
+
+
+def make_adversarial_queries(seed: int, T: int, H: int, d: int, M: int, noise: float = 0.3) -> np.ndarray:
+    """Queries along the hidden directions: q_{t,h} = u_m + noise for a uniform m."""
+    rng = _rng(seed, STREAM_QUERY + 100)
+    u = adversarial_directions(seed, M, d)
+    m = rng.integers(0, M, size=(T, H))
+    eps = rng.standard_normal((T, H, d))
+    return (u[m] + (noise / np.sqrt(d)) * eps).astype(np.float32)
+
+
 def make_adversarial_keys(seed: int, N: int, d: int, M: int, a: float = 1.0,
                           noise: float = 0.3) -> np.ndarray:
     """Mixture whose components hold members of opposite sign along u_m.
@@ -112,9 +130,7 @@ def make_adversarial_keys(seed: int, N: int, d: int, M: int, a: float = 1.0,
     """
     rng = _rng(seed, STREAM_ADVERSARIAL)
     mu = centres(seed, M, d)
-    g = rng.standard_normal((M, d))
-    g -= (g * mu).sum(1, keepdims=True) * mu
-    u = g / np.linalg.norm(g, axis=1, keepdims=True)
+    u = adversarial_directions(seed, M, d)
     j = np.arange(N)
     z = np.where(rng.random(N) < 0.8, ((j * M) // N + rng.integers(-2, 3, N)) % M,
                  rng.integers(0, M, N))
