@@ -110,6 +110,7 @@ __device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi
 __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
   __shared__ uint64_t buf[ROW_CAP];
   __shared__ int hist[4096];
+  __shared__ Select32Scratch sc32;
   __shared__ int wtmp[16];
   __shared__ int s_cnt, s_digit, s_above, s_in, s_taken;
   const int tid = threadIdx.x, bd = blockDim.x;
@@ -127,6 +128,68 @@ __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
     bitonic_sort_desc(buf, P2);
     write_topk(buf, P2, K, oi, os);
     return;
+  }
+  // ---- sampled threshold: 8192 evenly spaced scores give a key tau that about
+  // min(2k, (k + ROW_CAP) / 2) scores of the row reach; one vectorized pass gathers
+  // every score >= tau.  If at least k and at most ROW_CAP do, their exact order gives
+  // the answer (every score above the k-th, and every tie with it, is among them);
+  // otherwise the digit passes below decide. ----
+  if (K < ROW_CAP) {
+    constexpr int NS = 8192;
+    uint32_t* sk = reinterpret_cast<uint32_t*>(buf);   // [NS] sample keys
+    for (int i = tid; i < NS; i += bd) sk[i] = order_bits(row[((int64_t)i * n) / NS]);
+    if (tid == 0) s_cnt = 0;
+    __syncthreads();
+    const int64_t aim = K + (K < (ROW_CAP - K) / 2 ? K : (ROW_CAP - K) / 2);
+    const int64_t want = (aim * NS + n - 1) / n + 8;
+    const int rank = (int)(want < NS ? want : NS);
+    const uint32_t tau = radix_select32_desc(sk, NS, rank, sc32);
+    __syncthreads();   // the sample is no longer read; buf collects candidates
+    const float4* row4 = reinterpret_cast<const float4*>(row);
+    const int64_t n4 = (n + 3) / 4;
+    const int lane = tid & 63;
+    for (int64_t b4 = 0; b4 < n4; b4 += 4 * bd) {
+      float e[16];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t j4 = b4 + u * bd + tid;
+        const float4 v = j4 < n4 ? row4[j4] : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        e[4 * u] = v.x;
+        e[4 * u + 1] = v.y;
+        e[4 * u + 2] = v.z;
+        e[4 * u + 3] = v.w;
+      }
+      bool any = false;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int64_t j = 4 * (b4 + (u >> 2) * bd + tid) + (u & 3);
+        any |= j < n && order_bits(e[u]) >= tau;
+      }
+      if (__ballot(any) == 0ull) continue;   // uniform: most groups hold no candidate
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int64_t j = 4 * (b4 + (u >> 2) * bd + tid) + (u & 3);
+        const bool take = j < n && order_bits(e[u]) >= tau;
+        const uint64_t m = __ballot(take);
+        if (m == 0ull) continue;
+        int base = 0;
+        if (lane == 0) base = atomicAdd(&s_cnt, __popcll(m));
+        base = __shfl(base, 0);
+        const int at = base + __popcll(m & ((1ull << lane) - 1ull));
+        if (take && at < ROW_CAP) buf[at] = make_comp(e[u], (uint32_t)j);
+      }
+    }
+    __syncthreads();
+    const int cnt = s_cnt;
+    if (cnt >= K && cnt <= ROW_CAP) {
+      const int P2 = next_pow2(cnt);
+      for (int i = cnt + tid; i < P2; i += bd) buf[i] = 0ull;
+      __syncthreads();
+      bitonic_sort_desc(buf, P2);
+      write_topk(buf, P2, K, oi, os);
+      return;
+    }
+    __syncthreads();
   }
   // pass 1: top 12 bits of the order key
   for (int i = tid; i < 4096; i += bd) hist[i] = 0;

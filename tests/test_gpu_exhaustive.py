@@ -105,3 +105,29 @@ def test_exhaustive_exact_ties():
     ridx, rsc = exhaustive_topk(keys.astype(np.float64), q.astype(np.float64), w.astype(np.float64), q_pos0, k)
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)
+
+
+def test_exhaustive_large_k_long_rows():
+    """k close to the in-LDS capacity: the sampled threshold must aim between k and
+    that capacity (or fall back to the digit passes) and stay exact."""
+    _run("bf16_small", q_pos0=12000, T=24, k=4096)
+
+
+def test_exhaustive_all_equal_scores_long_rows():
+    """Zero queries: every score is zero, so any threshold keeps the whole row and
+    the selection must fall back to the digit passes; ties go to the lower position."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    rng = np.random.default_rng(6)
+    N, T, H, d, k = 20000, 6, 4, 32, 700
+    keys = rng.standard_normal((N, d)).astype(np.float32)
+    q = np.zeros((T, H, d), np.float32)
+    w = np.ones((T, H), np.float32)
+    q_pos0 = N - T
+    idx, sc = ivf.idx_exhaustive_topk(to_dev(keys), None, "f32", H, to_dev(q), None, to_dev(w), q_pos0, k)
+    torch.cuda.synchronize()
+    ridx, rsc = exhaustive_topk(keys.astype(np.float64), q.astype(np.float64), w.astype(np.float64), q_pos0, k)
+    assert np.array_equal(ridx, np.tile(np.arange(k), (T, 1)))
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)
