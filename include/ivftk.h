@@ -158,6 +158,18 @@ typedef struct {
   float* rep_scale;      /* [n_slots] (1.0 unless E4M3)                                 */
   float* rep_f32;        /* [n_slots, d]: representative before quantization (the
                             centroid, or the learned representative with an encoder)     */
+  /* Refit statistics and per-key bound state, filled only when `which` is the newest
+   * computed epoch e (its refit is the last one launched; the state is overwritten by
+   * the next refit).  Otherwise the counts are -1 / 0 and the arrays are untouched. */
+  int64_t n_screened;    /* out: keys refit e compared with every warm centroid: its R new
+                            keys plus the older keys whose bounds did not certify them    */
+  int64_t n_brute;       /* out: of those, keys whose screening list overflowed and that
+                            the fixed-order brute force assigned                          */
+  int64_t n_bound_keys;  /* out: keys with bound state, positions [S, S + e*R)            */
+  int32_t* assign;       /* [n_bound_keys]: warm-centroid slot each key was assigned to   */
+  float* ub;             /* [n_bound_keys]: upper bound on the distance to that centroid  */
+  float* lb;             /* [n_bound_keys]: lower bound on the distance to every other
+                            live warm centroid (+inf when there is none)                 */
 } idx_export_buf;
 
 /* Create an index on the current HIP device; *out receives the handle. */

@@ -219,17 +219,24 @@ def idx_exhaustive_topk(keys: torch.Tensor, k_scale, dtype: str, heads: int, q: 
 
 
 def idx_export(ix: Index, which: int) -> dict:
-    """Host copy of one cluster set: which=-1 sealed windows, which=e epoch e."""
+    """Host copy of one cluster set: which=-1 sealed windows, which=e epoch e.  For the
+    newest computed epoch it also holds the refit's counts (n_screened, n_brute) and
+    the per-key bound state (assign, ub, lb for positions S .. S + e*R - 1)."""
     buf = _lib.idx_export_buf()
     _check(lib().idx_export(ix.handle, which, ctypes.byref(buf)))
-    ns, nm, d = buf.n_slots, buf.n_members, ix.cfg["dim"]
+    ns, nm, d, nb = buf.n_slots, buf.n_members, ix.cfg["dim"], buf.n_bound_keys
     out = dict(sizes=np.zeros(ns, np.int32), offsets=np.zeros(ns, np.int32), members=np.zeros(nm, np.int32),
                centroids=np.zeros((ns, d), np.float32),
                reps=np.zeros((ns, d), {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[ix.dtype]),
-               rep_scale=np.zeros(ns, np.float32), rep_f32=np.zeros((ns, d), np.float32))
+               rep_scale=np.zeros(ns, np.float32), rep_f32=np.zeros((ns, d), np.float32),
+               assign=np.zeros(nb, np.int32), ub=np.zeros(nb, np.float32), lb=np.zeros(nb, np.float32))
     for k in out:
         setattr(buf, k, out[k].ctypes.data if out[k].size else None)
     _check(lib().idx_export(ix.handle, which, ctypes.byref(buf)))
+    out["n_screened"], out["n_brute"], out["n_bound_keys"] = int(buf.n_screened), int(buf.n_brute), int(nb)
+    if nb == 0:
+        for k in ("assign", "ub", "lb"):
+            del out[k]
     return out
 
 

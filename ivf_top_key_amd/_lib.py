@@ -34,7 +34,9 @@ class idx_route_debug(ctypes.Structure):
 
 class idx_export_buf(ctypes.Structure):
     _fields_ = [("n_slots", c_i32), ("n_members", c_i32), ("sizes", c_vp), ("offsets", c_vp), ("members", c_vp),
-                ("centroids", c_vp), ("reps", c_vp), ("rep_scale", c_vp), ("rep_f32", c_vp)]
+                ("centroids", c_vp), ("reps", c_vp), ("rep_scale", c_vp), ("rep_f32", c_vp),
+                ("n_screened", c_i64), ("n_brute", c_i64), ("n_bound_keys", c_i64), ("assign", c_vp), ("ub", c_vp),
+                ("lb", c_vp)]
 
 
 # (name, restype, argtypes) of every exported function

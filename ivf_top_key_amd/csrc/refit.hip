@@ -77,6 +77,43 @@ __device__ __forceinline__ void sqdist4(const float (&x)[D], const float* c, flo
   d3 = a3;
 }
 
+// sqdist of key row `row` (scale sk) to c, streaming the row 16 bytes at a time
+// (few registers; the row is in cache): the same values and the same fixed order as
+// load_key_f32 followed by sqdist.
+template <int DT, int D>
+__device__ __forceinline__ float sqdist_row(const uint8_t* row, float sk, const float* c) {
+  constexpr int EPC = 16 / Elem<DT>::bytes;   // elements per 16-byte chunk
+  float acc = 0.0f;
+#pragma unroll 1
+  for (int i0 = 0; i0 < D; i0 += EPC) {
+    const u32x4 raw = *reinterpret_cast<const u32x4*>(row + (size_t)i0 * Elem<DT>::bytes);
+    const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+    float cv[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; e += 4) {
+      const float4 c4 = *reinterpret_cast<const float4*>(c + i0 + e);
+      cv[e] = c4.x;
+      cv[e + 1] = c4.y;
+      cv[e + 2] = c4.z;
+      cv[e + 3] = c4.w;
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) {
+      float v;
+      if constexpr (DT == DT_F32) {
+        v = __uint_as_float(wds[e]);
+      } else if constexpr (DT == DT_BF16) {
+        v = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+      } else {
+        v = e4m3_to_f32((wds[e >> 2] >> (8 * (e & 3))) & 0xFFu) * sk;
+      }
+      const float t = v - cv[e];
+      acc = acc + t * t;
+    }
+  }
+  return acc;
+}
+
 // warm centroid and liveness of slot s
 __device__ __forceinline__ const float* warm_cent(const RefitParams& p, int s, int D) {
   return (s < (p.r - 1) * p.Q) ? p.prev.cent + (size_t)s * D : p.seal.cent + (size_t)s * D;
@@ -249,22 +286,48 @@ __global__ __launch_bounds__(256) void k_refit_prep(RefitParams p) {
 constexpr int SCR_LIST = 8;   // candidate entries per lane (each half-wave sees half the slots)
 
 // Per key (one column of a wave's 32), each lane keeps the smallest approximate
-// distance Amin of its half of the slots and the slots with A <= Amin + 2E; at the
-// end the halves merge, the survivors are evaluated exactly, and the bounds for the
-// next refit are ub = exact best, lb = min(second-best exact survivor, Amin + E)
-// (every other slot has A - E > Amin + E).
+// distance Amin of its half of the slots, the slots with A <= Amin + 2E, and the
+// smallest A of every slot that falls outside that cut (Aout); at the end the halves
+// merge, the survivors are evaluated exactly, and the bounds for the next refit are
+// ub = exact best, lb = min(second-best exact survivor, Aout - E) (every other slot
+// has D >= A - E >= Aout - E).
 template <int DT, int D>
 __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
   using GB = Geo<DT_BF16, D>;
   constexpr int CPR = GB::RB / 16;
-  __shared__ u32x4 ctile[2][32 * CPR];   // hi and lo rows of 32 slots
-  __shared__ float cn[32];
+  constexpr int TCH = 2 * 32 * CPR;   // 16-byte chunks of one tile: hi rows, then lo rows
+  constexpr int CPT = TCH / 256;      // chunks per thread
+  static_assert(TCH % 256 == 0, "a tile must split evenly over the block");
+  // two tile buffers: the loads of tile t+1 are in flight while tile t is contracted
+  __shared__ u32x4 ctile[2][TCH];
+  __shared__ float cn[2][32];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, g = (lane >> 5) & 1;
   const int64_t n_new = p.B_r - p.B_prev;
   const int64_t total = n_new + *p.work_count;
   const int nslots = p.r * p.Q;
   const int ntl = (nslots + 31) / 32;
   const float cmr = __builtin_sqrtf(__uint_as_float(p.tile_cmax[0])) * (1.0f + 1e-6f);
+  auto gload = [&](int tl, u32x4 (&r)[CPT], float& cr) {
+    const int t0 = tl * 32;
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = k * 256 + tid;
+      const int h = c / (32 * CPR), cc = c % (32 * CPR);
+      const int sl = min(t0 + cc / CPR, nslots - 1) + h * nslots;
+      r[k] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.cbf) + (size_t)sl * GB::RB +
+                                             (cc % CPR) * 16);
+    }
+    cr = (tid < 32 && t0 + tid < nslots) ? p.cnrm[t0 + tid] : __builtin_inff();
+  };
+  auto lstore = [&](int b, const u32x4 (&r)[CPT], float cr) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) {
+      const int c = k * 256 + tid;
+      const int h = c / (32 * CPR), cc = c % (32 * CPR);
+      ctile[b][h * 32 * CPR + stage_slot<CPR>(cc / CPR, cc % CPR)] = r[k];
+    }
+    if (tid < 32) cn[b][tid] = cr;
+  };
   for (int64_t base = (int64_t)blockIdx.x * 128; base < total; base += (int64_t)gridDim.x * 128) {
     const int64_t item = base + wave * 32 + col;
     const bool active = item < total;
@@ -298,6 +361,7 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     const float E = (2.5e-4f * nxr * cmr + 6e-5f * sum * sum + 1e-30f) * (1.0f + 1e-5f);
     const float E2 = 2.02f * E;   // the cut Amin + 2E with 1% slack
     float amin = __builtin_inff();
+    float aout = __builtin_inff();   // smallest A among slots that cannot survive the cut
     int ls[SCR_LIST];
     float la[SCR_LIST];
 #pragma unroll
@@ -306,25 +370,22 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
       la[q] = 0.0f;
     }
     bool ovf = false;
+    u32x4 reg[CPT];
+    float creg;
+    gload(0, reg, creg);
+    lstore(0, reg, creg);
+    __syncthreads();
     for (int tl = 0; tl < ntl; ++tl) {
-      const int t0 = tl * 32;
-      __syncthreads();
-      for (int c = tid; c < 2 * 32 * CPR; c += 256) {
-        const int h = c / (32 * CPR), cc = c % (32 * CPR);
-        const int r = cc / CPR, ch = cc % CPR;
-        const int sl = min(t0 + r, nslots - 1) + h * nslots;
-        ctile[h][stage_slot<CPR>(r, ch)] = *reinterpret_cast<const u32x4*>(
-            reinterpret_cast<const uint8_t*>(p.cbf) + (size_t)sl * GB::RB + ch * 16);
-      }
-      if (tid < 32) cn[tid] = t0 + tid < nslots ? p.cnrm[t0 + tid] : __builtin_inff();
-      __syncthreads();
+      const int t0 = tl * 32, b = tl & 1;
+      const bool more = tl + 1 < ntl;
+      if (more) gload(tl + 1, reg, creg);
       v16f acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
 #pragma unroll
       for (int i = 0; i < GB::HW / 4; ++i) {
-        const u32x4 a4 = ctile[0][stage_slot<CPR>(col, g * (CPR / 2) + i)];
-        const u32x4 l4 = ctile[1][stage_slot<CPR>(col, g * (CPR / 2) + i)];
+        const u32x4 a4 = ctile[b][stage_slot<CPR>(col, g * (CPR / 2) + i)];
+        const u32x4 l4 = ctile[b][32 * CPR + stage_slot<CPR>(col, g * (CPR / 2) + i)];
         const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w};
         const uint32_t al[4] = {l4.x, l4.y, l4.z, l4.w};
         mfma_step<DT_BF16>(acc, a, &bx[4 * i]);
@@ -335,7 +396,7 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
       float tmin = __builtin_inff();
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float4 c4 = *reinterpret_cast<const float4*>(cn + 8 * j + 4 * g);
+        const float4 c4 = *reinterpret_cast<const float4*>(&cn[b][8 * j + 4 * g]);
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -353,7 +414,10 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
             bool placed = false;
 #pragma unroll
             for (int q = 0; q < SCR_LIST; ++q) {
-              if (ls[q] >= 0 && la[q] > cut) ls[q] = -1;
+              if (ls[q] >= 0 && la[q] > cut) {
+                aout = __builtin_fminf(aout, la[q]);
+                ls[q] = -1;
+              }
               if (!placed && ls[q] < 0) {
                 ls[q] = t0 + 8 * (v >> 2) + 4 * g + (v & 3);
                 la[q] = A[v];
@@ -361,23 +425,33 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
               }
             }
             ovf = ovf || !placed;
+          } else {
+            aout = __builtin_fminf(aout, A[v]);   // the cut only moves down
           }
         }
+      } else {
+        aout = __builtin_fminf(aout, tmin);
       }
+      if (more) lstore(b ^ 1, reg, creg);
+      __syncthreads();
     }
     // both halves of the wave hold the same key: final cut, then exact distances of
     // this lane's survivors
     amin = __builtin_fminf(amin, __shfl_xor(amin, 32));
     ovf = ovf || __shfl_xor((int)ovf, 32);
     const float cut = amin + E2;
+#pragma unroll
+    for (int q = 0; q < SCR_LIST; ++q)
+      if (ls[q] >= 0 && la[q] > cut) aout = __builtin_fminf(aout, la[q]);
+    aout = __builtin_fminf(aout, __shfl_xor(aout, 32));
     float e1 = __builtin_inff(), e2 = __builtin_inff();
     int s1 = 0x7fffffff;
-    float xv[D];
-    load_key_f32<DT, D>(xv, p, x);
+    const uint8_t* krow = p.keys + (size_t)x * (D * Elem<DT>::bytes);
+    const float ksc = (DT == DT_E4M3) ? p.kscale[x] : 1.0f;
 #pragma unroll
     for (int q = 0; q < SCR_LIST; ++q) {
       if (ls[q] < 0 || la[q] > cut) continue;
-      const float de = sqdist<D>(xv, warm_cent(p, ls[q], D));
+      const float de = sqdist_row<DT, D>(krow, ksc, warm_cent(p, ls[q], D));
       if (de < e1 || (de == e1 && ls[q] < s1)) {
         e2 = e1;
         e1 = de;
@@ -399,7 +473,7 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
       best = ps1;
       b2 = __builtin_fminf(__builtin_fminf(e2, pe2), e1);
     }
-    b2 = __builtin_fminf(b2, amin + 0.99f * E);   // every non-survivor has D > Amin + E
+    b2 = __builtin_fminf(b2, aout - 1.01f * E);   // every non-survivor has D >= A - E >= aout - E
     if (active && g == 0) {
       if (ovf || best == 0x7fffffff) {
         p.ovf[atomicAdd(p.ovf_count, 1)] = (int)x;

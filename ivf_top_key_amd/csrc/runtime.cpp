@@ -727,6 +727,21 @@ int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
   cp(buf->reps, rep, (size_t)n_slots * ix->RB);
   cp(buf->rep_scale, rsc, (size_t)n_slots * 4);
   cp(buf->rep_f32, lrep, (size_t)n_slots * c.dim * 4);
+  buf->n_screened = -1;
+  buf->n_brute = -1;
+  buf->n_bound_keys = 0;
+  if (which >= 1 && which == ix->computed) {
+    int wc = 0, oc = 0;
+    cp(&wc, ix->work_count, 4);
+    cp(&oc, ix->ovf_count, 4);
+    const int64_t nb = (int64_t)which * c.refit_every;
+    buf->n_screened = (int64_t)c.refit_every + wc;
+    buf->n_brute = oc;
+    buf->n_bound_keys = nb;
+    cp(buf->assign, ix->assign + c.n_sink, (size_t)nb * 4);
+    cp(buf->ub, ix->ub + c.n_sink, (size_t)nb * 4);
+    cp(buf->lb, ix->lb + c.n_sink, (size_t)nb * 4);
+  }
   if (e != hipSuccess) return device_error(ix, e, "export copy");
   return IDX_OK;
 }

@@ -16,7 +16,10 @@
 // greedy walk over (D, key, cluster) triples in ascending order, which gives a key
 // to a cluster while the key is free and the cluster holds fewer than `cap` keys.
 // (When nearest assignment respects the cap the walk returns exactly it: every key
-// meets its nearest cluster first and that cluster cannot be full yet.)
+// meets its nearest cluster first and that cluster cannot be full yet.)  The
+// iterations stop early once an assignment repeats: from there on every iteration
+// would reproduce the same members and centroids, so the result equals the one
+// after the full iteration count.
 #include "dispatch.h"
 #include "launch.h"
 #include "params.h"
@@ -58,6 +61,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   }
   __syncthreads();
 
+  int prev_a = tid < W ? -2 : -1;   // this key's assignment in the previous iteration
   for (int it = 0; it < p.iters; ++it) {
     if (p.positional) {
       // ---- position blocks: no distances, the means below are the centroids ----
@@ -175,8 +179,14 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
       }
     }
 
-    // ---- stable member lists: ascending position within each cluster ----
+    // ---- stop at a fixed point: an unchanged assignment gives the same members and
+    // means as the previous iteration, hence the same centroids and again the same
+    // assignment, so the remaining iterations would change nothing ----
     const int a = tid < W ? asg[tid] : -1;
+    if (!__syncthreads_or(a != prev_a)) break;
+    prev_a = a;
+
+    // ---- stable member lists: ascending position within each cluster ----
     int myrank = 0;
 #pragma unroll
     for (int cc = 0; cc < CS; ++cc) {

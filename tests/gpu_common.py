@@ -222,3 +222,45 @@ def check_routed_query(t, d, od, oix, qv, wv, k, budget, dt, stats):
     assert np.all(err <= RTOL[dt] * sig + 1e-30), f"query {t}: candidate score error"
     if err.size:
         stats["max_err"] = max(stats["max_err"], float(np.max(err / np.maximum(sig, 1e-300))))
+
+
+def check_refit_bounds(ivf, gix, wl, keys_f64, sample=None, seed=0):
+    """Bound state of the newest refit epoch e against distances computed here in
+    float64: every key's upper bound covers the distance to its assigned warm
+    centroid, which is the nearest one (up to fp32 near ties), and its lower bound
+    stays below the distance to every other live warm centroid.  The warm set of
+    refit e is epoch e-1's centroids for slots below (e-1)*Q and the seal centroids
+    above.  Returns (keys checked, fraction of the prefix the refit screened)."""
+    info = ivf.idx_get_info(gix)
+    e = info["computed_epoch"]
+    assert e >= 1
+    Q = info["slots_per_epoch"]
+    cur = ivf.idx_export(gix, e)
+    seal = ivf.idx_export(gix, -1)
+    if e >= 2:
+        prev = ivf.idx_export(gix, e - 1)
+        warm = np.concatenate([prev["centroids"][:(e - 1) * Q], seal["centroids"][(e - 1) * Q:e * Q]])
+        alive = np.concatenate([prev["sizes"][:(e - 1) * Q] > 0, seal["sizes"][(e - 1) * Q:e * Q] > 0])
+    else:
+        warm, alive = seal["centroids"][:Q], seal["sizes"][:Q] > 0
+    warm = warm.astype(np.float64)
+    S, nb = wl["n_sink"], cur["n_bound_keys"]
+    assert nb == e * wl["refit_every"]
+    idx = np.arange(nb)
+    if sample is not None and sample < nb:
+        idx = np.sort(np.random.default_rng(seed).choice(nb, sample, replace=False))
+    X = keys_f64[S + idx]
+    D2 = (X * X).sum(1)[:, None] + (warm * warm).sum(1)[None, :] - 2.0 * (X @ warm.T)
+    D = np.sqrt(np.maximum(D2, 0.0))
+    D[:, ~alive] = np.inf
+    a = cur["assign"][idx]
+    assert np.all((a >= 0) & (a < e * Q)) and np.all(alive[a]), "assigned to a dead or missing slot"
+    rows = np.arange(idx.size)
+    own = D[rows, a]
+    assert np.all(own <= D.min(1) * (1 + 1e-6) + 1e-12), "assignment is not the nearest warm centroid"
+    assert np.all(cur["ub"][idx] >= own * (1 - 1e-6)), "upper bound below the distance to the own centroid"
+    D[rows, a] = np.inf
+    other = D.min(1)
+    lb = cur["lb"][idx].astype(np.float64)
+    assert np.all(lb <= other * (1 + 1e-6) + 1e-12), "lower bound above the distance to another centroid"
+    return idx.size, cur["n_screened"] / nb

@@ -80,3 +80,21 @@ def test_seal_with_binding_cap():
         assert max(sizes) == 140
     finally:
         ivf.idx_destroy(gix)
+
+
+@pytest.mark.parametrize("name", ["c1r", "bf16_small", "e4m3_small"])
+def test_refit_bound_state_is_valid(name):
+    """After the last refit every key's Hamerly bounds hold against its warm
+    centroids (the state the next refit prunes with)."""
+    import ivf_top_key_amd as ivf
+    from gpu_common import check_refit_bounds
+    from oracle.index import key_values
+    ensure_built()
+    wl, inp = workload(name)
+    gix = gpu_index(wl, inp)
+    try:
+        kv = key_values(inp["keys"], inp["k_scale"], wl["dtype"])
+        n, frac = check_refit_bounds(ivf, gix, wl, kv)
+        say(f"  ok: {n} keys, last refit screened {frac:.3f} of its prefix")
+    finally:
+        ivf.idx_destroy(gix)

@@ -132,6 +132,9 @@ def _scale_case(name, n_exh, n_route, n_windows, n_slots, n_keys_assign, seed):
             D = sqdist_exact(X[xs], warm_c[alive_ids])
             assert np.array_equal(owner[xs], alive_ids[nearest(D)]), "refit assignment is not the nearest centroid"
             say(f"  epoch {P}: {n_slots} clusters exact means, {n_keys_assign} keys nearest")
+            from gpu_common import check_refit_bounds
+            nchk, frac = check_refit_bounds(ivf, ix, wl, kv, sample=2000, seed=seed)
+            say(f"  bounds of {nchk} sampled keys hold; the last refit screened {frac:.3f} of its prefix")
 
         # routing of sampled queries over the published clusters
         cfg = OracleConfig(heads=wl["H"], dim=wl["d"], dtype=dt, n_sink=S, window=W,
