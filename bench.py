@@ -169,6 +169,11 @@ def main():
     build_s = time.time() - t0
     info = ivf.idx_get_info(ix)
     log(f"index built in {build_s:.2f}s: {info}")
+    screened = None
+    if info["computed_epoch"] >= 1:
+        ex = ivf.idx_export(ix, info["computed_epoch"])
+        screened = dict(keys=ex["n_bound_keys"], screened=ex["n_screened"], brute=ex["n_brute"])
+        del ex
 
     if args.copy_calibration:
         # a plain copy of known size: 1 GiB read + 1 GiB written
@@ -309,7 +314,14 @@ def main():
         hip.h.hipEventRecord(ctypes.c_void_p(d1), ctypes.c_void_p(stream.cuda_stream))
         torch.cuda.synchronize()
         dms = hip.elapsed(d0, d1) / 20
-        dec[str(B)] = dict(ms_per_call=round(dms, 4), queries_per_s=round(B / (dms * 1e-3), 1))
+        devs = [[hip.event() for _ in range(8)] for _ in range(10)]
+        for e in devs:
+            ivf.idx_route_topk_pos(ix, qb, qsb, wb, pos, k, budget, debug={"events": e})
+        torch.cuda.synchronize()
+        dnames = ["rep_score", "route_select", "split_score", "rescore_topk"]
+        dk = {n: round(float(np.mean([hip.elapsed(e[2 * i], e[2 * i + 1]) for e in devs])), 4)
+              for i, n in enumerate(dnames)}
+        dec[str(B)] = dict(ms_per_call=round(dms, 4), queries_per_s=round(B / (dms * 1e-3), 1), kernels_ms=dk)
     extra["decode_batches"] = dec
     log(f"decode batches {dec}")
 
@@ -352,6 +364,7 @@ def main():
             "refits": len(refit_ms),
             "refit_ms_last": round(refit_ms[-1], 3) if refit_ms else None,
             "refit_ms_mean": round(float(np.mean(refit_ms)), 3) if refit_ms else None,
+            "last_refit_keys": screened,
         },
         **extra,
     }

@@ -15,6 +15,7 @@ hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t 
 hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s);
 hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s);
 hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s);
+hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
 hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
 // True if one rescoring block holds cand_cap candidates and k winners.
 bool rescore_fits(int cand_cap, int k);

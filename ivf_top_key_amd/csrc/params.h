@@ -77,6 +77,9 @@ struct RouteParams {
   int64_t item_cap;
   int* ctr;            // [2] next work item, number of work items
   float* sbuf;         // [T, cand_ld] scores of the cluster candidates
+  // Small batches: every candidate was scored into sbuf by blocks that split each
+  // query's list (prescored = 1); the final kernel then only selects.
+  int prescored;
 };
 
 struct ExhParams {

@@ -72,6 +72,11 @@ constexpr size_t LDS_BYTES = 163840;
 
 }  // namespace
 
+// Batches of at most this many queries score their candidates with blocks that split
+// each query's list (the final kernel then only selects); larger batches use one
+// block per query for both.
+constexpr int kSplitQueries = 64;
+
 struct idx_index {
   idx_config cfg{};
   int device = 0;
@@ -246,6 +251,8 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->item_id, ix->item_cap) && ix->alloc(&ix->item_first, ix->item_cap) &&
             ix->alloc(&ix->item_n, ix->item_cap) && ix->alloc(&ix->ctr, 2) &&
             ix->alloc(&ix->sbuf, (int64_t)c.max_queries * ix->cand_cap);
+  else if (ok)
+    ok = ix->alloc(&ix->sbuf, (int64_t)std::min(c.max_queries, kSplitQueries) * ix->cand_cap);
   if (ok && ix->wpr) {
     for (int i = 0; i < 3 && ok; ++i) {
       EpochStore& e = ix->ep[i];
@@ -543,6 +550,7 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   p.item_cap = ix->item_cap;
   p.ctr = ix->ctr;
   p.sbuf = ix->sbuf;
+  p.prescored = (!p.cluster_major && T <= kSplitQueries) ? 1 : 0;
   if (dbg) {
     p.dbg_order = dbg->order;
     p.dbg_take = dbg->order_take;
@@ -572,10 +580,11 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
   if (p.cluster_major && e == hipSuccess) e = launch_pairs_group(p, s);
   mark(3);
+  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
   mark(4);
   if (p.cluster_major && e == hipSuccess) e = launch_cluster_score(p, c.dtype, c.dim, ix->HT, s);
+  if (p.prescored && e == hipSuccess) e = launch_cand_score(p, c.dtype, c.dim, ix->HT, call_cap, s);
   mark(5);
-  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
   mark(6);
   if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
   mark(7);

@@ -395,7 +395,11 @@ __global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
 
 template <int DT, int D, int HT>
 static hipError_t launch_rep_score_t(const RouteParams& p, int max_slots, hipStream_t s) {
-  const int chunk = 1024;
+  // slots per block: 1024 for large batches; small batches split the slots finer so
+  // that about 512 blocks run (at least 64 slots per block)
+  const int64_t groups = (p.T + 3) / 4;
+  int chunk = (int)((max_slots * groups + 511) / 512);
+  chunk = chunk < 64 ? 64 : (chunk > 1024 ? 1024 : ((chunk + 63) / 64) * 64);
   dim3 grid((p.T + 3) / 4, (max_slots + chunk - 1) / chunk);
   hipLaunchKernelGGL((k_rep_score<DT, D, HT>), grid, dim3(256), 0, s, p, chunk);
   return hipGetLastError();
@@ -599,6 +603,60 @@ hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht
 }
 
 // ---------------------------------------------------------------------------
+// split candidate scoring for small batches
+// ---------------------------------------------------------------------------
+// A batch of a few queries leaves most of the chip idle with one block per query,
+// so block (t, b) scores candidates [b*CSB, (b+1)*CSB) of query t into sbuf (the
+// same score tile, hence the same bits) and the final kernel only selects.
+constexpr int CSB = 256;   // candidates per block
+
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256) void k_cand_score(RouteParams p) {
+  using G = Geo<DT, D>;
+  __shared__ float wq_s[HT * 32];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31;
+  const int t = blockIdx.x;
+  const int L = p.cand_len[t];
+  const int i0 = blockIdx.y * CSB;
+  if (i0 >= L) return;
+  const int n = min(CSB, L - i0);
+  const int* cand = p.cand + (size_t)t * p.cand_ld + i0;
+  float* out = p.sbuf + (size_t)t * p.cand_ld + i0;
+  const int nk1 = (int)(p.n_keys - 1);
+  if (wave == 0)
+    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+  QueryFrag<DT, D, HT> f;
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
+  __syncthreads();
+  load_query_wregs<DT, D, HT>(f, wq_s);
+  score_gather<DT, D, HT, 2>(
+      f, wave, 4, (n + 31) >> 5,
+      [&](int blk) -> int {
+        const int i = blk * 32 + col;
+        return cand[i < n ? i : n - 1];
+      },
+      [&](int j, uint32_t* buf, float& scl) {
+        j = j < 0 ? 0 : (j > nk1 ? nk1 : j);
+        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
+        scl = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
+      },
+      [&](int blk, float x) {
+        const int i = blk * 32 + col;
+        if (lane < 32 && i < n) out[i] = x;
+      });
+}
+
+template <int DT, int D, int HT>
+static hipError_t launch_cand_score_t(const RouteParams& p, int cand_cap, hipStream_t s) {
+  hipLaunchKernelGGL((k_cand_score<DT, D, HT>), dim3(p.T, (cand_cap + CSB - 1) / CSB), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s) {
+  IVFTK_DISPATCH(launch_cand_score_t, dtype, dim, ht, p, cand_cap, s);
+}
+
+// ---------------------------------------------------------------------------
 // candidate rescoring + top-k: one block per query
 // ---------------------------------------------------------------------------
 // The candidates' scores go to LDS as 32-bit order keys while the waves gather
@@ -643,19 +701,22 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   const int* cand = p.cand + (size_t)t * p.cand_ld;
   const int K = p.k;
   const int nk1 = (int)(p.n_keys - 1);
-  if (wave == 0)
-    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
   QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-  __syncthreads();
-  load_query_wregs<DT, D, HT>(f, wq_s);
+  if (!p.prescored) {
+    if (wave == 0)
+      load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
+    load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
+    __syncthreads();
+    load_query_wregs<DT, D, HT>(f, wq_s);
+  }
   // the sinks and the open window are scored here, and with cluster-major rescoring
-  // the selected clusters' candidates [base_len, L) were scored into sbuf; otherwise
+  // the selected clusters' candidates [base_len, L) were scored into sbuf; a small
+  // batch has every candidate scored into sbuf already (base_len = 0); otherwise
   // every candidate is gathered and scored here
   const QVer qv = query_version(p, t);
   const int n_sink = (int)(qv.n < p.S ? qv.n : p.S);
   const int base_len =
-      p.cluster_major ? min(L, n_sink + (qv.n > qv.open_lo ? (int)(qv.n - qv.open_lo) : 0)) : L;
+      p.prescored ? 0 : (p.cluster_major ? min(L, n_sink + (qv.n > qv.open_lo ? (int)(qv.n - qv.open_lo) : 0)) : L);
   const int nb = (base_len + 31) >> 5;
   score_gather<DT, D, HT, 3>(
       f, wave, nw, nb,

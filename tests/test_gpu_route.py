@@ -194,3 +194,41 @@ def test_route_rescore_modes_bit_identical(name, over):
         assert np.array_equal(a[3][t, :L].view(np.uint32), b[3][t, :L].view(np.uint32)), f"query {t}: scores differ"
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
     say(f"  {name}: {T} queries, query-major and cluster-major bit-identical")
+
+
+@pytest.mark.parametrize("name", ["c1r", "e4m3_small"])
+def test_route_small_batches_bit_identical(name):
+    """Batches of at most 64 queries score their candidates with blocks that split
+    each list; the outputs must equal those of one large batch bit for bit."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload(name)
+    T, k, budget, q_pos0 = 160, wl["k"], wl["budget"], wl["q_pos0"]
+    q = to_dev(inp["q"][:T])
+    qs = to_dev(inp["q_scale"][:T]) if inp["q_scale"] is not None else None
+    w = to_dev(inp["w"][:T])
+    ix = gpu_index(wl, inp, max_queries=max(T, wl["T"]))
+    try:
+        cap = budget + wl["window"] + 64
+        dbg = ivf.make_route_debug(T, cap, 8, 8)
+        idx, sc = ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, debug=dbg)
+        torch.cuda.synchronize()
+        big = (idx.cpu().numpy(), sc.cpu().numpy(), dbg["cand_scores"].cpu().numpy(), dbg["cand_len"].cpu().numpy())
+        parts = []
+        for a, b in ((0, 64), (64, 65), (65, 100), (100, 160)):
+            d2 = ivf.make_route_debug(b - a, cap, 8, 8)
+            i2, s2 = ivf.idx_route_topk(ix, q[a:b], None if qs is None else qs[a:b], w[a:b], q_pos0 + a, k, budget,
+                                        debug=d2)
+            torch.cuda.synchronize()
+            parts.append((i2.cpu().numpy(), s2.cpu().numpy(), d2["cand_scores"].cpu().numpy(),
+                          d2["cand_len"].cpu().numpy()))
+        small = [np.concatenate([pp[i] for pp in parts]) for i in range(4)]
+        assert np.array_equal(big[3], small[3])
+        for t in range(T):
+            L = int(big[3][t])
+            assert np.array_equal(big[2][t, :L].view(np.uint32), small[2][t, :L].view(np.uint32)), f"query {t}"
+        assert np.array_equal(big[0], small[0]) and np.array_equal(big[1].view(np.uint32), small[1].view(np.uint32))
+        say(f"  {name}: {T} queries as one batch and as batches of 64, 1, 35 and 60: bit-identical")
+    finally:
+        ivf.idx_destroy(ix)
