@@ -616,48 +616,28 @@ __device__ __forceinline__ int stage_slot(int r, int ch) {
   return r * CPR + (ch ^ (key & (CPR - 1)));
 }
 
-// Loads this thread's chunks of stage st (rows clamped to nrows - 1) into reg,
-// and for threads below SR the scale of stage row tid.
-template <class S, int NT, int CPT, class Row>
-__device__ __forceinline__ void stage_gload(u32x4 (&reg)[CPT], float& rsc, int st, int nrows, Row& row) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int c = k * NT + tid;
-    int i = st * S::SR + c / S::CPR;
-    i = i < nrows ? i : nrows - 1;
-    const uint8_t* rp;
-    float sc;
-    row(i, rp, sc);
-    reg[k] = *reinterpret_cast<const u32x4*>(rp + (c % S::CPR) * 16);
-  }
-  if (tid < S::SR) {
-    int i = st * S::SR + tid;
-    i = i < nrows ? i : nrows - 1;
-    const uint8_t* rp;
-    row(i, rp, rsc);
-  }
+// Buffer resource over `bytes` bytes at `base` (raw, no stride): loads at offsets
+// past the end return zeros, which lets the staged loads run without clamping.
+// base and bytes must be the same in every lane; they are read from the first
+// active lane so that the resource lives in scalar registers.
+constexpr int BUF_WORD3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* u = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane(bytes), BUF_WORD3);
 }
 
-template <class S, int NT, int CPT>
-__device__ __forceinline__ void stage_lstore(const u32x4 (&reg)[CPT], float rsc, int b, u32x4* tile, float* tsc) {
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < CPT; ++k) {
-    const int c = k * NT + tid;
-    tile[b * S::CHUNKS + stage_slot<S::CPR>(c / S::CPR, c % S::CPR)] = reg[k];
-  }
-  if (tid < S::SR) tsc[b * S::SR + tid] = rsc;
-}
-
-// Scores rows [0, nrows) (nrows uniform over the block; every thread of the block
-// calls).  NW waves of 64 lanes.  row(i, &ptr, &scale): address of row i's bytes
-// and its scale.  sink(i, x): score of row i for this lane's column (i may be
-// >= nrows; lanes 32..63 repeat lanes 0..31).  tile: 2 * CHUNKS 16-byte vectors of LDS,
-// tsc: 2 * SR floats of LDS.
-template <int DT, int D, int HT, int NW, class Row, class Sink>
-__device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, int nrows, u32x4* tile, float* tsc, Row row,
-                                             Sink sink) {
+// Scores rows [0, nrows) of a dense run: row i at base + i * RB (16-byte aligned),
+// its scale at scale[i] (scale null: 1).  nrows * RB must fit in 31 bits.  Every
+// thread of the block calls, with uniform arguments; NW waves of 64 lanes.
+// sink(i, x): score of row i for this lane's column (i may be >= nrows; lanes
+// 32..63 repeat lanes 0..31).  tile: 2 * CHUNKS 16-byte vectors of LDS, tsc: 2 * SR
+// floats of LDS.  Rows past nrows read as zeros and are never sunk by the callers.
+template <int DT, int D, int HT, int NW, class Sink>
+__device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, const uint8_t* base, const float* scale,
+                                             int nrows, u32x4* tile, float* tsc, Sink sink) {
   using S = Stage<DT, D>;
   using G = Geo<DT, D>;
   constexpr int NT = NW * 64;
@@ -667,14 +647,34 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, int 
   const int tid = threadIdx.x, col = tid & 31, g = (tid >> 5) & 1;
   const int nst = (nrows + S::SR - 1) / S::SR;
   if (nst == 0) return;
+  const __amdgpu_buffer_rsrc_t rrow = buffer_rsrc(base, nrows * S::RB);
+  const __amdgpu_buffer_rsrc_t rscl = buffer_rsrc(scale, scale ? nrows * 4 : 0);
+  // this thread's chunks: byte offset inside a stage, and LDS slot
+  int voff[CPT], lslot[CPT];
+#pragma unroll
+  for (int k = 0; k < CPT; ++k) {
+    const int c = k * NT + tid;
+    voff[k] = (c / S::CPR) * S::RB + (c % S::CPR) * 16;
+    lslot[k] = stage_slot<S::CPR>(c / S::CPR, c % S::CPR);
+  }
   u32x4 reg[CPT];
   float rsc = 1.0f;
-  stage_gload<S, NT, CPT>(reg, rsc, 0, nrows, row);
-  stage_lstore<S, NT, CPT>(reg, rsc, 0, tile, tsc);
+  auto gload = [&](int st) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) reg[k] = __builtin_amdgcn_raw_buffer_load_b128(rrow, voff[k], st * S::SR * S::RB, 0);
+    if (scale && tid < S::SR) rsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rscl, tid * 4, st * S::SR * 4, 0));
+  };
+  auto lstore = [&](int b) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k) tile[b * S::CHUNKS + lslot[k]] = reg[k];
+    if (tid < S::SR) tsc[b * S::SR + tid] = rsc;
+  };
+  gload(0);
+  lstore(0);
   __syncthreads();
   for (int st = 0; st < nst; ++st) {
     const int b = st & 1;
-    if (st + 1 < nst) stage_gload<S, NT, CPT>(reg, rsc, st + 1, nrows, row);
+    if (st + 1 < nst) gload(st + 1);
 #pragma unroll
     for (int tt = 0; tt < S::SR / 32; ++tt) {
       const int r0 = st * S::SR + tt * 32;
@@ -693,7 +693,7 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, int 
         sink(r0 + col, x);
       }
     }
-    if (st + 1 < nst) stage_lstore<S, NT, CPT>(reg, rsc, b ^ 1, tile, tsc);
+    if (st + 1 < nst) lstore(b ^ 1);
     __syncthreads();
   }
 }

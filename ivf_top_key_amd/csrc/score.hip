@@ -41,12 +41,7 @@ __global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
   load_query_wregs<DT, D, HT>(f, wq_s[wave]);
   float* out = p.ws + (size_t)(active ? tl : 0) * p.ld;
   score_staged<DT, D, HT, 4>(
-      f, (int)(j1 - j0), tile, tsc,
-      [&](int i, const uint8_t*& rp, float& sc) {
-        const int64_t j = j0 + i;
-        rp = p.keys + (size_t)j * G::RB;
-        sc = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
-      },
+      f, p.keys + (size_t)j0 * G::RB, DT == DT_E4M3 ? p.kscale + j0 : nullptr, (int)(j1 - j0), tile, tsc,
       [&](int i, float x) {
         const int64_t j = j0 + i;
         if (lane < 32 && j < j_end) out[j] = x;
@@ -352,22 +347,22 @@ __global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
     if (s0 >= s1) return;
     const int own_end = active ? min(v.cvis, s1) : s0;
     const StoreView ep = epoch_store(p, r_all);
-    const int split = v.split;
+    const int split = v.split;   // the same for every query of the epoch
     QueryFrag<DT, D, HT> f;
     load_query<DT, D, HT>(f, p.q + (size_t)tc * p.H * G::RB, p.H);
     load_query_wregs<DT, D, HT>(f, wq_s[wave]);
-    score_staged<DT, D, HT, 4>(
-        f, s1 - s0, tile, tsc,
-        [&](int i, const uint8_t*& rp, float& sc) {
-          const int s = s0 + i;
-          const bool from_epoch = s < split;
-          rp = (from_epoch ? ep.rep : p.seal.rep) + (size_t)s * G::RB;
-          sc = (DT == DT_E4M3) ? (from_epoch ? ep.rsc : p.seal.rsc)[s] : 1.0f;
-        },
-        [&](int i, float x) {
-          const int s = s0 + i;
-          if (lane < 32 && s < own_end) out[s] = x;
-        });
+    // slots below the split are the epoch's, the rest the seal store's: one dense run each
+    auto run = [&](const uint8_t* rep, const float* rsc, int a, int b) {
+      if (a >= b) return;
+      score_staged<DT, D, HT, 4>(
+          f, rep + (size_t)a * G::RB, DT == DT_E4M3 ? rsc + a : nullptr, b - a, tile, tsc,
+          [&](int i, float x) {
+            const int s = a + i;
+            if (lane < 32 && s < own_end) out[s] = x;
+          });
+    };
+    run(ep.rep, ep.rsc, s0, min(s1, split));
+    run(p.seal.rep, p.seal.rsc, max(s0, split), s1);
     return;
   }
   if (!active) return;
