@@ -696,14 +696,12 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   const int* cand = p.cand + (size_t)t * p.cand_ld;
   const int K = p.k;
   const int nk1 = (int)(p.n_keys - 1);
+  if (wave == 0)
+    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
   QueryFrag<DT, D, HT> f;
-  if (!p.prescored) {
-    if (wave == 0)
-      load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
-    load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-    __syncthreads();
-    load_query_wregs<DT, D, HT>(f, wq_s);
-  }
+  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
+  __syncthreads();
+  load_query_wregs<DT, D, HT>(f, wq_s);
   // the sinks and the open window are scored here, and with cluster-major rescoring
   // the selected clusters' candidates [base_len, L) were scored into sbuf; a small
   // batch has every candidate scored into sbuf already (base_len = 0); otherwise
@@ -732,11 +730,23 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
         }
       });
   {
-    const float* sb = p.sbuf + (size_t)t * p.cand_ld;
-    for (int i = base_len + tid; i < L; i += bd) {
-      const float x = sb[i];
-      okey[i] = order_bits(x);
-      if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x;
+    // eight loads in flight per thread before the first store
+    const int tail_end = p.prescored ? 0 : L;   // prescored lists are read below
+    for (int i0 = base_len + tid; i0 < tail_end; i0 += 8 * bd) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * bd;
+        x[u] = i < L ? p.sbuf[(size_t)t * p.cand_ld + i] : 0.0f;
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int i = i0 + u * bd;
+        if (i < L) {
+          okey[i] = order_bits(x[u]);
+          if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x[u];
+        }
+      }
     }
   }
   __syncthreads();
@@ -745,26 +755,56 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   auto ent = [&](int u) { return 4 * ((u >> 2) * bd + tid) + (u & 3); };
   uint32_t kv[PT];
   uint32_t cv[PT];
+  // prescored: the scores come straight from sbuf into registers (no LDS pass);
+  // kv holds the raw float bits until every load has been issued
+  if (p.prescored) {
+    const uint32_t* sb = reinterpret_cast<const uint32_t*>(p.sbuf + (size_t)t * p.cand_ld);
 #pragma unroll
-  for (int u4 = 0; u4 < PT / 4; ++u4) {
-    const int i0 = 4 * (u4 * bd + tid);
-    if (i0 + 3 < L) {
-      const uint4 k4 = *reinterpret_cast<const uint4*>(okey + i0);
-      const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
-      kv[4 * u4 + 0] = k4.x;
-      kv[4 * u4 + 1] = k4.y;
-      kv[4 * u4 + 2] = k4.z;
-      kv[4 * u4 + 3] = k4.w;
-      cv[4 * u4 + 0] = (uint32_t)c4.x;
-      cv[4 * u4 + 1] = (uint32_t)c4.y;
-      cv[4 * u4 + 2] = (uint32_t)c4.z;
-      cv[4 * u4 + 3] = (uint32_t)c4.w;
-    } else {
+    for (int u4 = 0; u4 < PT / 4; ++u4) {
+      const int i0 = 4 * (u4 * bd + tid);
+      if (i0 + 3 < L) {
+        const uint4 x4 = *reinterpret_cast<const uint4*>(sb + i0);
+        const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
+        kv[4 * u4] = x4.x, kv[4 * u4 + 1] = x4.y, kv[4 * u4 + 2] = x4.z, kv[4 * u4 + 3] = x4.w;
+        cv[4 * u4] = (uint32_t)c4.x, cv[4 * u4 + 1] = (uint32_t)c4.y, cv[4 * u4 + 2] = (uint32_t)c4.z,
+        cv[4 * u4 + 3] = (uint32_t)c4.w;
+      } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int i = i0 + e;
-        kv[4 * u4 + e] = i < L ? okey[i] : 0u;
-        cv[4 * u4 + e] = i < L ? (uint32_t)cand[i] : 0u;
+        for (int e = 0; e < 4; ++e) {
+          kv[4 * u4 + e] = i0 + e < L ? sb[i0 + e] : 0u;
+          cv[4 * u4 + e] = i0 + e < L ? (uint32_t)cand[i0 + e] : 0u;
+        }
+      }
+    }
+    float* dbs = p.dbg_cand_scores ? p.dbg_cand_scores + (size_t)t * p.dbg_cand_ld : nullptr;
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int i = ent(u);
+      if (dbs && i < L && i < p.dbg_cand_ld) dbs[i] = __uint_as_float(kv[u]);
+      kv[u] = i < L ? order_bits(__uint_as_float(kv[u])) : 0u;
+    }
+  } else {
+#pragma unroll
+    for (int u4 = 0; u4 < PT / 4; ++u4) {
+      const int i0 = 4 * (u4 * bd + tid);
+      if (i0 + 3 < L) {
+        const uint4 k4 = *reinterpret_cast<const uint4*>(okey + i0);
+        const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
+        kv[4 * u4 + 0] = k4.x;
+        kv[4 * u4 + 1] = k4.y;
+        kv[4 * u4 + 2] = k4.z;
+        kv[4 * u4 + 3] = k4.w;
+        cv[4 * u4 + 0] = (uint32_t)c4.x;
+        cv[4 * u4 + 1] = (uint32_t)c4.y;
+        cv[4 * u4 + 2] = (uint32_t)c4.z;
+        cv[4 * u4 + 3] = (uint32_t)c4.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int i = i0 + e;
+          kv[4 * u4 + e] = i < L ? okey[i] : 0u;
+          cv[4 * u4 + e] = i < L ? (uint32_t)cand[i] : 0u;
+        }
       }
     }
   }
@@ -864,7 +904,12 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
         const int bb = (int)bins((uint32_t)(v >> 32));
         const int lo = offs[bb], hi = offs[bb - 1];
         int rank = 0;
-        for (int j = lo; j < hi; ++j) rank += sel[j] > v;
+        int j = lo;
+        for (; j + 4 <= hi; j += 4) {   // four LDS reads in flight
+          const uint64_t a0 = sel[j], a1 = sel[j + 1], a2 = sel[j + 2], a3 = sel[j + 3];
+          rank += (a0 > v) + (a1 > v) + (a2 > v) + (a3 > v);
+        }
+        for (; j < hi; ++j) rank += sel[j] > v;
         pv[q] = v;
         pp[q] = lo + rank;
       }
