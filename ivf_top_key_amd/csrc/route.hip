@@ -254,18 +254,24 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
     return;
   }
   const float* srep = p.srep + (size_t)t * p.srep_ld;
-  // this thread's slots s = u * bd + tid: score order key and size (0 = dead or not visible)
+  // this thread's slots s = u * bd + tid: score order key and size (0 = dead or not
+  // visible).  The loads are unconditional (slots past the visible ones read the
+  // last visible slot and are masked afterwards) so that all of them are in flight
+  // together.
   uint32_t ks[SF_PT];
   int szs[SF_PT];
+  float scs[SF_PT];
 #pragma unroll
   for (int u = 0; u < SF_PT; ++u) {
-    const int s = u * bd + tid;
-    szs[u] = 0;
-    ks[u] = 0u;
-    if (s < v.cvis) {
-      szs[u] = (s < v.split ? ep.size : p.seal.size)[s];
-      ks[u] = order_bits(srep[s]);
-    }
+    const int s = min(u * bd + tid, v.cvis - 1);
+    szs[u] = (s < v.split ? ep.size : p.seal.size)[s];
+    scs[u] = srep[s];
+  }
+#pragma unroll
+  for (int u = 0; u < SF_PT; ++u) {
+    const bool vis = u * bd + tid < v.cvis;
+    ks[u] = vis ? order_bits(scs[u]) : 0u;
+    szs[u] = vis ? szs[u] : 0;
   }
   for (int i = tid; i < SF_NBIN; i += bd) hist[i] = 0;
   if (tid == 0) {
@@ -349,29 +355,30 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
   __syncthreads();
   const int nsel = s_nsel;
   record_selection(p, v, t, list, pre, base_len, nsel);
-  // fill: one wave per selected cluster copies its first `take` members, two
-  // clusters per step so that their loads are in flight together
-  for (int i0 = wave; i0 < nsel; i0 += 2 * nw) {
-    int start[2], take[2], mo[2];
+  // fill: one wave per selected cluster copies its first `take` members, four
+  // clusters per step; the loads are unconditional (clamped inside the cluster) so
+  // that all of a step's loads are in flight before its stores
+  for (int i0 = wave; i0 < nsel; i0 += 4 * nw) {
+    int start[4], take[4];
+    const int* src[4];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+    for (int h = 0; h < 4; ++h) {
       const int i = i0 + h * nw;
-      start[h] = i < nsel ? pre[i] : 0;
-      take[h] = i < nsel ? min(pre[i + 1], used) - start[h] : 0;
-      mo[h] = i < nsel ? moff[i] : 0;
+      const bool on = i < nsel;
+      start[h] = on ? pre[i] : 0;
+      take[h] = on ? min(pre[i + 1], used) - start[h] : 0;
+      const int mo = on ? moff[i] : ~0;
+      src[h] = mo >= 0 ? ep.members + mo : p.seal.members + ~mo;
     }
-    const int most = max(take[0], take[1]);
+    const int most = max(max(take[0], take[1]), max(take[2], take[3]));
     for (int m0 = 0; m0 < most; m0 += 128) {
-      int val[2][2];
+      int val[4][2];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-          const int m = m0 + r * 64 + lane;
-          if (m < take[h]) val[h][r] = mo[h] >= 0 ? ep.members[mo[h] + m] : p.seal.members[~mo[h] + m];
-        }
+        for (int r = 0; r < 2; ++r) val[h][r] = src[h][max(0, min(m0 + r * 64 + lane, take[h] - 1))];
 #pragma unroll
-      for (int h = 0; h < 2; ++h)
+      for (int h = 0; h < 4; ++h)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int m = m0 + r * 64 + lane;
