@@ -42,16 +42,15 @@ struct Elem<DT_E4M3> { static constexpr int bytes = 1; };
 // stored formats
 // ---------------------------------------------------------------------------
 
-// E4M3 code -> fp32 (exact).  Exponent field 0 is subnormal: m * 2^-9.
+// E4M3 code -> fp32 (exact).  Exponent field 0 is subnormal: m * 2^-9.  Both
+// forms are computed and one selected, so no branch separates the loads of a row.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
   const uint32_t sign = (code & 0x80u) << 24;
   const uint32_t e = (code >> 3) & 0xFu;
   const uint32_t m = code & 7u;
-  if (e == 0) {
-    const float v = (float)m * 0x1p-9f;
-    return __uint_as_float(__float_as_uint(v) | sign);
-  }
-  return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+  const float sub = __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
+  const float nrm = __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+  return e == 0 ? sub : nrm;
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -89,6 +88,32 @@ __device__ __forceinline__ float load_elem(const uint8_t* row, int i) {
     return bf16_to_f32(reinterpret_cast<const uint16_t*>(row)[i]);
   } else {
     return e4m3_to_f32(row[i]);
+  }
+}
+
+// N consecutive elements of a stored row as fp32 times sk (sk = 1 for unscaled
+// formats): 16-byte loads first, then the conversion, so all loads are in flight
+// together.  row must be 16-byte aligned and N * element size a multiple of 16.
+template <int DT, int N>
+__device__ __forceinline__ void load_row_f32(float (&x)[N], const uint8_t* row, float sk) {
+  constexpr int EB = DT == DT_F32 ? 4 : (DT == DT_BF16 ? 2 : 1);
+  constexpr int NV = N * EB / 16;
+  static_assert(N * EB % 16 == 0, "whole 16-byte chunks");
+  uint32_t w[4 * NV];
+#pragma unroll
+  for (int v = 0; v < NV; ++v) {
+    const uint4 q = reinterpret_cast<const uint4*>(row)[v];
+    w[4 * v] = q.x, w[4 * v + 1] = q.y, w[4 * v + 2] = q.z, w[4 * v + 3] = q.w;
+  }
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    if constexpr (DT == DT_F32) {
+      x[i] = __uint_as_float(w[i]);
+    } else if constexpr (DT == DT_BF16) {
+      x[i] = bf16_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
+    } else {
+      x[i] = e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sk;
+    }
   }
 }
 

@@ -34,14 +34,7 @@ constexpr int REFIT_TILE_SLOTS = 64;
 template <int DT, int D>
 __device__ __forceinline__ void load_key_f32(float (&x)[D], const RefitParams& p, int64_t pos) {
   const uint8_t* row = p.keys + (size_t)pos * (D * Elem<DT>::bytes);
-  float sk = 1.0f;
-  if constexpr (DT == DT_E4M3) sk = p.kscale[pos];
-#pragma unroll
-  for (int i = 0; i < D; ++i) {
-    float v = load_elem<DT>(row, i);
-    if constexpr (DT == DT_E4M3) v = v * sk;
-    x[i] = v;
-  }
+  load_row_f32<DT, D>(x, row, DT == DT_E4M3 ? p.kscale[pos] : 1.0f);
 }
 
 template <int D>
@@ -340,14 +333,11 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     float nh = 0.0f;
     {
       const uint8_t* row = p.keys + (size_t)x * (D * Elem<DT>::bytes) + (size_t)g * (D / 2) * Elem<DT>::bytes;
-      const float sk = (DT == DT_E4M3) ? p.kscale[x] : 1.0f;
+      float xh[D / 2];
+      load_row_f32<DT, D / 2>(xh, row, (DT == DT_E4M3) ? p.kscale[x] : 1.0f);
 #pragma unroll
       for (int i = 0; i < GB::HW; ++i) {
-        float a = load_elem<DT>(row, 2 * i), b = load_elem<DT>(row, 2 * i + 1);
-        if constexpr (DT == DT_E4M3) {
-          a = a * sk;
-          b = b * sk;
-        }
+        const float a = xh[2 * i], b = xh[2 * i + 1];
         const uint32_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
         bx[i] = ah | (bh << 16);
         bl[i] = f32_to_bf16(a - __uint_as_float(ah << 16)) | (f32_to_bf16(b - __uint_as_float(bh << 16)) << 16);
