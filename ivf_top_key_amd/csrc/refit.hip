@@ -115,6 +115,27 @@ __device__ __forceinline__ bool warm_alive(const RefitParams& p, int s) {
   return ((s < (p.r - 1) * p.Q) ? p.prev.size : p.seal.size)[s] > 0;
 }
 
+// tile[c * D + i] = row(c)[i] for c < nt (fp32 centroid rows): 16-byte loads, eight
+// per thread issued before any store.  Every thread of the block calls.
+template <int D, class Row>
+__device__ __forceinline__ void load_cent_tile(float* tile, int nt, Row row) {
+  constexpr int VPR = D / 4;   // 16-byte vectors per row
+  const int nv = nt * VPR;
+  for (int v0 = threadIdx.x; v0 < nv; v0 += 8 * blockDim.x) {
+    float4 r[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = min(v0 + u * (int)blockDim.x, nv - 1);
+      r[u] = reinterpret_cast<const float4*>(row(v / VPR))[v % VPR];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int v = v0 + u * (int)blockDim.x;
+      if (v < nv) reinterpret_cast<float4*>(tile)[v] = r[u];
+    }
+  }
+}
+
 __global__ void k_refit_begin(RefitParams p) {
   if (threadIdx.x == 0) {
     *p.work_count = 0;
@@ -145,7 +166,7 @@ __global__ __launch_bounds__(256) void k_refit_old(RefitParams p) {
   for (int t0 = n0; t0 < n1; t0 += REFIT_TILE_SLOTS) {
     const int nt = min(REFIT_TILE_SLOTS, n1 - t0);
     __syncthreads();
-    for (int i = threadIdx.x; i < nt * D; i += blockDim.x) tile[i] = p.seal.cent[(size_t)t0 * D + i];
+    load_cent_tile<D>(tile, nt, [&](int c) { return p.seal.cent + (size_t)(t0 + c) * D; });
     for (int i = threadIdx.x; i < nt; i += blockDim.x) alive[i] = p.seal.size[t0 + i] > 0;
     __syncthreads();
     if (active) {
@@ -205,10 +226,7 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
     for (int t0 = 0; t0 < nslots; t0 += REFIT_TILE_SLOTS) {
       const int nt = min(REFIT_TILE_SLOTS, nslots - t0);
       __syncthreads();
-      for (int i = threadIdx.x; i < nt * D; i += blockDim.x) {
-        const int s = t0 + i / D;
-        tile[i] = warm_cent(p, s, D)[i % D];
-      }
+      load_cent_tile<D>(tile, nt, [&](int c) { return warm_cent(p, t0 + c, D); });
       for (int i = threadIdx.x; i < nt; i += blockDim.x) alive[i] = warm_alive(p, t0 + i);
       __syncthreads();
       if (active) {

@@ -132,7 +132,13 @@ __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
   if (K < ROW_CAP) {
     constexpr int NS = 8192;
     uint32_t* sk = reinterpret_cast<uint32_t*>(buf);   // [NS] sample keys
-    for (int i = tid; i < NS; i += bd) sk[i] = order_bits(row[((int64_t)i * n) / NS]);
+    {
+      float v[NS / 1024];   // the kernel runs 1024 threads: eight samples each, loaded together
+#pragma unroll
+      for (int u = 0; u < NS / 1024; ++u) v[u] = row[((int64_t)(u * 1024 + tid) * n) / NS];
+#pragma unroll
+      for (int u = 0; u < NS / 1024; ++u) sk[u * 1024 + tid] = order_bits(v[u]);
+    }
     if (tid == 0) s_cnt = 0;
     __syncthreads();
     const int64_t aim = K + (K < (ROW_CAP - K) / 2 ? K : (ROW_CAP - K) / 2);
