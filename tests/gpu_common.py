@@ -264,3 +264,49 @@ def check_refit_bounds(ivf, gix, wl, keys_f64, sample=None, seed=0):
     lb = cur["lb"][idx].astype(np.float64)
     assert np.all(lb <= other * (1 + 1e-6) + 1e-12), "lower bound above the distance to another centroid"
     return idx.size, cur["n_screened"] / nb
+
+
+def route_parity(name, budget=None, k=None, T=None, q_pos0=None, list_cap=0, **over):
+    """Route the workload's queries on the GPU (with debug outputs) and check every
+    query against the oracle's routing over the same index (check_routed_query)."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    if T is not None:
+        over["T"] = T
+    if q_pos0 is not None:
+        over["q_pos0"] = q_pos0
+    wl, inp = workload(name, **over)
+    budget = wl["budget"] if budget is None else budget
+    k = wl["k"] if k is None else k
+    T, q_pos0 = wl["T"], wl["q_pos0"]
+    dt = wl["dtype"]
+    say(f"route {name} dtype={dt} T={T} q_pos0={q_pos0} k={k} budget={budget}")
+    gix = gpu_index(wl, inp, max_budget=max(budget, wl["budget"]), max_queries=T, max_k=max(k, wl["k"]))
+    try:
+        oix = oracle_index(wl, inp)
+        q = to_dev(inp["q"][:T])
+        qs = to_dev(inp["q_scale"][:T]) if inp["q_scale"] is not None else None
+        w = to_dev(inp["w"][:T])
+        cfg = oix.cfg
+        cand_cap = max(budget, cfg.n_sink + cfg.window) + 32
+        n_slots = ((q_pos0 + T - cfg.n_sink) // cfg.window) * cfg.n_clusters
+        dbg = ivf.make_route_debug(T, cand_cap, max(n_slots, 1), max(n_slots, 1))
+        dbg["list_cap"] = list_cap
+        idx, sc = ivf.idx_route_topk(gix, q, qs, w, q_pos0, k, budget, debug=dbg)
+        torch.cuda.synchronize()
+        idx, sc = idx.cpu().numpy(), sc.cpu().numpy()
+        d = {kk: v.cpu().numpy() for kk, v in dbg.items() if hasattr(v, "cpu")}
+        d["topk_idx"], d["topk_score"] = idx, sc
+        qraw = inp["q"][:T]
+        qsc = None if inp["q_scale"] is None else inp["q_scale"][:T]
+        ridx, rsc, odbg = oix.route(qraw, qsc, inp["w"][:T], q_pos0, k, budget, debug=True)
+        qv = query_values(qraw, qsc, dt)
+        wv = inp["w"][:T].astype(np.float64)
+        stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
+        for t in range(T):
+            check_routed_query(t, d, odbg[t], oix, qv, wv, k, budget, dt, stats)
+        say(f"  ok {stats}")
+        return stats
+    finally:
+        ivf.idx_destroy(gix)
