@@ -234,16 +234,17 @@ def main():
         # contractions: flops against the MFMA peak of the format
         "rep_score": ("mfma", float(2 * H * d * c_vis.sum())),
         "cluster_score": ("mfma", float(2 * H * d * clus_t.sum())),
-        # cut + fill: read each query's representative scores and cluster sizes, write its list
-        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 4)),
+        # cut + fill: read each query's representative scores and cluster sizes, write its
+        # list (position and gather row of every candidate)
+        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 8)),
     }
     if args.rescore == "cluster":
         # sink / open-window rows gathered and scored, cluster scores and positions read, top-k written
-        work["rescore_topk"] = ("hbm", float(base_t.sum() * (rb + scale_b + 4) + clus_t.sum() * 8
+        work["rescore_topk"] = ("hbm", float(base_t.sum() * (rb + scale_b + 8) + clus_t.sum() * 8
                                              + T * H * (rb + 8) + T * k * 8))
     else:
-        # every candidate's key row (+ scale) and position gathered, query read, top-k written
-        work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b + 4) + T * H * (rb + 8) + T * k * 8))
+        # every candidate's key row (+ scale), gather row and position read, query read, top-k written
+        work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b + 8) + T * H * (rb + 8) + T * k * 8))
         work["cluster_score"] = ("mfma", 0.0)
     rescore_flops = float(2 * H * d * cand_t.sum())
     keys_scored = float((c_vis + cand_t).sum())

@@ -92,7 +92,7 @@ typedef struct {
                             IDX_RESCORE_AUTO, IDX_RESCORE_QUERY or IDX_RESCORE_CLUSTER      */
   int32_t cluster_mode;  /* IDX_CLUSTERS_CONTENT (size-capped k-means seal + refits) or
                             IDX_CLUSTERS_POSITIONAL (position blocks; refit_every must be 0) */
-  int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1)                       */
+  int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1), 1 .. 2^29            */
 } idx_config;
 
 /* Candidate rescoring of idx_route_topk.  Both give bit-identical results.

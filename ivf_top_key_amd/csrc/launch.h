@@ -20,6 +20,9 @@ hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht,
 // True if one rescoring block holds cand_cap candidates and k winners.
 bool rescore_fits(int cand_cap, int k);
 hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, hipStream_t s);
+hipError_t launch_copy_member_rows(const int* members, int64_t j0, int64_t j1, const uint8_t* keys,
+                                   const float* kscale, int64_t n_keys, int rb, uint8_t* ckeys, float* cscale,
+                                   hipStream_t s);
 hipError_t launch_refit(const RefitParams& p, int dtype, int dim, hipStream_t s);
 hipError_t launch_encode(const EncParams& p, int dtype, int dim, hipStream_t s);
 int64_t encoder_floats(int dim);

@@ -11,6 +11,8 @@ namespace ivftk {
 //   members[]    key positions, ascending within a slot
 //   cent[s*d]    fp32 centroid; rep[s*RB] representative in the key format;
 //   rsc[s]       representative scale (E4M3), 1 otherwise
+//   ckeys[j*RB]  the key of members[j] (a copy in member order, so a cluster's keys
+//                are contiguous); cscale[j] its scale (E4M3), null otherwise
 struct StoreView {
   const int* size;
   const int* off;
@@ -18,7 +20,15 @@ struct StoreView {
   const float* cent;
   const uint8_t* rep;
   const float* rsc;
+  const uint8_t* ckeys;
+  const float* cscale;
 };
+
+// Candidate rows for the rescoring gathers: (source << CROW_SHIFT) | row, source 0 =
+// the position-ordered keys (row = position), 1 = the seal store's member-ordered
+// copy, 2 + e = epoch store e's copy (row = index into that store's members).
+constexpr int CROW_SHIFT = 29;
+constexpr int CROW_MASK = (1 << CROW_SHIFT) - 1;
 
 // Everything the routed path needs.  Query t sits at position qpos[t] when qpos is
 // set (a decode batch), at q_pos0 + t otherwise; its
@@ -44,6 +54,7 @@ struct RouteParams {
   float* srep;         // [T, srep_ld] representative scores
   int64_t srep_ld;
   int* cand;           // [T, cand_ld] candidate positions
+  int* cand_row;       // [T, cand_ld] the row each candidate's key is gathered from (CROW_*)
   int64_t cand_ld;
   int* cand_len;       // [T]
   int* redo;           // [T]: 1 when the fast cut kernel left the query to the full one

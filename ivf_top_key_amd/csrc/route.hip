@@ -72,13 +72,18 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   const QV v = qversion(p, t);
   const StoreView ep = p.ep[v.r % 3];
   int* cand = p.cand + (size_t)t * p.cand_ld;
+  int* crow = p.cand_row + (size_t)t * p.cand_ld;
 
-  // sinks [0, min(S, n)) then the open window [open_lo, n)
+  // sinks [0, min(S, n)) then the open window [open_lo, n); their keys are gathered
+  // from the position-ordered keys
   const int n_sink = (int)(v.n < p.S ? v.n : p.S);
   const int n_open = v.n > v.open_lo ? (int)(v.n - v.open_lo) : 0;
   const int base_len = n_sink + n_open;
-  for (int i = tid; i < base_len; i += bd)
-    cand[i] = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+  for (int i = tid; i < base_len; i += bd) {
+    const int pos = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+    cand[i] = pos;
+    crow[i] = pos;
+  }
   if (p.dbg_version && tid == 0) {
     p.dbg_version[4 * t + 0] = v.r;
     p.dbg_version[4 * t + 1] = v.m;
@@ -165,7 +170,9 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
     const int s = (int)comp_id(comp[lo]);
     const bool from_epoch = s < v.split;
     const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
-    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[off + (c - wt[lo])];
+    const int j = off + (c - wt[lo]);
+    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[j];
+    crow[base_len + c] = ((from_epoch ? 2 + v.r % 3 : 1) << CROW_SHIFT) | j;
   }
   if (p.dbg_order) {
     for (int i = tid; i < nsel && i < p.dbg_order_cap; i += bd) {
@@ -232,11 +239,15 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
   const QV v = qversion(p, t);
   const StoreView ep = p.ep[v.r % 3];
   int* cand = p.cand + (size_t)t * p.cand_ld;
+  int* crow = p.cand_row + (size_t)t * p.cand_ld;
   const int n_sink = (int)(v.n < p.S ? v.n : p.S);
   const int n_open = v.n > v.open_lo ? (int)(v.n - v.open_lo) : 0;
   const int base_len = n_sink + n_open;
-  for (int i = tid; i < base_len; i += bd)
-    cand[i] = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+  for (int i = tid; i < base_len; i += bd) {
+    const int pos = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
+    cand[i] = pos;
+    crow[i] = pos;
+  }
   if (p.dbg_version && tid == 0) {
     p.dbg_version[4 * t + 0] = v.r;
     p.dbg_version[4 * t + 1] = v.m;
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
   // clusters per step; the loads are unconditional (clamped inside the cluster) so
   // that all of a step's loads are in flight before its stores
   for (int i0 = wave; i0 < nsel; i0 += 4 * nw) {
-    int start[4], take[4];
+    int start[4], take[4], rtag[4];
     const int* src[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -369,6 +380,8 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
       take[h] = on ? min(pre[i + 1], used) - start[h] : 0;
       const int mo = on ? moff[i] : ~0;
       src[h] = mo >= 0 ? ep.members + mo : p.seal.members + ~mo;
+      // gather row of member m: (store copy << CROW_SHIFT) | (first member index + m)
+      rtag[h] = mo >= 0 ? (((2 + v.r % 3) << CROW_SHIFT) | mo) : ((1 << CROW_SHIFT) | ~mo);
     }
     const int most = max(max(take[0], take[1]), max(take[2], take[3]));
     for (int m0 = 0; m0 < most; m0 += 128) {
@@ -382,7 +395,10 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int m = m0 + r * 64 + lane;
-          if (m < take[h]) cand[base_len + start[h] + m] = val[h][r];
+          if (m < take[h]) {
+            cand[base_len + start[h] + m] = val[h][r];
+            crow[base_len + start[h] + m] = rtag[h] + m;
+          }
         }
     }
   }

@@ -64,6 +64,8 @@ struct EpochStore {
   float* rsc = nullptr;
   float* drift = nullptr;
   float* drift_max = nullptr;
+  uint8_t* ckeys = nullptr;   // [members, RB] keys in member order
+  float* cscale = nullptr;    // [members] their scales (E4M3)
 };
 
 constexpr int TILE = 1024;
@@ -94,6 +96,9 @@ struct idx_index {
   bool has_enc = false;
   uint8_t* sl_rep = nullptr;
   float* sl_rsc = nullptr;
+  uint8_t* sl_ckeys = nullptr;   // [member_cap, RB] sealed keys in member order
+  float* sl_cscale = nullptr;    // [member_cap] their scales (E4M3)
+  int* cand_row = nullptr;       // [max_queries, cand_cap] gather rows of the candidates
   EpochStore ep[3];
   int* assign = nullptr;
   float* ub = nullptr;
@@ -149,11 +154,13 @@ struct idx_index {
     ev_main = ev_refit = nullptr;
   }
 
-  StoreView seal_view() const { return StoreView{sl_size, sl_off, sl_members, sl_cent, sl_rep, sl_rsc}; }
+  StoreView seal_view() const {
+    return StoreView{sl_size, sl_off, sl_members, sl_cent, sl_rep, sl_rsc, sl_ckeys, sl_cscale};
+  }
   StoreView epoch_view(int r) const {
-    if (r <= 0) return StoreView{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
+    if (r <= 0) return StoreView{nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr};
     const EpochStore& e = ep[r % 3];
-    return StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc};
+    return StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc, e.ckeys, e.cscale};
   }
 };
 
@@ -202,7 +209,7 @@ int idx_create(const idx_config* cfg, idx_index** out) {
     return fail(IDX_EINVAL, "cluster_mode must be IDX_CLUSTERS_CONTENT or IDX_CLUSTERS_POSITIONAL");
   if (c.cluster_mode == IDX_CLUSTERS_POSITIONAL && c.refit_every != 0)
     return fail(IDX_EINVAL, "positional blocks are never refitted: refit_every must be 0");
-  if (c.max_keys < 1 || c.max_keys > (int64_t)1 << 30) return fail(IDX_EINVAL, "max_keys must be 1..2^30");
+  if (c.max_keys < 1 || c.max_keys > (int64_t)1 << 29) return fail(IDX_EINVAL, "max_keys must be 1..2^29");
 
   idx_index* ix = new (std::nothrow) idx_index();
   if (!ix) return fail(IDX_ENOMEM, "host allocation failed");
@@ -241,6 +248,9 @@ int idx_create(const idx_config* cfg, idx_index** out) {
             ix->alloc(&ix->sl_lrep, ix->slot_cap * c.dim) && ix->alloc(&ix->enc, encoder_floats(c.dim)) &&
             ix->alloc(&ix->srep, (int64_t)c.max_queries * std::max<int64_t>(ix->slot_cap, 1)) &&
             ix->alloc(&ix->cand, (int64_t)c.max_queries * ix->cand_cap) &&
+            ix->alloc(&ix->cand_row, (int64_t)c.max_queries * ix->cand_cap) &&
+            ix->alloc(&ix->sl_ckeys, ix->member_cap * ix->RB) &&
+            (c.dtype != IDX_E4M3 || ix->alloc(&ix->sl_cscale, ix->member_cap)) &&
             ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries) &&
             ix->alloc(&ix->qpos, c.max_queries);
   if (ok && c.rescore_mode == IDX_RESCORE_CLUSTER)
@@ -258,6 +268,8 @@ int idx_create(const idx_config* cfg, idx_index** out) {
       EpochStore& e = ix->ep[i];
       ok = ix->alloc(&e.size, ix->ep_slot_cap) && ix->alloc(&e.off, ix->ep_slot_cap) &&
            ix->alloc(&e.members, ix->ep_member_cap) && ix->alloc(&e.cent, ix->ep_slot_cap * c.dim) &&
+           ix->alloc(&e.ckeys, ix->ep_member_cap * ix->RB) &&
+           (c.dtype != IDX_E4M3 || ix->alloc(&e.cscale, ix->ep_member_cap)) &&
            ix->alloc(&e.lrep, ix->ep_slot_cap * c.dim) &&
            ix->alloc(&e.rep, ix->ep_slot_cap * ix->RB) && ix->alloc(&e.rsc, ix->ep_slot_cap) &&
            ix->alloc(&e.drift, ix->ep_slot_cap) && ix->alloc(&e.drift_max, 1);
@@ -349,6 +361,9 @@ int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_
     p.rep = ix->sl_rep;
     p.rsc = ix->sl_rsc;
     e = launch_seal(p, c.dtype, c.dim, new_windows, s);
+    if (e == hipSuccess)
+      e = launch_copy_member_rows(ix->sl_members, (int64_t)ix->sealed * c.window, full * (int64_t)c.window, ix->keys,
+                                  ix->kscale, ix->n_keys, ix->RB, ix->sl_ckeys, ix->sl_cscale, s);
     if (e == hipSuccess && ix->has_enc) {
       EncParams ep{};
       ep.keys = ix->keys;
@@ -422,12 +437,15 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   p.tile = TILE;
   p.n_tiles = (int)((p.B_r - p.S + TILE - 1) / TILE);
   e = launch_refit(p, c.dtype, c.dim, side);
+  if (e == hipSuccess)
+    e = launch_copy_member_rows(out.members, 0, p.B_r - p.S, ix->keys, ix->kscale, ix->n_keys, ix->RB, out.ckeys,
+                                out.cscale, side);
   if (e == hipSuccess && ix->has_enc) {
     EncParams ep{};
     ep.keys = ix->keys;
     ep.kscale = ix->kscale;
     ep.n_keys = ix->n_keys;
-    ep.st = StoreView{out.size, out.off, out.members, out.cent, out.rep, out.rsc};
+    ep.st = StoreView{out.size, out.off, out.members, out.cent, out.rep, out.rsc, out.ckeys, out.cscale};
     ep.w = ix->enc;
     ep.lrep = out.lrep;
     ep.rep = out.rep;
@@ -521,12 +539,13 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   p.P = P;
   for (int i = 0; i < 3; ++i) {
     const EpochStore& e = ix->ep[i];
-    p.ep[i] = StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc};
+    p.ep[i] = StoreView{e.size, e.off, e.members, e.cent, e.rep, e.rsc, e.ckeys, e.cscale};
   }
   p.seal = ix->seal_view();
   p.srep = ix->srep;
   p.srep_ld = std::max<int64_t>(ix->slot_cap, 1);
   p.cand = ix->cand;
+  p.cand_row = ix->cand_row;
   p.cand_ld = ix->cand_cap;
   p.cand_len = ix->cand_len;
   p.redo = ix->redo;

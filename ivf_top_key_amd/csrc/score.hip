@@ -604,6 +604,54 @@ hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht
 }
 
 // ---------------------------------------------------------------------------
+// candidate key rows
+// ---------------------------------------------------------------------------
+// The three sources a query's candidate rows come from: the position-ordered keys
+// (sinks and open window), the seal store's member-ordered copy and the query's
+// epoch store's copy (CROW_* in params.h).  Rows are clamped below n_keys, which
+// bounds every source.
+// The per-lane choice of source is arithmetic on byte offsets from the first source
+// (masks, no selects), which keeps the compiler from turning it into a table in
+// scratch memory.
+struct RowSources {
+  const uint8_t* key0;
+  int64_t dk1, dk2;      // key1 - key0, key2 - key0 (bytes)
+  const float* scale0;
+  int64_t ds1, ds2;      // scale1 - scale0, scale2 - scale0 (bytes)
+};
+
+__device__ __forceinline__ RowSources row_sources(const RouteParams& p, int r) {
+  const int e = r % 3;
+  const uint8_t* k2 = e == 0 ? p.ep[0].ckeys : (e == 1 ? p.ep[1].ckeys : p.ep[2].ckeys);
+  const float* s2 = e == 0 ? p.ep[0].cscale : (e == 1 ? p.ep[1].cscale : p.ep[2].cscale);
+  RowSources rs;
+  rs.key0 = p.keys;
+  rs.dk1 = (int64_t)(uintptr_t)p.seal.ckeys - (int64_t)(uintptr_t)p.keys;
+  rs.dk2 = (int64_t)(uintptr_t)k2 - (int64_t)(uintptr_t)p.keys;
+  rs.scale0 = p.kscale;
+  rs.ds1 = (int64_t)(uintptr_t)p.seal.cscale - (int64_t)(uintptr_t)p.kscale;
+  rs.ds2 = (int64_t)(uintptr_t)s2 - (int64_t)(uintptr_t)p.kscale;
+  return rs;
+}
+
+template <int DT, int D>
+__device__ __forceinline__ void load_cand_row(const RowSources& rs, int code, int nk1, uint32_t* buf, float& scl) {
+  const int src = (int)((uint32_t)code >> CROW_SHIFT);
+  int j = code & CROW_MASK;
+  j = j > nk1 ? nk1 : j;
+  const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
+  const uint8_t* kb = rs.key0 + ((rs.dk1 & m1) | (rs.dk2 & m2));
+  load_half_row<DT, D>(buf, kb + (size_t)j * Geo<DT, D>::RB);
+  if constexpr (DT == DT_E4M3) {
+    const float* sb = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(rs.scale0) +
+                                                     ((rs.ds1 & m1) | (rs.ds2 & m2)));
+    scl = sb[j];
+  } else {
+    scl = 1.0f;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // split candidate scoring for small batches
 // ---------------------------------------------------------------------------
 // A batch of a few queries leaves most of the chip idle with one block per query,
@@ -621,9 +669,10 @@ __global__ __launch_bounds__(256) void k_cand_score(RouteParams p) {
   const int i0 = blockIdx.y * CSB;
   if (i0 >= L) return;
   const int n = min(CSB, L - i0);
-  const int* cand = p.cand + (size_t)t * p.cand_ld + i0;
+  const int* crow = p.cand_row + (size_t)t * p.cand_ld + i0;
   float* out = p.sbuf + (size_t)t * p.cand_ld + i0;
   const int nk1 = (int)(p.n_keys - 1);
+  const RowSources rs = row_sources(p, query_version(p, t).r);
   if (wave == 0)
     load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
   QueryFrag<DT, D, HT> f;
@@ -634,13 +683,9 @@ __global__ __launch_bounds__(256) void k_cand_score(RouteParams p) {
       f, wave, 4, (n + 31) >> 5,
       [&](int blk) -> int {
         const int i = blk * 32 + col;
-        return cand[i < n ? i : n - 1];
+        return crow[i < n ? i : n - 1];
       },
-      [&](int j, uint32_t* buf, float& scl) {
-        j = j < 0 ? 0 : (j > nk1 ? nk1 : j);
-        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
-        scl = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
-      },
+      [rs, nk1](int code, uint32_t* buf, float& scl) { load_cand_row<DT, D>(rs, code, nk1, buf, scl); },
       [&](int blk, float x) {
         const int i = blk * 32 + col;
         if (lane < 32 && i < n) out[i] = x;
@@ -717,17 +762,15 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   const int base_len =
       p.prescored ? 0 : (p.cluster_major ? min(L, n_sink + (qv.n > qv.open_lo ? (int)(qv.n - qv.open_lo) : 0)) : L);
   const int nb = (base_len + 31) >> 5;
+  const int* crow = p.cand_row + (size_t)t * p.cand_ld;
+  const RowSources rs = row_sources(p, qv.r);
   score_gather<DT, D, HT, 3>(
       f, wave, nw, nb,
       [&](int blk) -> int {
         const int i = blk * 32 + col;
-        return cand[i < base_len ? i : base_len - 1];
+        return crow[i < base_len ? i : base_len - 1];
       },
-      [&](int j, uint32_t* buf, float& scl) {
-        j = j < 0 ? 0 : (j > nk1 ? nk1 : j);
-        load_half_row<DT, D>(buf, p.keys + (size_t)j * G::RB);
-        scl = (DT == DT_E4M3) ? p.kscale[j] : 1.0f;
-      },
+      [rs, nk1](int code, uint32_t* buf, float& scl) { load_cand_row<DT, D>(rs, code, nk1, buf, scl); },
       [&](int blk, float x) {
         const int i = blk * 32 + col;
         if (lane < 32 && i < base_len) {

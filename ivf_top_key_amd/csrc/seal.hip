@@ -293,4 +293,34 @@ hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, h
   IVFTK_DISPATCH_D(launch_seal_t, dtype, dim, p, n_windows, s);
 }
 
+// ---------------------------------------------------------------------------
+// member-ordered key copies of a store
+// ---------------------------------------------------------------------------
+// ckeys[j] = keys[members[j]] and cscale[j] = kscale[members[j]] for j in [j0, j1):
+// a cluster's keys then sit in one contiguous run (with their scales), which the
+// rescoring gathers read instead of the position-ordered keys.  One thread per
+// 16-byte chunk of a row.
+__global__ __launch_bounds__(256) void k_copy_member_rows(const int* members, int64_t j0, int64_t j1,
+                                                          const uint8_t* keys, const float* kscale, int64_t n_keys,
+                                                          int rb, uint8_t* ckeys, float* cscale) {
+  const int cpr = rb / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t j = j0 + idx / cpr;
+  if (j >= j1) return;
+  const int c = (int)(idx % cpr);
+  const int64_t pos = min(max((int64_t)members[j], (int64_t)0), n_keys - 1);
+  reinterpret_cast<uint4*>(ckeys + (size_t)j * rb)[c] = reinterpret_cast<const uint4*>(keys + (size_t)pos * rb)[c];
+  if (cscale && c == 0) cscale[j] = kscale[pos];
+}
+
+hipError_t launch_copy_member_rows(const int* members, int64_t j0, int64_t j1, const uint8_t* keys,
+                                   const float* kscale, int64_t n_keys, int rb, uint8_t* ckeys, float* cscale,
+                                   hipStream_t s) {
+  if (j1 <= j0) return hipSuccess;
+  const int64_t threads = (j1 - j0) * (rb / 16);
+  hipLaunchKernelGGL(k_copy_member_rows, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, members, j0, j1,
+                     keys, kscale, n_keys, rb, ckeys, cscale);
+  return hipGetLastError();
+}
+
 }  // namespace ivftk
