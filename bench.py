@@ -235,15 +235,16 @@ def main():
         "rep_score": ("mfma", float(2 * H * d * c_vis.sum())),
         "cluster_score": ("mfma", float(2 * H * d * clus_t.sum())),
         # cut + fill: read each query's representative scores and cluster sizes, write its
-        # list (position and gather row of every candidate)
-        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 8)),
+        # list (the gather row of every candidate)
+        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 4)),
     }
     if args.rescore == "cluster":
         # sink / open-window rows gathered and scored, cluster scores and positions read, top-k written
         work["rescore_topk"] = ("hbm", float(base_t.sum() * (rb + scale_b + 8) + clus_t.sum() * 8
                                              + T * H * (rb + 8) + T * k * 8))
     else:
-        # every candidate's key row (+ scale), gather row and position read, query read, top-k written
+        # every candidate's key row (+ scale) and gather row read, its position read from the
+        # member list, query read, top-k written
         work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b + 8) + T * H * (rb + 8) + T * k * 8))
         work["cluster_score"] = ("mfma", 0.0)
     rescore_flops = float(2 * H * d * cand_t.sum())

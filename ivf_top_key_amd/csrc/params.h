@@ -55,6 +55,8 @@ struct RouteParams {
   int64_t srep_ld;
   int* cand;           // [T, cand_ld] candidate positions
   int* cand_row;       // [T, cand_ld] the row each candidate's key is gathered from (CROW_*)
+  int write_cand;      // 1: the cut also writes the candidate positions to cand (debug
+                       // read-back); the rescoring derives positions from cand_row
   int64_t cand_ld;
   int* cand_len;       // [T]
   int* redo;           // [T]: 1 when the fast cut kernel left the query to the full one

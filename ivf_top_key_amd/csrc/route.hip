@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   const int base_len = n_sink + n_open;
   for (int i = tid; i < base_len; i += bd) {
     const int pos = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
-    cand[i] = pos;
+    if (p.write_cand) cand[i] = pos;
     crow[i] = pos;
   }
   if (p.dbg_version && tid == 0) {
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
     const bool from_epoch = s < v.split;
     const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
     const int j = off + (c - wt[lo]);
-    cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[j];
+    if (p.write_cand) cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[j];
     crow[base_len + c] = ((from_epoch ? 2 + v.r % 3 : 1) << CROW_SHIFT) | j;
   }
   if (p.dbg_order) {
@@ -245,7 +245,7 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
   const int base_len = n_sink + n_open;
   for (int i = tid; i < base_len; i += bd) {
     const int pos = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
-    cand[i] = pos;
+    if (p.write_cand) cand[i] = pos;
     crow[i] = pos;
   }
   if (p.dbg_version && tid == 0) {
@@ -385,20 +385,26 @@ __global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p)
     }
     const int most = max(max(take[0], take[1]), max(take[2], take[3]));
     for (int m0 = 0; m0 < most; m0 += 128) {
-      int val[4][2];
+      if (p.write_cand) {   // positions only for the debug read-back
+        int val[4][2];
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+        for (int h = 0; h < 4; ++h)
 #pragma unroll
-        for (int r = 0; r < 2; ++r) val[h][r] = src[h][max(0, min(m0 + r * 64 + lane, take[h] - 1))];
+          for (int r = 0; r < 2; ++r) val[h][r] = src[h][max(0, min(m0 + r * 64 + lane, take[h] - 1))];
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+#pragma unroll
+          for (int r = 0; r < 2; ++r) {
+            const int m = m0 + r * 64 + lane;
+            if (m < take[h]) cand[base_len + start[h] + m] = val[h][r];
+          }
+      }
 #pragma unroll
       for (int h = 0; h < 4; ++h)
 #pragma unroll
         for (int r = 0; r < 2; ++r) {
           const int m = m0 + r * 64 + lane;
-          if (m < take[h]) {
-            cand[base_len + start[h] + m] = val[h][r];
-            crow[base_len + start[h] + m] = rtag[h] + m;
-          }
+          if (m < take[h]) crow[base_len + start[h] + m] = rtag[h] + m;
         }
     }
   }

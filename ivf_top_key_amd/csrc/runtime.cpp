@@ -546,6 +546,7 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   p.srep_ld = std::max<int64_t>(ix->slot_cap, 1);
   p.cand = ix->cand;
   p.cand_row = ix->cand_row;
+  p.write_cand = (dbg && dbg->cand) ? 1 : 0;
   p.cand_ld = ix->cand_cap;
   p.cand_len = ix->cand_len;
   p.redo = ix->redo;

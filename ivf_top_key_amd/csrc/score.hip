@@ -744,7 +744,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
   const int t = blockIdx.x;
   const int L = p.cand_len[t];
-  const int* cand = p.cand + (size_t)t * p.cand_ld;
+  const int* cand = p.cand_row + (size_t)t * p.cand_ld;   // gather rows; positions derived below
   const int K = p.k;
   const int nk1 = (int)(p.n_keys - 1);
   if (wave == 0)
@@ -855,6 +855,31 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
           cv[4 * u4 + e] = i < L ? (uint32_t)cand[i] : 0u;
         }
       }
+    }
+  }
+  {
+    // positions: source 0 rows are positions; a store copy's row j holds that store's
+    // member j.  Every lane loads (source 0 reads a valid dummy word), then selects.
+    const QVer qv2 = query_version(p, t);
+    const int e = qv2.r % 3;
+    const int* mem0 = p.cand_len + t;
+    const int* mem2 = e == 0 ? p.ep[0].members : (e == 1 ? p.ep[1].members : p.ep[2].members);
+    const int64_t d1 = (int64_t)(uintptr_t)p.seal.members - (int64_t)(uintptr_t)mem0;
+    const int64_t d2 = (int64_t)(uintptr_t)mem2 - (int64_t)(uintptr_t)mem0;
+    const int jmax = (int)max((int64_t)0, p.n_keys - 1 - p.S);
+    int mv[PT];
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int src = (int)(cv[u] >> CROW_SHIFT);
+      const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
+      const int* mb = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(mem0) + ((d1 & m1) | (d2 & m2)));
+      const int j = (int)(cv[u] & (uint32_t)CROW_MASK);
+      mv[u] = mb[src == 0 ? 0 : (j < jmax ? j : jmax)];
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int src = (int)(cv[u] >> CROW_SHIFT);
+      cv[u] = src == 0 ? (cv[u] & (uint32_t)CROW_MASK) : (uint32_t)mv[u];
     }
   }
   if (tid == 0) {
