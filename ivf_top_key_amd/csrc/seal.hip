@@ -158,19 +158,24 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
               placed += __popcll(__ballot(win));
               __builtin_amdgcn_wave_barrier();
             } else {
-              int add = 0;
-              if (lane == 0) {
-                for (int q = 0; q < 64 && st + q < ntr; ++q) {
-                  const uint32_t id2 = (uint32_t)sortbuf[st + q];
-                  const int j2 = (int)(id2 / CS), c2 = (int)(id2 % CS);
-                  if (asg[j2] < 0 && cnt[c2] < cap) {
-                    asg[j2] = c2;
-                    cnt[c2] += 1;
-                    ++add;
-                  }
+              // a cluster fills inside this group: decide the 64 triples one by one in
+              // order, with the state in registers (lane cc holds cluster cc's count)
+              const bool free0 = valid && asg[j] < 0;
+              int hv = lane < CS ? cnt[lane] : 0;
+              bool taken = false, win = false;
+              for (int q = 0; q < 64; ++q) {
+                const int jq = __shfl(j, q), cq = __shfl(c, q);
+                const bool fq = __shfl((int)(free0 && !taken), q) != 0;
+                const bool ok = fq && __shfl(hv, cq) < cap;   // uniform across the wave
+                if (ok) {
+                  if (lane == q) win = true;
+                  if (j == jq) taken = true;
+                  if (lane == cq) hv += 1;
                 }
               }
-              placed += __shfl(add, 0);
+              if (win) asg[j] = c;
+              if (lane < CS) cnt[lane] = hv;
+              placed += __popcll(__ballot(win));
               __builtin_amdgcn_wave_barrier();
             }
           }
