@@ -259,7 +259,10 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
 // approximate squared distance A(x,c) = |x|^2 + |c|^2 - 2 <x, c>' where <x, c>' is
 // accumulated in fp32 from split bf16 values, v = v_hi + v_lo + e with v_hi =
 // bf16(v), v_lo = bf16(v - v_hi), |e| <= 2^-16 |v|, as hi.hi + hi.lo + lo.hi (the
-// products are exact).  |A - D| for the fixed-order distance D is at most
+// products are exact).  E4M3 codes and bf16 keys are exact in bf16, so for them the
+// key is not split (x_lo = 0, and the E4M3 key scale multiplies the accumulated
+// dot product, one more rounding and the 2^-24 rounding of each scaled key value,
+// both far inside the bound below).  |A - D| for the fixed-order distance D is at most
 //   E(x) = 2.5e-4 |x| cmax + 6e-5 (|x| + cmax)^2 + 1e-30   (cmax >= every |c|):
 // the split drops lo.lo and e terms (< 3.1 * 2^-16 |x||c| per dot product), the
 // fp32 sums of 3d products add < 384 * 2^-23 * 1.01 |x||c|, both doubled by the
@@ -347,18 +350,25 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     else if (item < total) x = (int64_t)p.work[item - n_new];
     x = min(max(x, (int64_t)p.S), p.B_r - 1);
     // this lane's half of the key as bf16 (B operand), and the squared norm
-    uint32_t bx[GB::HW], bl[GB::HW];   // split bf16 of this lane's half of the key
+    // B operand: this lane's half of the key in bf16.  E4M3 codes and bf16 keys are
+    // exact in bf16 (the E4M3 scale multiplies the dot product afterwards), so one
+    // copy suffices; fp32 keys are split hi + lo.
+    constexpr bool SPLIT_KEY = DT == DT_F32;
+    uint32_t bx[GB::HW], bl[SPLIT_KEY ? GB::HW : 1];
     float nh = 0.0f;
+    const float ksc = (DT == DT_E4M3) ? p.kscale[x] : 1.0f;
     {
       const uint8_t* row = p.keys + (size_t)x * (D * Elem<DT>::bytes) + (size_t)g * (D / 2) * Elem<DT>::bytes;
-      float xh[D / 2];
-      load_row_f32<DT, D / 2>(xh, row, (DT == DT_E4M3) ? p.kscale[x] : 1.0f);
+      float xc[D / 2];   // the stored values (E4M3: codes, unscaled)
+      load_row_f32<DT, D / 2>(xc, row, 1.0f);
 #pragma unroll
       for (int i = 0; i < GB::HW; ++i) {
-        const float a = xh[2 * i], b = xh[2 * i + 1];
-        const uint32_t ah = f32_to_bf16(a), bh = f32_to_bf16(b);
+        const float ca = xc[2 * i], cb = xc[2 * i + 1];
+        const uint32_t ah = f32_to_bf16(ca), bh = f32_to_bf16(cb);
         bx[i] = ah | (bh << 16);
-        bl[i] = f32_to_bf16(a - __uint_as_float(ah << 16)) | (f32_to_bf16(b - __uint_as_float(bh << 16)) << 16);
+        if constexpr (SPLIT_KEY)
+          bl[i] = f32_to_bf16(ca - __uint_as_float(ah << 16)) | (f32_to_bf16(cb - __uint_as_float(bh << 16)) << 16);
+        const float a = DT == DT_E4M3 ? ca * ksc : ca, b = DT == DT_E4M3 ? cb * ksc : cb;
         nh = nh + a * a;
         nh = nh + b * b;
       }
@@ -397,8 +407,12 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
         const uint32_t a[4] = {a4.x, a4.y, a4.z, a4.w};
         const uint32_t al[4] = {l4.x, l4.y, l4.z, l4.w};
         mfma_step<DT_BF16>(acc, a, &bx[4 * i]);
-        mfma_step<DT_BF16>(acc, a, &bl[4 * i]);
+        if constexpr (SPLIT_KEY) mfma_step<DT_BF16>(acc, a, &bl[4 * i]);
         mfma_step<DT_BF16>(acc, al, &bx[4 * i]);
+      }
+      if constexpr (DT == DT_E4M3) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = acc[v] * ksc;
       }
       float A[16];
       float tmin = __builtin_inff();
@@ -455,7 +469,6 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     float e1 = __builtin_inff(), e2 = __builtin_inff();
     int s1 = 0x7fffffff;
     const uint8_t* krow = p.keys + (size_t)x * (D * Elem<DT>::bytes);
-    const float ksc = (DT == DT_E4M3) ? p.kscale[x] : 1.0f;
 #pragma unroll
     for (int q = 0; q < SCR_LIST; ++q) {
       if (ls[q] < 0 || la[q] > cut) continue;
