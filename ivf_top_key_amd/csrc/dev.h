@@ -545,8 +545,10 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
 #pragma unroll
     for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.w[ht][v], relu(acc[ht][v]), p);
   }
-  const float o = __shfl_xor(p, 32);
-  return p + o;
+  // lanes l and l ^ 32 hold the two halves of the head rows of one column: one
+  // cross-half swap gives every lane both (p of lane l & 31 plus p of lane l | 32)
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Score column blocks blk = first, first + step, ... < nblk of one query with a ring
@@ -629,7 +631,7 @@ template <int DT, int D>
 struct Stage {
   static constexpr int RB = Geo<DT, D>::RB;
   static constexpr int CPR = RB / 16;                          // 16-byte chunks per row
-  static constexpr int SR = (8192 / RB) < 32 ? 32 : 8192 / RB;  // rows per stage
+  static constexpr int SR = (16384 / RB) < 32 ? 32 : 16384 / RB;  // rows per stage (16 KB)
   static constexpr int CHUNKS = SR * CPR;                      // chunks per stage
 };
 
