@@ -104,7 +104,10 @@ __device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi
 
 __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
   __shared__ uint64_t buf[ROW_CAP];
-  __shared__ int hist[4096];
+  // the digit histograms share buf's memory: each is read to its last use (the
+  // digit search) before buf collects anything, so two blocks fit on a CU
+  static_assert(4096 * sizeof(int) <= ROW_CAP * sizeof(uint64_t), "histogram must fit in buf");
+  int* const hist = reinterpret_cast<int*>(buf);
   __shared__ Select32Scratch sc32;
   __shared__ int wtmp[16];
   __shared__ int s_cnt, s_digit, s_above, s_in, s_taken;
