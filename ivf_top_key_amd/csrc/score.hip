@@ -768,7 +768,11 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   const int nb = (base_len + 31) >> 5;
   const int* crow = p.cand_row + (size_t)t * p.cand_ld;
   const RowSources rs = row_sources(p, qv.r);
-  score_gather<DT, D, HT, 3>(
+  // rows in flight per wave: two at 32 entries per thread keep the kernel under 168
+  // VGPRs, i.e. three waves per SIMD (more loads in flight per CU than three rows
+  // at two waves); at 64 entries the registers allow only two waves either way
+  constexpr int RING = PT <= 32 ? 2 : 3;
+  score_gather<DT, D, HT, RING>(
       f, wave, nw, nb,
       [&](int blk) -> int {
         const int i = blk * 32 + col;
