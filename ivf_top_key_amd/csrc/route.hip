@@ -222,18 +222,24 @@ __device__ inline void find_bin_desc(const int* hist, int nbins, int need, int* 
   __syncthreads();
 }
 
-constexpr int SF_THREADS = 512;
-constexpr int SF_PT = 16;   // visible slots per thread: SF_THREADS * SF_PT >= the 8192 routed slots
+constexpr int SF_SLOTS = 8192;        // routed slots at most (checked when an index is created)
+constexpr int SF_THREADS = 512;       // threads per query in large batches
+constexpr int SF_SMALL_BATCH = 64;    // batches this small leave most CUs idle: a block of
+constexpr int SF_SMALL_THREADS = 1024;   // 1024 threads per query halves the per-thread chains
 
-__global__ __launch_bounds__(SF_THREADS) void k_route_select_fast(RouteParams p) {
+// NT threads per block; each thread holds SF_SLOTS / NT slots.
+template <int NT>
+__global__ __launch_bounds__(NT) void k_route_select_fast(RouteParams p) {
+  constexpr int SF_PT = SF_SLOTS / NT;
+  static_assert(SF_SLOTS % NT == 0 && NT <= 1024, "block shape");
   __shared__ int hist[SF_NBIN];
   __shared__ uint64_t list[LIST_CAP];
   __shared__ int pre[LIST_CAP + 1];
   __shared__ int moff[LIST_CAP];   // first member index; epoch store if >= 0, else seal store at ~moff
   __shared__ int wtmp[16];
-  __shared__ uint32_t mm_tmp[16];
+  __shared__ uint32_t mm_tmp[2 * NT / 64];
   __shared__ int s_digit, s_cnt, s_nsel;
-  const int tid = threadIdx.x, bd = SF_THREADS;
+  const int tid = threadIdx.x, bd = NT;
   const int wave = tid >> 6, lane = tid & 63, nw = bd >> 6;
   const int t = blockIdx.x;
   const QV v = qversion(p, t);
@@ -496,7 +502,10 @@ hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s) {
 }
 
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s) {
-  hipLaunchKernelGGL(k_route_select_fast, dim3(p.T), dim3(SF_THREADS), 0, s, p);
+  if (p.T <= SF_SMALL_BATCH)
+    hipLaunchKernelGGL(k_route_select_fast<SF_SMALL_THREADS>, dim3(p.T), dim3(SF_SMALL_THREADS), 0, s, p);
+  else
+    hipLaunchKernelGGL(k_route_select_fast<SF_THREADS>, dim3(p.T), dim3(SF_THREADS), 0, s, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
   const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);

@@ -720,8 +720,8 @@ hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, i
 // bin) use an exact radix select.
 constexpr int RS_NBIN = 1024;     // value bins of the top-k histogram
 constexpr int RS_TIE_CAP = 512;   // largest cut bin resolved by a local sort
-constexpr int RS_THREADS = 256;
-constexpr int RS_KPT = 4096 / RS_THREADS;   // winners per thread at the largest k
+constexpr int RS_THREADS = 256;        // scoring + selection blocks
+constexpr int RS_SEL_THREADS = 1024;   // selection-only blocks (candidates scored beforehand)
 
 // LDS bytes of the selection region for a candidate capacity and k (both powers of two).
 __host__ __device__ constexpr size_t rescore_region_bytes(int cap_pow2, int k_pow2) {
@@ -730,13 +730,19 @@ __host__ __device__ constexpr size_t rescore_region_bytes(int cap_pow2, int k_po
              : (size_t)(k_pow2 + RS_TIE_CAP) * 8 + (size_t)RS_NBIN * 8;
 }
 
-template <int DT, int D, int HT, int PT>
-__global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int k_pow2) {
+// NT threads per block.  With NT = RS_SEL_THREADS the block only selects: every
+// candidate was scored into sbuf beforehand (small batches), and the selection's
+// per-thread chains are a quarter as long, which is what a lone query waits on.
+template <int DT, int D, int HT, int PT, int NT>
+__global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) {
   using G = Geo<DT, D>;
+  constexpr bool SELECT_ONLY = NT != RS_THREADS;
+  constexpr int KPT = 4096 / NT;   // winners per thread at the largest k
+  static_assert(RS_NBIN % NT == 0 && NT % 64 == 0 && NT <= 1024, "block shape");
   extern __shared__ uint64_t lds[];
   __shared__ float wq_s[HT * 32];
   __shared__ Select32Scratch sc;
-  __shared__ uint32_t mm_tmp[16];
+  __shared__ uint32_t mm_tmp[2 * NT / 64];
   __shared__ int wtmp[16];
   __shared__ int s_cnt, s_tie, s_bstar;
   uint32_t* okey = reinterpret_cast<uint32_t*>(lds);   // scoring: [L] score keys
@@ -744,13 +750,14 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   uint64_t* tie = lds + k_pow2;                        // [RS_TIE_CAP] cut bin
   int* hist = reinterpret_cast<int*>(lds + k_pow2 + RS_TIE_CAP);   // [RS_NBIN]
   int* offs = hist + RS_NBIN;                                      // [RS_NBIN]
-  const int tid = threadIdx.x, bd = RS_THREADS;
+  const int tid = threadIdx.x, bd = NT;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
   const int t = blockIdx.x;
   const int L = p.cand_len[t];
   const int* cand = p.cand_row + (size_t)t * p.cand_ld;   // gather rows; positions derived below
   const int K = p.k;
   const int nk1 = (int)(p.n_keys - 1);
+  if constexpr (!SELECT_ONLY) {
   if (wave == 0)
     load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
   QueryFrag<DT, D, HT> f;
@@ -807,6 +814,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
     }
   }
   __syncthreads();
+  }   // !SELECT_ONLY
   // this thread's entries: groups of four consecutive list entries, ent(u) below,
   // with their score keys and candidate positions (16-byte loads)
   auto ent = [&](int u) { return 4 * ((u >> 2) * bd + tid) + (u & 3); };
@@ -814,7 +822,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   uint32_t cv[PT];
   // prescored: the scores come straight from sbuf into registers (no LDS pass);
   // kv holds the raw float bits until every load has been issued
-  if (p.prescored) {
+  if (SELECT_ONLY || p.prescored) {
     const uint32_t* sb = reinterpret_cast<const uint32_t*>(p.sbuf + (size_t)t * p.cand_ld);
 #pragma unroll
     for (int u4 = 0; u4 < PT / 4; ++u4) {
@@ -840,7 +848,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
       if (dbs && i < L && i < p.dbg_cand_ld) dbs[i] = __uint_as_float(kv[u]);
       kv[u] = i < L ? order_bits(__uint_as_float(kv[u])) : 0u;
     }
-  } else {
+  } else if constexpr (!SELECT_ONLY) {
 #pragma unroll
     for (int u4 = 0; u4 < PT / 4; ++u4) {
       const int i0 = 4 * (u4 * bd + tid);
@@ -931,7 +939,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
       if (ent(u) < L) atomicAdd(&hist[bins(kv[u])], 1);
     __syncthreads();
     // offs[b] = entries in bins above b (descending order); the bin holding the K-th
-    constexpr int per = RS_NBIN / RS_THREADS;
+    constexpr int per = RS_NBIN / NT;
     int sum = 0;
 #pragma unroll
     for (int q = 0; q < per; ++q) sum += hist[RS_NBIN - 1 - tid * per - q];
@@ -975,10 +983,10 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
     }
     // entries above the cut move to bin start + rank inside the bin (ranks are taken
     // before any entry moves), the cut bin's winners follow them
-    uint64_t pv[RS_KPT];
-    int pp[RS_KPT];
+    uint64_t pv[KPT];
+    int pp[KPT];
 #pragma unroll
-    for (int q = 0; q < RS_KPT; ++q) {
+    for (int q = 0; q < KPT; ++q) {
       const int i = q * bd + tid;
       pp[q] = -1;
       if (i < above) {
@@ -998,7 +1006,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < RS_KPT; ++q)
+    for (int q = 0; q < KPT; ++q)
       if (pp[q] >= 0) sel[pp[q]] = pv[q];
     for (int r = tid; r < K - above; r += bd) sel[above + r] = tie[r];
     __syncthreads();
@@ -1043,13 +1051,13 @@ __global__ __launch_bounds__(RS_THREADS) void k_rescore_topk(RouteParams p, int 
   write_topk(sel, K, K, oi, os);
 }
 
-template <int DT, int D, int HT, int PT>
+template <int DT, int D, int HT, int PT, int NT>
 static hipError_t launch_rescore_pt(const RouteParams& p, int cap_pow2, int k_pow2, hipStream_t s) {
   const size_t lds = rescore_region_bytes(cap_pow2, k_pow2);
-  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT, PT>,
+  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT, PT, NT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT, PT>), dim3(p.T), dim3(RS_THREADS), lds, s, p, k_pow2);
+  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT, PT, NT>), dim3(p.T), dim3(NT), lds, s, p, k_pow2);
   return hipGetLastError();
 }
 
@@ -1057,8 +1065,14 @@ template <int DT, int D, int HT>
 static hipError_t launch_rescore_topk_t(const RouteParams& p, int cand_cap, hipStream_t s) {
   const int cap_pow2 = next_pow2(cand_cap);
   const int k_pow2 = next_pow2(p.k);
-  if (cap_pow2 <= 32 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 32>(p, cap_pow2, k_pow2, s);
-  if (cap_pow2 <= 64 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 64>(p, cap_pow2, k_pow2, s);
+  if (p.prescored) {   // selection only: four times the threads, a quarter of the entries each
+    if (cap_pow2 <= 8 * RS_SEL_THREADS) return launch_rescore_pt<DT, D, HT, 8, RS_SEL_THREADS>(p, cap_pow2, k_pow2, s);
+    if (cap_pow2 <= 16 * RS_SEL_THREADS)
+      return launch_rescore_pt<DT, D, HT, 16, RS_SEL_THREADS>(p, cap_pow2, k_pow2, s);
+    return hipErrorInvalidValue;
+  }
+  if (cap_pow2 <= 32 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 32, RS_THREADS>(p, cap_pow2, k_pow2, s);
+  if (cap_pow2 <= 64 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 64, RS_THREADS>(p, cap_pow2, k_pow2, s);
   return hipErrorInvalidValue;
 }
 
