@@ -73,11 +73,13 @@ def test_route_budget_covering_prefix_is_exhaustive_bit_exact():
         ivf.idx_destroy(gix)
 
 
+@pytest.mark.parametrize("batch", [200, 64])
 @pytest.mark.parametrize("zero_queries", [False, True])
-def test_route_exact_ties(zero_queries):
+def test_route_exact_ties(zero_queries, batch):
     """Integer-valued fp32 keys and queries give exactly equal scores (all zero when
     the queries are zero): GPU and oracle must then agree exactly, ties going to the
-    lower position (the crowded-cut-bin and all-equal paths of the top-k)."""
+    lower position (the crowded-cut-bin and all-equal paths of the top-k).  Batches of
+    64 run the small-batch kernels (split scoring, 1024-thread cut and selection)."""
     import torch
     import ivf_top_key_amd as ivf
     from oracle import OracleConfig, OracleIndex
@@ -96,8 +98,14 @@ def test_route_exact_ties(zero_queries):
         while ivf.idx_refit(gix):
             ivf.idx_publish(gix)
         q_pos0 = N - T
-        idx, sc = ivf.idx_route_topk(gix, to_dev(q), None, to_dev(w), q_pos0, k, budget)
+        qd, wd = to_dev(q), to_dev(w)
+        parts = []
+        for a in range(0, T, batch):
+            b = min(T, a + batch)
+            parts.append(ivf.idx_route_topk(gix, qd[a:b], None, wd[a:b], q_pos0 + a, k, budget))
         torch.cuda.synchronize()
+        idx = torch.cat([pp[0] for pp in parts])
+        sc = torch.cat([pp[1] for pp in parts])
         oix = OracleIndex(OracleConfig(**cfg))
         oix.append(keys)
         while oix.refit_due():
