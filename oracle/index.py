@@ -16,9 +16,10 @@ explainer of AttentionIndex unless noted:
   previous centres, add new centres from recent keys, one round of
   assignment plus update.  Every seal or refit makes a new version; a query
   uses a version only when its own prefix holds every key of that version.
-* kurate.org assessment, "Core Contribution" item 1: windows sealed with
-  size-capped k-means; versioned publication so that no query sees centroids
-  built from future keys.
+* kurate.org assessment, "Core Contribution" item 1: windows are sealed with
+  size-capped k-means, and seals and refits are published as versions; a query
+  may use a version only if every key it was built from lies in the query's
+  prefix.
 
 Readings where the pages are silent (each is a constructor argument or stated
 here):
