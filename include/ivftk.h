@@ -37,7 +37,8 @@
  *     "host" pointers are ordinary CPU memory.  Every array is dense and row-major.
  *   - Streams are hipStream_t passed as void* (NULL = the default stream).  Calls
  *     validate on the host, enqueue work on the given stream(s) and return without
- *     waiting, except idx_export and idx_destroy, which wait.
+ *     waiting, except idx_create, idx_destroy, idx_export, idx_export_version and
+ *     idx_import_version, which wait.
  *   - Caller-owned inputs must stay valid until the stream has passed the enqueued
  *     work; caller-owned outputs are written by that work.
  *   - An index handle is used from one host thread at a time, with one main stream
@@ -92,7 +93,10 @@ typedef struct {
                             IDX_RESCORE_AUTO, IDX_RESCORE_QUERY or IDX_RESCORE_CLUSTER      */
   int32_t cluster_mode;  /* IDX_CLUSTERS_CONTENT (size-capped k-means seal + refits) or
                             IDX_CLUSTERS_POSITIONAL (position blocks; refit_every must be 0) */
-  int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1), 1 .. 2^29            */
+  int64_t max_keys;      /* capacity in keys (positions 0 .. max_keys-1), 1 .. 2^29; also at most
+                            8192 clusters may ever be routed: (max_keys - S) / W sealed windows
+                            times W / cluster_size clusters each must be <= 8192 (at W = 1024
+                            and cluster_size = 128: max_keys < S + 1025 * 1024), else ECAPACITY */
 } idx_config;
 
 /* Candidate rescoring of idx_route_topk.  Both give bit-identical results.
@@ -172,8 +176,30 @@ typedef struct {
                             live warm centroid (+inf when there is none)                 */
 } idx_export_buf;
 
-/* Create an index on the current HIP device; *out receives the handle. */
-int idx_create(const idx_config* cfg, idx_index** out);
+/* Host buffers for idx_import_version: a cluster set built by the caller (a test
+ * fixture, or an epoch saved with idx_export_version to rebuild an index).  All
+ * pointers are host memory, read during the call only. */
+typedef struct {
+  int32_t n_slots;          /* slots of the set: e * slots_per_epoch for the imported epoch e    */
+  const int32_t* sizes;     /* [n_slots]: members per slot (0 = empty slot, never routed)       */
+  const int32_t* members;   /* [sum of sizes]: key positions slot by slot in slot order,
+                               strictly ascending within a slot                                 */
+  const float* centroids;   /* [n_slots, d] fp32: the centres the next refit starts from         */
+  const void* reps;         /* [n_slots, d] representatives in the key format (what is scored)  */
+  const float* rep_scale;   /* [n_slots] fp32 scales, finite and > 0 (E4M3); NULL otherwise     */
+  const float* rep_f32;     /* [n_slots, d] representative before quantization, or NULL
+                               (= centroids); only read back by the exports                    */
+} idx_import_buf;
+
+/* Create an index on the current HIP device; *out receives the handle.  Every
+ * device allocation of the index happens here (W, the clusters per seal and R are
+ * the maintenance parameters of the paper-daily explainer, "索引怎么边算边建？"
+ * items 2 and 3); the memory is zero-filled on `stream`, and the call returns once
+ * that work is done.
+ * Errors: EINVAL / ENOTIMPL for the config fields above, ECAPACITY for the cluster
+ * ceiling at max_keys or budgets too large for one rescoring block, ENOMEM when a
+ * device allocation fails, EDEVICE when the fill fails. */
+int idx_create(const idx_config* cfg, void* stream, idx_index** out);
 
 /* Wait for all work of the device, free everything.  NULL is accepted. */
 int idx_destroy(idx_index* ix);
@@ -184,6 +210,10 @@ const char* idx_last_error(void);
 int idx_get_info(const idx_index* ix, idx_info* out);
 
 /* Insert n keys at positions [n_keys, n_keys + n) and seal every window that fills.
+ * Insert and seal are items 1 and 2 of the paper-daily explainer, "索引怎么边算边建？"
+ * (a new key is searchable at once through the open window; every W keys are
+ * grouped and appended, older clusters untouched); the seal's size-capped k-means
+ * is from the kurate.org assessment, "Core Contribution" item 1.
  *   keys:    device [n, d] in the index dtype; copied, free once the stream passes.
  *   k_scale: device [n] fp32 (> 0) for E4M3, NULL otherwise.
  * Each sealed window runs `seal_iters` Lloyd iterations with the size-capped greedy
@@ -192,8 +222,11 @@ int idx_get_info(const idx_index* ix, idx_info* out);
  * Errors: EINVAL (pointers, n < 0), ECAPACITY (n_keys + n > max_keys). */
 int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_t n, void* stream);
 
-/* Launch the next refit if one is due: sealed windows >= (e+1)*R/W for the next
- * epoch e+1, and the previous epoch has been published.  Refit e+1 covers keys
+/* Launch the next refit if one is due (paper-daily explainer, "索引怎么边算边建？"
+ * item 3 and the paragraph after it: every R tokens the whole prefix is regrouped,
+ * warm-started, with per-key distance bounds, one round, on another stream; kurate.org
+ * assessment, "Core Contribution" item 1).  Due means: sealed windows >= (e+1)*R/W
+ * for the next epoch e+1, and the previous epoch has been published.  Refit e+1 covers keys
  * [S, S + (e+1)*R): it starts from the centroids of slots [0, (e+1)*Q) (epoch e plus
  * the newer seal clusters), assigns every covered key to its nearest centroid (ties
  * to the lower slot; Hamerly-style bounds skip keys whose cluster is certified), and
@@ -203,9 +236,21 @@ int idx_build_seal(idx_index* ix, const void* keys, const float* k_scale, int64_
 int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched);
 
 /* Make the launched refit visible: `stream` waits for it; later routes may use the
- * new epoch for queries whose prefix holds all of its keys.  published: host out,
- * the newest visible epoch (may be NULL). */
+ * new epoch for queries whose prefix holds all of its keys (the versioning rule of
+ * the paper-daily explainer, "索引怎么边算边建？", last paragraph).  published: host
+ * out, the newest visible epoch (may be NULL).  A launched refit that is never
+ * published is never seen by any query.
+ * Errors: ESTATE (poisoned handle). */
 int idx_publish(idx_index* ix, void* stream, int32_t* published);
+
+/* Abandon a launched, unpublished refit: it never becomes visible, routes keep
+ * using the published epoch, and the next idx_refit computes the same epoch again.
+ * `stream` is ordered after the abandoned work (it may still be running on the side
+ * stream when this returns).  This is the failure path of a refit whose result must
+ * not be used (a caller that detects a fault on its side stream, or a test hook).
+ * abandoned: host out, the epoch given up (0 if no refit was in flight; may be NULL).
+ * Errors: ESTATE (poisoned handle), EDEVICE. */
+int idx_abandon_refit(idx_index* ix, void* stream, int32_t* abandoned);
 
 /* Learned representatives (paper-daily explainer, "代表向量为什么要学？"): clusters
  * keep their distance-based members and centroid, and the representative that
@@ -219,7 +264,12 @@ int idx_publish(idx_index* ix, void* stream, int32_t* published);
 int64_t idx_encoder_floats(int32_t dim);   /* -1 for an unsupported dim */
 int idx_set_encoder(idx_index* ix, const float* weights, void* stream);
 
-/* Routed top-k for T queries at positions q_pos0 .. q_pos0 + T - 1.
+/* Routed top-k for T queries at positions q_pos0 .. q_pos0 + T - 1 (paper-daily
+ * explainer, "查询时怎么挑候选？": score each cluster representative with the
+ * indexer formula, rank high to low, fill the budget with the first keys and the
+ * not-yet-grouped keys, then all members of clusters in rank order, truncating the
+ * last, score the candidates exactly and keep the top k; the version of each query
+ * follows "索引怎么边算边建？", last paragraph).
  *   q:       device [T, H, d] in the index dtype.
  *   q_scale: device [T, H] fp32 (> 0) for E4M3, NULL otherwise.
  *   w:       device [T, H] fp32 head weights (any sign).
@@ -251,7 +301,10 @@ int idx_route_topk_pos(idx_index* ix, const void* q, const float* q_scale, const
                        const int64_t* positions, int32_t T, int32_t k, int32_t budget, int32_t* topk_idx,
                        float* topk_score, const idx_route_debug* dbg, void* stream);
 
-/* Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass. */
+/* Exhaustive selection, the method's baseline and the reference answer for recall
+ * (paper-daily explainer, "它到底在解决什么问题？": the indexer scores every earlier
+ * key and keeps the top k).
+ * Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass. */
 int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T);
 
 /* Exhaustive top-k (stateless): query t at position q_pos0 + t scores keys
@@ -266,13 +319,44 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
                         int32_t T, int32_t k, int32_t* topk_idx, float* topk_score, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
-/* Copy one cluster set to host memory (waits for the index's streams).
+/* Copy one cluster store to host memory (waits for the device).
  *   which = -1: every sealed window's clusters (slots [0, m*C)), members grouped
  *               per window in slot order;
  *   which = e >= 1: refit epoch e (must be one of the last three computed), slots
  *               [0, e*Q).
- * Call once with NULL arrays to read n_slots / n_members, then with buffers. */
+ * Call once with NULL arrays to read n_slots / n_members, then with buffers.
+ * Errors: EINVAL (null buf), ESTATE (epoch not held), EDEVICE. */
 int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf);
+
+/* Copy the version a query whose prefix holds `prefix_len` keys routes over (the
+ * versioning rule of the paper-daily explainer, "索引怎么边算边建？", last
+ * paragraph) to host memory: the clusters of slots [0, m*C), where m sealed
+ * windows lie inside the prefix; slots below e*Q come from its epoch e (the newest
+ * published epoch whose keys all lie in the prefix), the others from the seal
+ * store.  Members are slot by slot; offsets index into `members`.  The refit fields
+ * of buf are not filled (counts -1 / 0).  Waits for the device.
+ *   epoch, windows: host out (may be NULL): e and m.
+ * Call once with NULL arrays to read n_slots / n_members, then with buffers.
+ * Errors: EINVAL (null buf, prefix_len < 1), ECAUSAL (prefix_len > inserted keys),
+ * ESTATE (its epoch is no longer held), EDEVICE. */
+int idx_export_version(idx_index* ix, int64_t prefix_len, int32_t* epoch, int32_t* windows, idx_export_buf* buf);
+
+/* Install a caller-built cluster set as the next refit epoch e = computed + 1 in
+ * place of running that refit, for test fixtures (hand-computed indexes) and to
+ * restore an exported epoch.  prefix_len must be e's boundary S + e*R; the keys
+ * below it must be inserted and sealed, and no refit may be in flight.  The set
+ * must hold e*Q slots whose members cover every key of [S, prefix_len) exactly
+ * once.  Representatives are used as given (no encoder runs).  The epoch is then
+ * like a computed one: idx_publish makes it visible, and the next refit starts
+ * from its centroids and compares every key with every centre (the imported set
+ * carries no distance bounds).  The data is copied before the call returns; the
+ * member-ordered key copy is built on `stream`.
+ * Errors: EINVAL (shape, order, duplicate or missing member, bad scale or code,
+ * prefix_len not the boundary, refit_every = 0), ECAUSAL (a member at or beyond
+ * prefix_len, which would let a query see a key outside its prefix; or prefix_len
+ * beyond the inserted keys), ESTATE (a refit in flight, keys not sealed yet),
+ * EDEVICE. */
+int idx_import_version(idx_index* ix, int64_t prefix_len, const idx_import_buf* buf, void* stream);
 
 #ifdef __cplusplus
 }

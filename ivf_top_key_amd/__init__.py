@@ -19,6 +19,7 @@ RESCORE = {"auto": 0, "query": 1, "cluster": 2}
 CLUSTERS = {"content": 0, "positional": 1}
 DTYPES = {"f32": 0, "bf16": 1, "e4m3": 2}
 ELEM_BYTES = {"f32": 4, "bf16": 2, "e4m3": 1}
+_HOST_DTYPE = {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}
 IDX_OK, IDX_EINVAL, IDX_ENOMEM, IDX_EDEVICE, IDX_ECAUSAL, IDX_ESTATE, IDX_ECAPACITY, IDX_ENOTIMPL = \
     0, -1, -2, -3, -4, -5, -6, -7
 
@@ -77,7 +78,7 @@ class Index:
 def idx_create(heads: int, dim: int, dtype: str, max_keys: int, n_sink: int = 4, window: int = 1024,
                cluster_size: int = 128, seal_cap: int = 256, seal_iters: int = 10, refit_every: int = 16384,
                max_queries: int = 4096, max_budget: int = 8192, max_k: int = 2048,
-               rescore: str = "auto", clusters: str = "content") -> Index:
+               rescore: str = "auto", clusters: str = "content", stream=None) -> Index:
     cfg = dict(heads=heads, dim=dim, dtype=dtype, n_sink=n_sink, window=window, cluster_size=cluster_size,
                seal_cap=seal_cap, seal_iters=seal_iters, refit_every=refit_every, max_queries=max_queries,
                max_budget=max_budget, max_k=max_k, rescore=rescore, clusters=clusters, max_keys=max_keys)
@@ -85,7 +86,7 @@ def idx_create(heads: int, dim: int, dtype: str, max_keys: int, n_sink: int = 4,
                         refit_every, max_queries, max_budget, max_k, RESCORE[rescore], CLUSTERS[clusters],
                         max_keys)
     h = ctypes.c_void_p()
-    _check(lib().idx_create(ctypes.byref(c), ctypes.byref(h)))
+    _check(lib().idx_create(ctypes.byref(c), _stream(stream), ctypes.byref(h)))
     return Index(h, cfg)
 
 
@@ -119,6 +120,13 @@ def idx_publish(ix: Index, stream=None) -> int:
     pub = ctypes.c_int32(0)
     _check(lib().idx_publish(ix.handle, _stream(stream), ctypes.byref(pub)))
     return pub.value
+
+
+def idx_abandon_refit(ix: Index, stream=None) -> int:
+    """Give up the launched, unpublished refit; returns its epoch (0 if none)."""
+    ab = ctypes.c_int32(0)
+    _check(lib().idx_abandon_refit(ix.handle, _stream(stream), ctypes.byref(ab)))
+    return ab.value
 
 
 def make_route_debug(T: int, cand_cap: int, order_cap: int, rep_cap: int, device="cuda") -> dict:
@@ -173,18 +181,7 @@ def idx_route_topk(ix: Index, q: torch.Tensor, q_scale, w: torch.Tensor, q_pos0:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=q.device)
     if topk_score is None:
         topk_score = torch.empty((T, k), dtype=torch.float32, device=q.device)
-    dbg = None
-    if debug is not None:
-        ev = debug.get("events")
-        if ev is not None:
-            ev = ctypes.cast((ctypes.c_void_p * len(ev))(*ev), ctypes.POINTER(ctypes.c_void_p))
-        dbg = _lib.idx_route_debug(
-            _ptr(debug.get("cand")), debug["cand"].shape[1] if debug.get("cand") is not None else 0,
-            _ptr(debug.get("cand_len")), _ptr(debug.get("order")), _ptr(debug.get("order_take")),
-            debug["order"].shape[1] if debug.get("order") is not None else 0, _ptr(debug.get("n_order")),
-            _ptr(debug.get("rep_scores")),
-            debug["rep_scores"].shape[1] if debug.get("rep_scores") is not None else 0,
-            _ptr(debug.get("version")), ev, int(debug.get("list_cap", 0)), _ptr(debug.get("cand_scores")))
+    dbg = _route_debug(debug)
     _check(lib().idx_route_topk(ix.handle, _ptr(q, ELEM_BYTES[ix.dtype], "q"), _ptr(q_scale, 4, "q_scale"),
                                 _ptr(w, 4, "w"), q_pos0, T, k, budget, _ptr(topk_idx, 4, "topk_idx"),
                                 _ptr(topk_score, 4, "topk_score"), ctypes.byref(dbg) if dbg is not None else None,
@@ -227,7 +224,7 @@ def idx_export(ix: Index, which: int) -> dict:
     ns, nm, d, nb = buf.n_slots, buf.n_members, ix.cfg["dim"], buf.n_bound_keys
     out = dict(sizes=np.zeros(ns, np.int32), offsets=np.zeros(ns, np.int32), members=np.zeros(nm, np.int32),
                centroids=np.zeros((ns, d), np.float32),
-               reps=np.zeros((ns, d), {"f32": np.float32, "bf16": np.uint16, "e4m3": np.uint8}[ix.dtype]),
+               reps=np.zeros((ns, d), _HOST_DTYPE[ix.dtype]),
                rep_scale=np.zeros(ns, np.float32), rep_f32=np.zeros((ns, d), np.float32),
                assign=np.zeros(nb, np.int32), ub=np.zeros(nb, np.float32), lb=np.zeros(nb, np.float32))
     for k in out:
@@ -238,6 +235,45 @@ def idx_export(ix: Index, which: int) -> dict:
         for k in ("assign", "ub", "lb"):
             del out[k]
     return out
+
+
+def idx_export_version(ix: Index, prefix_len: int) -> dict:
+    """Host copy of the clusters a query with `prefix_len` keys in its prefix routes
+    over: slots [0, m*C), the epoch's below e*Q and seal clusters above; also 'epoch'
+    and 'windows' (e and m)."""
+    buf = _lib.idx_export_buf()
+    ep, win = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().idx_export_version(ix.handle, prefix_len, ctypes.byref(ep), ctypes.byref(win), ctypes.byref(buf)))
+    ns, nm, d = buf.n_slots, buf.n_members, ix.cfg["dim"]
+    out = dict(sizes=np.zeros(ns, np.int32), offsets=np.zeros(ns, np.int32), members=np.zeros(nm, np.int32),
+               centroids=np.zeros((ns, d), np.float32), reps=np.zeros((ns, d), _HOST_DTYPE[ix.dtype]),
+               rep_scale=np.zeros(ns, np.float32), rep_f32=np.zeros((ns, d), np.float32))
+    for k in out:
+        setattr(buf, k, out[k].ctypes.data if out[k].size else None)
+    _check(lib().idx_export_version(ix.handle, prefix_len, ctypes.byref(ep), ctypes.byref(win), ctypes.byref(buf)))
+    out["epoch"], out["windows"] = ep.value, win.value
+    return out
+
+
+def idx_import_version(ix: Index, prefix_len: int, sizes, members, centroids, reps, rep_scale=None, rep_f32=None,
+                       stream=None):
+    """Install a host-built cluster set as the next refit epoch (see the C header).
+    sizes [n_slots], members (slot by slot, ascending within a slot), centroids
+    [n_slots, d] fp32, reps [n_slots, d] in the key format (uint16 bf16 bits, uint8
+    E4M3 codes), rep_scale [n_slots] for E4M3, rep_f32 optional."""
+    d = ix.cfg["dim"]
+    arrs = dict(sizes=np.ascontiguousarray(sizes, dtype=np.int32),
+                members=np.ascontiguousarray(members, dtype=np.int32),
+                centroids=np.ascontiguousarray(centroids, dtype=np.float32).reshape(-1, d),
+                reps=np.ascontiguousarray(reps, dtype=_HOST_DTYPE[ix.dtype]).reshape(-1, d),
+                rep_scale=None if rep_scale is None else np.ascontiguousarray(rep_scale, dtype=np.float32),
+                rep_f32=None if rep_f32 is None else np.ascontiguousarray(rep_f32, dtype=np.float32).reshape(-1, d))
+    ns = arrs["sizes"].shape[0]
+    if arrs["centroids"].shape[0] != ns or arrs["reps"].shape[0] != ns:
+        raise ValueError("centroids and reps need one row per slot")
+    buf = _lib.idx_import_buf(ns, *[arrs[k].ctypes.data if arrs[k] is not None and arrs[k].size else None
+                                    for k in ("sizes", "members", "centroids", "reps", "rep_scale", "rep_f32")])
+    _check(lib().idx_import_version(ix.handle, prefix_len, ctypes.byref(buf), _stream(stream)))
 
 
 def idx_encoder_floats(dim: int) -> int:
@@ -255,6 +291,6 @@ def idx_set_encoder(ix: Index, weights: torch.Tensor | None, stream=None):
 
 
 __all__ = ["IdxError", "Index", "idx_create", "idx_destroy", "idx_last_error", "idx_get_info", "idx_build_seal",
-           "idx_refit", "idx_publish", "idx_route_topk", "idx_route_topk_pos", "idx_exhaustive_workspace_bytes",
-           "idx_exhaustive_topk", "idx_export", "idx_encoder_floats", "idx_set_encoder", "make_route_debug",
-           "DTYPES"]
+           "idx_refit", "idx_publish", "idx_abandon_refit", "idx_route_topk", "idx_route_topk_pos",
+           "idx_exhaustive_workspace_bytes", "idx_exhaustive_topk", "idx_export", "idx_export_version",
+           "idx_import_version", "idx_encoder_floats", "idx_set_encoder", "make_route_debug", "DTYPES"]

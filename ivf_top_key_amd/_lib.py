@@ -39,15 +39,21 @@ class idx_export_buf(ctypes.Structure):
                 ("lb", c_vp)]
 
 
+class idx_import_buf(ctypes.Structure):
+    _fields_ = [("n_slots", c_i32), ("sizes", c_vp), ("members", c_vp), ("centroids", c_vp), ("reps", c_vp),
+                ("rep_scale", c_vp), ("rep_f32", c_vp)]
+
+
 # (name, restype, argtypes) of every exported function
 SIGNATURES = [
-    ("idx_create", c_i32, [ctypes.POINTER(idx_config), ctypes.POINTER(c_vp)]),
+    ("idx_create", c_i32, [ctypes.POINTER(idx_config), c_vp, ctypes.POINTER(c_vp)]),
     ("idx_destroy", c_i32, [c_vp]),
     ("idx_last_error", ctypes.c_char_p, []),
     ("idx_get_info", c_i32, [c_vp, ctypes.POINTER(idx_info)]),
     ("idx_build_seal", c_i32, [c_vp, c_vp, c_vp, c_i64, c_vp]),
     ("idx_refit", c_i32, [c_vp, c_vp, c_vp, ctypes.POINTER(c_i32)]),
     ("idx_publish", c_i32, [c_vp, c_vp, ctypes.POINTER(c_i32)]),
+    ("idx_abandon_refit", c_i32, [c_vp, c_vp, ctypes.POINTER(c_i32)]),
     ("idx_route_topk", c_i32, [c_vp, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp,
                                ctypes.POINTER(idx_route_debug), c_vp]),
     ("idx_route_topk_pos", c_i32, [c_vp, c_vp, c_vp, c_vp, ctypes.POINTER(c_i64), c_i32, c_i32, c_i32, c_vp, c_vp,
@@ -56,6 +62,9 @@ SIGNATURES = [
     ("idx_exhaustive_topk", c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32,
                                     c_vp, c_vp, c_vp, c_i64, c_vp]),
     ("idx_export", c_i32, [c_vp, c_i32, ctypes.POINTER(idx_export_buf)]),
+    ("idx_export_version", c_i32, [c_vp, c_i64, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
+                                   ctypes.POINTER(idx_export_buf)]),
+    ("idx_import_version", c_i32, [c_vp, c_i64, ctypes.POINTER(idx_import_buf), c_vp]),
     ("idx_encoder_floats", c_i64, [c_i32]),
     ("idx_set_encoder", c_i32, [c_vp, c_vp, c_vp]),
 ]

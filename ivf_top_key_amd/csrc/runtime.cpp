@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -124,11 +125,14 @@ struct idx_index {
   int *item_id = nullptr, *item_first = nullptr, *item_n = nullptr, *ctr = nullptr;
   float* sbuf = nullptr;
   std::vector<void*> allocs;
+  hipStream_t fill_stream = nullptr;   // idx_create's stream: new memory is zero-filled on it
   int64_t bytes = 0;
   int64_t n_keys = 0;
   int sealed = 0;
   int computed = 0;
   int published = 0;
+  int imported = 0;          // epoch installed by idx_import_version (no refit bound state)
+  int lost = 0;              // newest epoch whose ring store a later refit or import reused
   hipEvent_t ev_main = nullptr, ev_refit = nullptr;
   bool poisoned = false;
 
@@ -139,7 +143,10 @@ struct idx_index {
     void* v = nullptr;
     const size_t b = (size_t)count * sizeof(T);
     if (hipMalloc(&v, b) != hipSuccess) return false;
-    if (hipMemset(v, 0, b) != hipSuccess) return false;
+    if (hipMemsetAsync(v, 0, b, fill_stream) != hipSuccess) {
+      (void)hipFree(v);
+      return false;
+    }
     allocs.push_back(v);
     bytes += (int64_t)b;
     *p = static_cast<T*>(v);
@@ -171,6 +178,11 @@ int device_error(idx_index* ix, hipError_t e, const char* what) {
   return fail(IDX_EDEVICE, "%s: %s", what, hipGetErrorString(e));
 }
 
+// Oldest refit epoch whose store still holds it: the ring keeps three stores, and a
+// refit or import of epoch r reuses the store of epoch r - 3 (also when that refit
+// is later abandoned).
+int oldest_held(const idx_index* ix) { return std::max(std::max(1, ix->computed - 2), ix->lost + 1); }
+
 int check_handle(const idx_index* ix) {
   if (!ix) return fail(IDX_EINVAL, "null index handle");
   if (ix->poisoned) return fail(IDX_ESTATE, "index handle is poisoned by an earlier device error");
@@ -183,7 +195,7 @@ extern "C" {
 
 const char* idx_last_error(void) { return g_err.c_str(); }
 
-int idx_create(const idx_config* cfg, idx_index** out) {
+int idx_create(const idx_config* cfg, void* stream, idx_index** out) {
   g_err.clear();
   if (!cfg || !out) return fail(IDX_EINVAL, "null config or output pointer");
   *out = nullptr;
@@ -214,6 +226,7 @@ int idx_create(const idx_config* cfg, idx_index** out) {
   idx_index* ix = new (std::nothrow) idx_index();
   if (!ix) return fail(IDX_ENOMEM, "host allocation failed");
   ix->cfg = c;
+  ix->fill_stream = (hipStream_t)stream;
   (void)hipGetDevice(&ix->device);
   ix->Cs = Cs;
   ix->wpr = c.refit_every ? c.refit_every / c.window : 0;
@@ -283,16 +296,18 @@ int idx_create(const idx_config* cfg, idx_index** out) {
          ix->alloc(&ix->ovf, c.max_keys) && ix->alloc(&ix->ovf_count, 1);
   }
   if (!ok) {
+    (void)hipStreamSynchronize(ix->fill_stream);
     ix->release();
     delete ix;
     return fail(IDX_ENOMEM, "device allocation failed");
   }
   if (hipEventCreateWithFlags(&ix->ev_main, hipEventDisableTiming) != hipSuccess ||
       hipEventCreateWithFlags(&ix->ev_refit, hipEventDisableTiming) != hipSuccess ||
-      hipDeviceSynchronize() != hipSuccess) {
+      hipStreamSynchronize(ix->fill_stream) != hipSuccess) {
+    (void)hipDeviceSynchronize();
     ix->release();
     delete ix;
-    return fail(IDX_EDEVICE, "event creation failed");
+    return fail(IDX_EDEVICE, "event creation or zero fill failed");
   }
   *out = ix;
   return IDX_OK;
@@ -457,6 +472,8 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   if (e == hipSuccess) e = hipEventRecord(ix->ev_refit, side);
   if (e != hipSuccess) return device_error(ix, e, "refit launch");
   ix->computed = r;
+  ix->lost = std::max(ix->lost, r - 3);
+  ix->imported = 0;
   if (launched) *launched = 1;
   return IDX_OK;
 }
@@ -471,6 +488,22 @@ int idx_publish(idx_index* ix, void* stream, int32_t* published) {
     ix->published = ix->computed;
   }
   if (published) *published = ix->published;
+  return IDX_OK;
+}
+
+int idx_abandon_refit(idx_index* ix, void* stream, int32_t* abandoned) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (abandoned) *abandoned = 0;
+  if (ix->computed == ix->published) return IDX_OK;
+  (void)hipSetDevice(ix->device);
+  // the store the refit writes is the one the next launch (or import) of the same
+  // epoch writes again: order everything later on the main stream after it
+  const hipError_t e = hipStreamWaitEvent((hipStream_t)stream, ix->ev_refit, 0);
+  if (e != hipSuccess) return device_error(ix, e, "abandon wait");
+  if (abandoned) *abandoned = ix->computed;
+  ix->computed = ix->published;
+  ix->imported = 0;
   return IDX_OK;
 }
 
@@ -511,7 +544,7 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
     // held (the ring keeps three stores and a refit in flight overwrites the oldest)
     const int r0 = std::min(P, windows_in(pmin + 1) / ix->wpr);
     const int r1 = std::min(P, windows_in(pmax + 1) / ix->wpr);
-    const int oldest = std::max(1, ix->computed - 2);
+    const int oldest = oldest_held(ix);
     const int lo = std::max(r0, 1);
     if (r1 >= 1 && lo < oldest)
       return fail(IDX_ESTATE, "queries at %lld..%lld need epoch %d; epochs below %d are no longer held",
@@ -734,7 +767,7 @@ int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
     size = ix->sl_size; off = ix->sl_off; members = ix->sl_members;
     cent = ix->sl_cent; rep = ix->sl_rep; rsc = ix->sl_rsc; lrep = ix->sl_lrep;
   } else {
-    if (which < 1 || which > ix->computed || which <= ix->computed - 3)
+    if (which < 1 || which > ix->computed || which < oldest_held(ix))
       return fail(IDX_ESTATE, "epoch %d is not held (computed %d)", which, ix->computed);
     n_slots = (int64_t)which * ix->Q;
     n_members = (int64_t)which * ix->wpr * c.window;
@@ -759,7 +792,7 @@ int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
   buf->n_screened = -1;
   buf->n_brute = -1;
   buf->n_bound_keys = 0;
-  if (which >= 1 && which == ix->computed) {
+  if (which >= 1 && which == ix->computed && ix->imported != which) {
     int wc = 0, oc = 0;
     cp(&wc, ix->work_count, 4);
     cp(&oc, ix->ovf_count, 4);
@@ -772,6 +805,161 @@ int idx_export(idx_index* ix, int32_t which, idx_export_buf* buf) {
     cp(buf->lb, ix->lb + c.n_sink, (size_t)nb * 4);
   }
   if (e != hipSuccess) return device_error(ix, e, "export copy");
+  return IDX_OK;
+}
+
+int idx_export_version(idx_index* ix, int64_t prefix_len, int32_t* epoch, int32_t* windows, idx_export_buf* buf) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (!buf) return fail(IDX_EINVAL, "null export buffer");
+  if (prefix_len < 1) return fail(IDX_EINVAL, "prefix_len must be >= 1");
+  if (prefix_len > ix->n_keys)
+    return fail(IDX_ECAUSAL, "prefix_len %lld exceeds the %lld inserted keys", (long long)prefix_len,
+                (long long)ix->n_keys);
+  const idx_config& c = ix->cfg;
+  const int m = prefix_len >= c.n_sink ? (int)((prefix_len - c.n_sink) / c.window) : 0;
+  const int r = ix->wpr ? std::min(ix->published, m / ix->wpr) : 0;
+  if (r >= 1 && r < oldest_held(ix))
+    return fail(IDX_ESTATE, "prefix %lld routes over epoch %d, which is no longer held", (long long)prefix_len, r);
+  if (epoch) *epoch = r;
+  if (windows) *windows = m;
+  const int64_t n_slots = (int64_t)m * ix->Cs, n_members = (int64_t)m * c.window;
+  const int64_t e_slots = (int64_t)r * ix->Q, e_members = (int64_t)r * c.refit_every;
+  buf->n_slots = (int32_t)n_slots;
+  buf->n_members = (int32_t)n_members;
+  buf->n_screened = -1;
+  buf->n_brute = -1;
+  buf->n_bound_keys = 0;
+  (void)hipSetDevice(ix->device);
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return device_error(ix, e, "export wait");
+  const EpochStore* es = r >= 1 ? &ix->ep[r % 3] : nullptr;
+  // slots [0, e_slots) and members [0, e_members) from the epoch, the rest from the
+  // seal store; a seal slot's offset already counts the members of the windows
+  // before it, e_members of them being the epoch's
+  auto cp = [&](void* dst, const void* ep_src, const void* sl_src, int64_t n_ep, int64_t n_all, size_t unit) {
+    if (!dst || e != hipSuccess) return;
+    uint8_t* d = static_cast<uint8_t*>(dst);
+    if (n_ep > 0) e = hipMemcpy(d, ep_src, (size_t)n_ep * unit, hipMemcpyDeviceToHost);
+    if (e == hipSuccess && n_all > n_ep)
+      e = hipMemcpy(d + (size_t)n_ep * unit, static_cast<const uint8_t*>(sl_src) + (size_t)n_ep * unit,
+                    (size_t)(n_all - n_ep) * unit, hipMemcpyDeviceToHost);
+  };
+  const size_t dbytes = (size_t)c.dim * 4;
+  cp(buf->sizes, es ? es->size : nullptr, ix->sl_size, e_slots, n_slots, 4);
+  cp(buf->offsets, es ? es->off : nullptr, ix->sl_off, e_slots, n_slots, 4);
+  cp(buf->members, es ? es->members : nullptr, ix->sl_members, e_members, n_members, 4);
+  cp(buf->centroids, es ? es->cent : nullptr, ix->sl_cent, e_slots, n_slots, dbytes);
+  cp(buf->reps, es ? es->rep : nullptr, ix->sl_rep, e_slots, n_slots, (size_t)ix->RB);
+  cp(buf->rep_scale, es ? es->rsc : nullptr, ix->sl_rsc, e_slots, n_slots, 4);
+  cp(buf->rep_f32, es ? es->lrep : nullptr, ix->sl_lrep, e_slots, n_slots, dbytes);
+  if (e != hipSuccess) return device_error(ix, e, "export copy");
+  return IDX_OK;
+}
+
+int idx_import_version(idx_index* ix, int64_t prefix_len, const idx_import_buf* buf, void* stream) {
+  g_err.clear();
+  if (int e = check_handle(ix)) return e;
+  if (!buf) return fail(IDX_EINVAL, "null import buffer");
+  const idx_config& c = ix->cfg;
+  if (!ix->wpr) return fail(IDX_EINVAL, "the index has no refit epochs (refit_every = 0)");
+  if (ix->computed != ix->published) return fail(IDX_ESTATE, "a refit is in flight; publish or abandon it first");
+  const int r = ix->computed + 1;
+  const int64_t S = c.n_sink, B = S + (int64_t)r * c.refit_every;
+  if (prefix_len != B)
+    return fail(IDX_EINVAL, "prefix_len %lld is not the boundary %lld of the next epoch %d", (long long)prefix_len,
+                (long long)B, r);
+  if (B > ix->n_keys)
+    return fail(IDX_ECAUSAL, "epoch %d covers keys below %lld; only %lld are inserted", r, (long long)B,
+                (long long)ix->n_keys);
+  if (ix->sealed < r * ix->wpr) return fail(IDX_ESTATE, "keys below %lld are not sealed yet", (long long)B);
+  const int64_t ns = (int64_t)r * ix->Q;
+  if (buf->n_slots != ns) return fail(IDX_EINVAL, "epoch %d has %lld slots (got %d)", r, (long long)ns, buf->n_slots);
+  if (!buf->sizes || !buf->members || !buf->centroids || !buf->reps)
+    return fail(IDX_EINVAL, "null sizes, members, centroids or reps");
+  if (c.dtype == IDX_E4M3 && !buf->rep_scale) return fail(IDX_EINVAL, "E4M3 representatives need rep_scale");
+  const int64_t nm = B - S;
+  std::vector<int> off((size_t)ns), assign_h((size_t)nm, -1);
+  int64_t total = 0;
+  for (int64_t s = 0; s < ns; ++s) {
+    const int sz = buf->sizes[s];
+    if (sz < 0 || total + sz > nm)
+      return fail(IDX_EINVAL, "slot %lld: size %d; the members must cover keys [%lld, %lld) exactly once",
+                  (long long)s, sz, (long long)S, (long long)B);
+    off[(size_t)s] = (int)total;
+    int64_t prev = -1;
+    for (int i = 0; i < sz; ++i) {
+      const int64_t pos = buf->members[total + i];
+      if (pos >= B)
+        return fail(IDX_ECAUSAL, "slot %lld: member %lld lies at or beyond the version's prefix %lld", (long long)s,
+                    (long long)pos, (long long)B);
+      if (pos < S) return fail(IDX_EINVAL, "slot %lld: member %lld is a sink or negative", (long long)s, (long long)pos);
+      if (pos <= prev) return fail(IDX_EINVAL, "slot %lld: members must be strictly ascending", (long long)s);
+      if (assign_h[(size_t)(pos - S)] >= 0)
+        return fail(IDX_EINVAL, "key %lld is a member of slots %d and %lld", (long long)pos,
+                    assign_h[(size_t)(pos - S)], (long long)s);
+      assign_h[(size_t)(pos - S)] = (int)s;
+      prev = pos;
+    }
+    total += sz;
+  }
+  if (total != nm) return fail(IDX_EINVAL, "the members cover %lld of the %lld keys of [%lld, %lld)", (long long)total,
+                               (long long)nm, (long long)S, (long long)B);
+  const int d = c.dim;
+  for (int64_t i = 0; i < ns * d; ++i)
+    if (!std::isfinite(buf->centroids[i]) || (buf->rep_f32 && !std::isfinite(buf->rep_f32[i])))
+      return fail(IDX_EINVAL, "slot %lld: centroid or representative is not finite", (long long)(i / d));
+  if (c.dtype == IDX_E4M3) {
+    const uint8_t* codes = static_cast<const uint8_t*>(buf->reps);
+    for (int64_t s = 0; s < ns; ++s) {
+      const float sc = buf->rep_scale[s];
+      if (!(sc > 0.0f) || !std::isfinite(sc)) return fail(IDX_EINVAL, "slot %lld: rep_scale must be finite and > 0", (long long)s);
+      for (int i = 0; i < d; ++i)
+        if ((codes[s * d + i] & 0x7F) == 0x7F) return fail(IDX_EINVAL, "slot %lld: E4M3 NaN code", (long long)s);
+    }
+  } else if (c.dtype == IDX_F32) {
+    const float* v = static_cast<const float*>(buf->reps);
+    for (int64_t i = 0; i < ns * d; ++i)
+      if (!std::isfinite(v[i])) return fail(IDX_EINVAL, "slot %lld: representative is not finite", (long long)(i / d));
+  } else {
+    const uint16_t* v = static_cast<const uint16_t*>(buf->reps);
+    for (int64_t i = 0; i < ns * d; ++i)
+      if ((v[i] & 0x7F80u) == 0x7F80u) return fail(IDX_EINVAL, "slot %lld: representative is not finite", (long long)(i / d));
+  }
+  (void)hipSetDevice(ix->device);
+  hipStream_t s = (hipStream_t)stream;
+  // the target store (epoch r - 3's) may still be read by routes enqueued earlier
+  hipError_t e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipEventSynchronize(ix->ev_refit);
+  if (e != hipSuccess) return device_error(ix, e, "import wait");
+  EpochStore& out = ix->ep[r % 3];
+  std::vector<float> ones((size_t)ns, 1.0f), zeros((size_t)ns, 0.0f), ub_h((size_t)nm, HUGE_VALF),
+      lb_h((size_t)nm, 0.0f);
+  const float zero = 0.0f;
+  auto h2d = [&](void* dst, const void* src, size_t bytes) {
+    if (e == hipSuccess && bytes) e = hipMemcpy(dst, src, bytes, hipMemcpyHostToDevice);
+  };
+  h2d(out.size, buf->sizes, (size_t)ns * 4);
+  h2d(out.off, off.data(), (size_t)ns * 4);
+  h2d(out.members, buf->members, (size_t)nm * 4);
+  h2d(out.cent, buf->centroids, (size_t)ns * d * 4);
+  h2d(out.lrep, buf->rep_f32 ? buf->rep_f32 : buf->centroids, (size_t)ns * d * 4);
+  h2d(out.rep, buf->reps, (size_t)ns * ix->RB);
+  h2d(out.rsc, c.dtype == IDX_E4M3 ? buf->rep_scale : ones.data(), (size_t)ns * 4);
+  // no bounds: the next refit finds every key uncertified (lower bound 0) and
+  // compares it with every centre; the centres did not move
+  h2d(out.drift, zeros.data(), (size_t)ns * 4);
+  h2d(out.drift_max, &zero, 4);
+  h2d(ix->assign + S, assign_h.data(), (size_t)nm * 4);
+  h2d(ix->ub + S, ub_h.data(), (size_t)nm * 4);
+  h2d(ix->lb + S, lb_h.data(), (size_t)nm * 4);
+  if (e == hipSuccess)
+    e = launch_copy_member_rows(out.members, 0, nm, ix->keys, ix->kscale, ix->n_keys, ix->RB, out.ckeys, out.cscale, s);
+  if (e == hipSuccess) e = hipEventRecord(ix->ev_refit, s);
+  if (e != hipSuccess) return device_error(ix, e, "import copy");
+  ix->computed = r;
+  ix->lost = std::max(ix->lost, r - 3);
+  ix->imported = r;
   return IDX_OK;
 }
 

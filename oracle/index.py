@@ -291,6 +291,26 @@ class OracleIndex:
     def publish(self):
         self.published = self.computed
 
+    def install_epoch(self, clusters: list) -> int:
+        """Take a cluster set built elsewhere as the next epoch r, in place of
+        computing refit r (test fixtures; the library's import of a version).
+        clusters: one Cluster per slot [0, r*Q), slot order.  The set must cover
+        the keys [S, B_r) exactly once, none at or beyond B_r.  Returns r."""
+        if not self.refit_due():
+            raise RuntimeError("no refit boundary has been sealed past")
+        r = self.computed + 1
+        lo, hi = self.cfg.n_sink, self.boundary(r)
+        if [c.slot for c in clusters] != list(range(r * self.cfg.slots_per_refit)):
+            raise ValueError("one cluster per slot of the epoch, in slot order")
+        allm = np.sort(np.concatenate([c.members for c in clusters]))
+        if allm.size and allm.max() >= hi:
+            raise CausalityError("a member lies beyond the epoch's prefix")
+        if not np.array_equal(allm, np.arange(lo, hi)):
+            raise ValueError("the members must cover the epoch's keys exactly once")
+        self.epochs[r] = list(clusters)
+        self.computed = r
+        return r
+
     # ---- versions --------------------------------------------------------
     def version_of(self, n: int):
         """(epoch r, windows m) seen by a query whose prefix has n keys."""

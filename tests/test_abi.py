@@ -29,7 +29,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for required in ("idx_build_seal", "idx_refit", "idx_route_topk", "idx_exhaustive_topk", "idx_create",
                      "idx_destroy", "idx_last_error", "idx_publish", "idx_export", "idx_get_info",
-                     "idx_exhaustive_workspace_bytes"):
+                     "idx_exhaustive_workspace_bytes", "idx_export_version", "idx_import_version",
+                     "idx_abandon_refit"):
         assert required in names
 
 
@@ -59,7 +60,7 @@ def _cfg(**over):
 ])
 def test_create_rejects_bad_config(lib, over, code):
     h = ctypes.c_void_p()
-    rc = lib.idx_create(ctypes.byref(_cfg(**over)), ctypes.byref(h))
+    rc = lib.idx_create(ctypes.byref(_cfg(**over)), None, ctypes.byref(h))
     assert rc == code, lib.idx_last_error()
     assert h.value is None
     assert lib.idx_last_error()
@@ -72,6 +73,9 @@ def test_calls_on_null_handle(lib):
     assert lib.idx_route_topk(None, None, None, None, 0, 1, 1, 1, None, None, None, None) == -1
     assert lib.idx_route_topk_pos(None, None, None, None, None, 1, 1, 1, None, None, None, None) == -1
     assert lib.idx_export(None, -1, None) == -1
+    assert lib.idx_export_version(None, 1, None, None, None) == -1
+    assert lib.idx_import_version(None, 1, None, None) == -1
+    assert lib.idx_abandon_refit(None, None, None) == -1
     assert lib.idx_get_info(None, None) == -1
     assert lib.idx_destroy(None) == 0
 
@@ -93,6 +97,12 @@ def test_exhaustive_rejects_bad_arguments(lib):
     assert call(q0=97, T=4) == -4        # query position 100 has no key
     assert call(ws=16) == -1             # workspace below one query row
     assert "workspace" in lib.idx_last_error().decode()
+
+
+def test_create_rejects_null_arguments(lib):
+    h = ctypes.c_void_p()
+    assert lib.idx_create(None, None, ctypes.byref(h)) == -1
+    assert lib.idx_create(ctypes.byref(_cfg()), None, None) == -1
 
 
 def test_workspace_size(lib):

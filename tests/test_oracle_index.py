@@ -247,3 +247,47 @@ def test_route_at_positions_matches_single_query_routes():
         assert np.all(idx[t][idx[t] >= 0] <= p)
     with pytest.raises(Exception):
         ix.route_at(q[:1], None, w[:1], np.array([6000]), 32, 1500)
+
+
+def test_hand_computed_index():
+    """The oracle's routing over a hand-built epoch reproduces every value worked out
+    by hand in tests/golden/hand_index.json (representative scores, version, cluster
+    order and takes, candidate list, top-k, exhaustive top-k)."""
+    import hand_fixture as hf
+    from oracle.index import make_cluster
+    from oracle.index import CausalityError
+    g = hf.load()
+    c = g["config"]
+    cfg = OracleConfig(heads=hf.H, dim=hf.D, dtype="f32", **c)
+    ix = OracleIndex(cfg)
+    ix.append(hf.keys(g))
+    assert ix.refit_due()
+    sizes, flat, cents, reps = hf.epoch_arrays(g)
+    offs = np.concatenate([[0], np.cumsum(sizes)])
+    clusters = [make_cluster(s, flat[offs[s]:offs[s + 1]], cents[s], "f32", reps[s]) for s in range(len(sizes))]
+    bad = [make_cluster(s, cl.members, cl.centroid, "f32") for s, cl in enumerate(clusters)]
+    bad[2] = make_cluster(2, np.array([3, 8]), cents[2], "f32")            # key 8 is beyond the epoch
+    with pytest.raises(CausalityError):
+        ix.install_epoch(bad)
+    assert ix.install_epoch(clusters) == 1
+    ix.publish()
+    q, w = hf.query(g)
+    for case in g["queries"]:
+        p = case["position"]
+        idx, sc, dbg = ix.route(q, None, w, p, case["k"], case["budget"], debug=True)
+        d = dbg[0]
+        if "rep_scores" in case:
+            assert d["slots"].tolist() == list(range(len(case["rep_scores"])))
+            assert d["srep"].tolist() == case["rep_scores"]
+        if "version" in case:
+            r, m = d["epoch"], d["windows"]
+            assert [r, m, m * cfg.n_clusters, cfg.n_sink + m * cfg.window] == case["version"]
+        assert [u for u, _ in d["used"]] == case["order"]
+        assert [t for _, t in d["used"]] == case["take"]
+        assert d["cand"].tolist() == case["candidates"]
+        assert idx[0].tolist() == case["topk"] and sc[0].tolist() == case["topk_scores"]
+        if "exhaustive_topk" in case:
+            eidx, _ = ix.exhaustive(q, None, w, p, case["k"])
+            assert eidx[0].tolist() == case["exhaustive_topk"]
+            if "recall" in case:
+                assert recall_per_query(idx, eidx)[0] == case["recall"]
