@@ -319,6 +319,23 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
                         int32_t T, int32_t k, int32_t* topk_idx, float* topk_score, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
+/* idx_exhaustive_topk for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * kernels and the same results, bit for bit, with the score rows kept in a device
+ * array that the library holds on every GPU it runs on, IDX_NOALLOC_SCRATCH_BYTES
+ * per GPU, until the process ends.  The call allocates nothing.  Queries run in
+ * passes of as many score rows (round_up(q_pos0 + T, 64) fp32 each) as the array
+ * holds.  Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (other streams, other threads) race and must be ordered by the caller.
+ * Errors: as idx_exhaustive_topk, and ECAPACITY when a single score row exceeds
+ * the array (q_pos0 + T > 33,554,432 keys); EDEVICE if the array's address cannot
+ * be obtained. */
+#define IDX_NOALLOC_SCRATCH_BYTES (128ll << 20)
+int idx_exhaustive_topk_noalloc(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype,
+                                int32_t heads, int32_t dim, const void* q, const float* q_scale, const float* w,
+                                int64_t q_pos0, int32_t T, int32_t k, int32_t* topk_idx, float* topk_score,
+                                void* stream);
+
 /* Copy one cluster store to host memory (waits for the device).
  *   which = -1: every sealed window's clusters (slots [0, m*C)), members grouped
  *               per window in slot order;

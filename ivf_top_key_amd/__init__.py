@@ -215,6 +215,21 @@ def idx_exhaustive_topk(keys: torch.Tensor, k_scale, dtype: str, heads: int, q: 
     return topk_idx, topk_score
 
 
+def idx_exhaustive_topk_noalloc(keys: torch.Tensor, k_scale, dtype: str, heads: int, q: torch.Tensor, q_scale,
+                                w: torch.Tensor, q_pos0: int, k: int, topk_idx: torch.Tensor,
+                                topk_score: torch.Tensor | None = None, n_keys: int | None = None, stream=None):
+    """idx_exhaustive_topk without a workspace (the library's own scratch array):
+    the caller passes the outputs, nothing is allocated."""
+    d = keys.shape[-1]
+    n_keys = keys.shape[0] if n_keys is None else n_keys
+    eb = ELEM_BYTES[dtype]
+    _check(lib().idx_exhaustive_topk_noalloc(_ptr(keys, eb, "keys"), _ptr(k_scale, 4, "k_scale"), n_keys,
+                                             DTYPES[dtype], heads, d, _ptr(q, eb, "q"), _ptr(q_scale, 4, "q_scale"),
+                                             _ptr(w, 4, "w"), q_pos0, q.shape[0], k, _ptr(topk_idx, 4, "topk_idx"),
+                                             _ptr(topk_score, 4, "topk_score"), _stream(stream)))
+    return topk_idx, topk_score
+
+
 def idx_export(ix: Index, which: int) -> dict:
     """Host copy of one cluster set: which=-1 sealed windows, which=e epoch e.  For the
     newest computed epoch it also holds the refit's counts (n_screened, n_brute) and
@@ -292,5 +307,5 @@ def idx_set_encoder(ix: Index, weights: torch.Tensor | None, stream=None):
 
 __all__ = ["IdxError", "Index", "idx_create", "idx_destroy", "idx_last_error", "idx_get_info", "idx_build_seal",
            "idx_refit", "idx_publish", "idx_abandon_refit", "idx_route_topk", "idx_route_topk_pos",
-           "idx_exhaustive_workspace_bytes", "idx_exhaustive_topk", "idx_export", "idx_export_version",
+           "idx_exhaustive_workspace_bytes", "idx_exhaustive_topk", "idx_exhaustive_topk_noalloc", "idx_export", "idx_export_version",
            "idx_import_version", "idx_encoder_floats", "idx_set_encoder", "make_route_debug", "DTYPES"]

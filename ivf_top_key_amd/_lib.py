@@ -61,6 +61,8 @@ SIGNATURES = [
     ("idx_exhaustive_workspace_bytes", c_i64, [c_i64, c_i32]),
     ("idx_exhaustive_topk", c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i32, c_i32,
                                     c_vp, c_vp, c_vp, c_i64, c_vp]),
+    ("idx_exhaustive_topk_noalloc", c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_i32, c_vp, c_vp, c_vp, c_i64, c_i32,
+                                            c_i32, c_vp, c_vp, c_vp]),
     ("idx_export", c_i32, [c_vp, c_i32, ctypes.POINTER(idx_export_buf)]),
     ("idx_export_version", c_i32, [c_vp, c_i64, ctypes.POINTER(c_i32), ctypes.POINTER(c_i32),
                                    ctypes.POINTER(idx_export_buf)]),

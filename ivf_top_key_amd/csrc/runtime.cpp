@@ -20,6 +20,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -680,32 +681,62 @@ int idx_route_topk_pos(idx_index* ix, const void* q, const float* q_scale, const
   return route_common(ix, q, q_scale, w, 0, positions, T, k, budget, topk_idx, topk_score, dbg, stream);
 }
 
-int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T) {
-  if (n_keys < 1 || T < 1) return 0;
-  return (int64_t)T * round_up(n_keys, 64) * (int64_t)sizeof(float);
+}  // extern "C"
+
+// Score rows of idx_exhaustive_topk_noalloc: one array per GPU, set up when the code
+// object is loaded and held until the process ends.  Host code never names it: its
+// device address comes from hipGetSymbolAddress, once per device.
+static __device__ __align__(256) float scratch[IDX_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+float* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr + message on failure).
+float* scratch_on_current_device(int* dev_out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    fail(IDX_EDEVICE, "no usable current device");
+    return nullptr;
+  }
+  *dev_out = dev;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      fail(IDX_EDEVICE, "scratch address on device %d: %s", dev, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = static_cast<float*>(ptr);
+  }
+  return g_scratch_ptr[dev];
 }
 
-int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
-                        int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
-                        int32_t k, int32_t* topk_idx, float* topk_score, void* workspace, int64_t workspace_bytes,
-                        void* stream) {
-  g_err.clear();
+// Checks shared by both exhaustive entry points (no device work).
+int exhaustive_check(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads, int32_t dim,
+                     const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T, int32_t k,
+                     int32_t* topk_idx) {
   if (dtype < IDX_F32 || dtype > IDX_E4M3) return fail(IDX_EINVAL, "unknown dtype %d", dtype);
   if (heads < 1 || heads > 128) return fail(IDX_EINVAL, "heads must be 1..128");
   if (!dim_supported(dtype, dim)) return fail(IDX_ENOTIMPL, "dim %d not built for dtype %d", dim, dtype);
-  if (!keys || !q || !w || !topk_idx || !workspace) return fail(IDX_EINVAL, "null pointer argument");
+  if (!keys || !q || !w || !topk_idx) return fail(IDX_EINVAL, "null pointer argument");
   if (dtype == IDX_E4M3 && (!k_scale || !q_scale)) return fail(IDX_EINVAL, "E4M3 needs k_scale and q_scale");
   if (T < 1) return fail(IDX_EINVAL, "T must be >= 1");
   if (k < 1 || k > 4096) return fail(IDX_EINVAL, "k must be 1..4096");
   if (q_pos0 < 0) return fail(IDX_EINVAL, "q_pos0 must be >= 0");
   if (q_pos0 + T > n_keys) return fail(IDX_ECAUSAL, "query position beyond n_keys");
-  const int64_t n_max = q_pos0 + T;
-  const int64_t ld = round_up(n_max, 64);
-  const int64_t per_query = ld * (int64_t)sizeof(float);
-  if (workspace_bytes < per_query) return fail(IDX_EINVAL, "workspace too small: %lld bytes, need >= %lld",
-                                               (long long)workspace_bytes, (long long)per_query);
-  const int Tb_max = (int)std::min<int64_t>(T, workspace_bytes / per_query);
-  hipStream_t s = (hipStream_t)stream;
+  return IDX_OK;
+}
+
+// The exhaustive passes: as many queries per pass as `ws_bytes` of score rows hold.
+int exhaustive_passes(const void* keys, const float* k_scale, int32_t dtype, int32_t heads, int32_t dim, const void* q,
+                      const float* q_scale, const float* w, int64_t q_pos0, int32_t T, int32_t k, int32_t* topk_idx,
+                      float* topk_score, float* ws, int64_t ws_bytes, hipStream_t s) {
+  const int64_t ld = round_up(q_pos0 + T, 64);
+  const int Tb_max = (int)std::min<int64_t>(T, ws_bytes / (ld * (int64_t)sizeof(float)));
   for (int t0 = 0; t0 < T; t0 += Tb_max) {
     ExhParams p{};
     p.keys = static_cast<const uint8_t*>(keys);
@@ -717,7 +748,7 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
     p.q_pos0 = q_pos0;
     p.t0 = t0;
     p.Tb = std::min(Tb_max, T - t0);
-    p.ws = static_cast<float*>(workspace);
+    p.ws = ws;
     p.ld = ld;
     p.kchunk = 8192;
     p.k = k;
@@ -729,6 +760,47 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
     if (e != hipSuccess) return fail(IDX_EDEVICE, "exhaustive launch: %s", hipGetErrorString(e));
   }
   return IDX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T) {
+  if (n_keys < 1 || T < 1) return 0;
+  return (int64_t)T * round_up(n_keys, 64) * (int64_t)sizeof(float);
+}
+
+int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
+                        int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0, int32_t T,
+                        int32_t k, int32_t* topk_idx, float* topk_score, void* workspace, int64_t workspace_bytes,
+                        void* stream) {
+  g_err.clear();
+  if (int e = exhaustive_check(keys, k_scale, n_keys, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx))
+    return e;
+  if (!workspace) return fail(IDX_EINVAL, "null pointer argument");
+  const int64_t per_query = round_up(q_pos0 + T, 64) * (int64_t)sizeof(float);
+  if (workspace_bytes < per_query) return fail(IDX_EINVAL, "workspace too small: %lld bytes, need >= %lld",
+                                               (long long)workspace_bytes, (long long)per_query);
+  return exhaustive_passes(keys, k_scale, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx, topk_score,
+                           static_cast<float*>(workspace), workspace_bytes, (hipStream_t)stream);
+}
+
+int idx_exhaustive_topk_noalloc(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
+                                int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
+                                int32_t T, int32_t k, int32_t* topk_idx, float* topk_score, void* stream) {
+  g_err.clear();
+  if (int e = exhaustive_check(keys, k_scale, n_keys, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx))
+    return e;
+  const int64_t per_query = round_up(q_pos0 + T, 64) * (int64_t)sizeof(float);
+  if (per_query > (int64_t)IDX_NOALLOC_SCRATCH_BYTES)
+    return fail(IDX_ECAPACITY, "a score row of %lld keys (%lld bytes) exceeds the %lld-byte scratch array",
+                (long long)(q_pos0 + T), (long long)per_query, (long long)IDX_NOALLOC_SCRATCH_BYTES);
+  int dev = 0;
+  float* ws = scratch_on_current_device(&dev);
+  if (!ws) return IDX_EDEVICE;
+  return exhaustive_passes(keys, k_scale, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx, topk_score, ws,
+                           (int64_t)IDX_NOALLOC_SCRATCH_BYTES, (hipStream_t)stream);
 }
 
 int64_t idx_encoder_floats(int32_t dim) {
