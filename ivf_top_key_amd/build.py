@@ -41,8 +41,20 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found")
 
 
-def _compile(src: str, verbose: bool) -> str:
+def _up_to_date(src: str, obj: str) -> bool:
+    """True if obj is newer than src and every header it may include."""
+    if not os.path.exists(obj):
+        return False
+    deps = [os.path.join(CSRC, src)] + [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".h")] + \
+        [os.path.join(INCLUDE, f) for f in os.listdir(INCLUDE)]
+    t = os.path.getmtime(obj)
+    return all(os.path.getmtime(dep) < t for dep in deps)
+
+
+def _compile(src: str, verbose: bool, incremental: bool = False) -> str:
     obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+    if incremental and _up_to_date(src, obj):
+        return obj
     cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-x")
@@ -55,11 +67,13 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
+def build(verbose: bool = False, jobs: int | None = None, incremental: bool = False) -> str:
+    """Compile every source and link the library.  incremental=True skips sources
+    whose object is newer than the source and every header."""
     os.makedirs(OUT_DIR, exist_ok=True)
     jobs = jobs or min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+        objs = list(ex.map(lambda s: _compile(s, verbose, incremental), SOURCES))
     tmp = LIB + ".tmp"
     cmd = [_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
@@ -72,4 +86,4 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, incremental="--incremental" in sys.argv))
