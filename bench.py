@@ -38,6 +38,8 @@ FP32_PEAK_TFLOPS = 157.3
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "rescore_topk_c4_e4m3_pmc.md")
 PMC_KERNEL = "rescore_topk"
 PMC_SOURCES = ("score.hip", "dev.h", "params.h")
+PMC_FETCH_SCALE = 2.0    # FETCH_SIZE read 524,316 KiB for a copy that reads 1,048,576 KiB
+PMC_WRITE_SCALE = 1.0    # WRITE_SIZE read the 1,048,576 KiB the copy writes
 
 
 def kernel_source_hash():
@@ -189,33 +191,22 @@ def main():
     for _ in range(args.warmup):
         ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc)
     torch.cuda.synchronize()
-    # timed region 1: K steps as a caller runs them -> throughput
+    # timed region: K steps, with HIP events recorded by the library around each kernel
+    # on its launch stream (per-kernel times and the roofline's launch duration come
+    # from the same steps as the throughput)
+    evs = [[hip.event() for _ in range(8)] for _ in range(args.steps)]
     start, stop = hip.event(), hip.event()
     torch.cuda.synchronize()
     hip.h.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream.cuda_stream))
     for s in range(args.steps):
-        ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc)
+        ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc, debug={"events": evs[s]})
     hip.h.hipEventRecord(ctypes.c_void_p(stop), ctypes.c_void_p(stream.cuda_stream))
     torch.cuda.synchronize()
-    total_ms = hip.elapsed(start, stop)
-    ms_per_step = total_ms / args.steps
-    # timed region 2: K more steps with HIP events recorded by the library around each
-    # kernel on its launch stream -> per-kernel times and the roofline (the events
-    # themselves add a little time between kernels, so the step time is taken above)
-    evs = [[hip.event() for _ in range(8)] for _ in range(args.steps)]
-    e0, e1 = hip.event(), hip.event()
-    torch.cuda.synchronize()
-    hip.h.hipEventRecord(ctypes.c_void_p(e0), ctypes.c_void_p(stream.cuda_stream))
-    for s in range(args.steps):
-        ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, out_idx, out_sc, debug={"events": evs[s]})
-    hip.h.hipEventRecord(ctypes.c_void_p(e1), ctypes.c_void_p(stream.cuda_stream))
-    torch.cuda.synchronize()
-    ms_per_step_events = hip.elapsed(e0, e1) / args.steps
+    ms_per_step = hip.elapsed(start, stop) / args.steps
     names = ["rep_score", "route_select", "cluster_score", "rescore_topk"]
     kern = {n: float(np.mean([hip.elapsed(e[2 * i], e[2 * i + 1]) for e in evs])) for i, n in enumerate(names)}
     value = T / (ms_per_step / 1e3)
-    log(f"routed: {ms_per_step:.3f} ms/step, {value:.0f} q/s; with per-kernel events "
-        f"{ms_per_step_events:.3f} ms/step, kernels {kern}")
+    log(f"routed: {ms_per_step:.3f} ms/step, {value:.0f} q/s; kernels {kern}")
 
     # ---- algorithmic work of one step ----
     Cs = W // wl["cluster_size"]
@@ -243,9 +234,10 @@ def main():
         work["rescore_topk"] = ("hbm", float(base_t.sum() * (rb + scale_b + 8) + clus_t.sum() * 8
                                              + T * H * (rb + 8) + T * k * 8))
     else:
-        # every candidate's key row (+ scale) and gather row read, its position read from the
-        # member list, query read, top-k written
-        work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b + 8) + T * H * (rb + 8) + T * k * 8))
+        # the method's bytes: every candidate's key row and scale, the query (row, head
+        # weight and scale per head), the top-k written (position and score); the gather
+        # rows and member positions this design also reads are not counted
+        work["rescore_topk"] = ("hbm", float(cand_t.sum() * (rb + scale_b) + T * H * (rb + 8) + T * k * 8))
         work["cluster_score"] = ("mfma", 0.0)
     rescore_flops = float(2 * H * d * cand_t.sum())
     keys_scored = float((c_vis + cand_t).sum())
@@ -259,9 +251,14 @@ def main():
                         frac=round(ach / peak_mfma, 4), traffic=None, algorithmic_flops=amount,
                         avg_launch_ms=round(kern[name], 4))
         ach = amount / sec / 1e9
-        return dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=round(ach / HBM_PEAK_GBS, 4), traffic=measured_traffic(name, args.workload, budget),
-                    algorithmic_bytes=amount, avg_launch_ms=round(kern[name], 4))
+        traffic = measured_traffic(name, args.workload, budget)
+        out = dict(kernel=name, bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                   frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic, algorithmic_bytes=amount,
+                   avg_launch_ms=round(kern[name], 4))
+        if traffic is not None:
+            out["traffic_calibration"] = {"FETCH_SIZE": PMC_FETCH_SCALE, "WRITE_SIZE": PMC_WRITE_SCALE,
+                                          "from": "one 1 GiB elementwise copy in the profiled process"}
+        return out
 
     dominant = max(kern, key=kern.get)
     roof = roof_of(dominant)
@@ -357,7 +354,6 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
-        "ms_per_step_with_kernel_events": round(ms_per_step_events, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -544,16 +540,49 @@ def cpu_baseline(ix, inp, wl, budget, sample):
     rng = np.random.default_rng(0)
     T = wl["T"]
     pick = np.sort(rng.choice(T, size=min(sample, T), replace=False))
+
+    def run(rows):
+        t0 = time.perf_counter()
+        for t in rows:
+            oix.route(inp["q"][t:t + 1], None if inp["q_scale"] is None else inp["q_scale"][t:t + 1],
+                      inp["w"][t:t + 1], wl["q_pos0"] + int(t), wl["k"], budget)
+        return time.perf_counter() - t0
+
     threads = blas_threads()
-    t0 = time.perf_counter()
-    for t in pick:
-        oix.route(inp["q"][t:t + 1], None if inp["q_scale"] is None else inp["q_scale"][t:t + 1],
-                  inp["w"][t:t + 1], wl["q_pos0"] + int(t), wl["k"], budget)
-    dt_s = time.perf_counter() - t0
+    dt_s = run(pick)
+    # the same oracle on one thread, over the first quarter of the sample
+    one = pick[:max(1, len(pick) // 4)]
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1, user_api="blas"):
+            dt_1 = run(one)
+        single = {"value": round(len(one) / dt_1, 3), "cores": 1, "sample": f"{len(one)} of the same queries; "
+                  f"{dt_1:.1f} s"}
+    except ImportError:
+        single = None
     return {"value": round(len(pick) / dt_s, 3), "unit": "queries/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(pick)} of the {T} tail queries (seeded), routed by the numpy oracle over the same "
                       f"1M-key index (cluster tables loaded from the library's export; fp64 scores; "
-                      f"{threads} BLAS threads); {dt_s:.1f} s"}
+                      f"{threads} BLAS threads); {dt_s:.1f} s",
+            "single_thread": single, "host": host_description()}
+
+
+def host_description():
+    """CPU model and logical CPU count of the machine running the oracle."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = None
+    return {"cpu_model": model, "os_cpu_count": os.cpu_count(), "usable_cpus": usable}
 
 
 if __name__ == "__main__":
