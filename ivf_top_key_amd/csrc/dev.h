@@ -525,10 +525,11 @@ __device__ __forceinline__ void load_query_wregs(QueryFrag<DT, D, HT>& f, const 
 // also quiet signalling NaNs first, which costs a second instruction.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// Score of this lane's column (key) against the query, before the key scale.
-// Lanes l and l+32 return the same value.
+// This lane's half of the score of its column (key): sum over the head rows the lane
+// holds (rows 8j + 4g + e of each head tile, in the order ht, j, e) of
+// w' * ReLU(q . k).  The other half is in lane l ^ 32.
 template <int DT, int D, int HT>
-__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
+__device__ __forceinline__ float tile_partial(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
   v16f acc[HT];
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -541,13 +542,34 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
   float p = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
-    // rows 8j + 4g + e of this head tile, in the order j, e
 #pragma unroll
     for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.w[ht][v], relu(acc[ht][v]), p);
   }
-  // lanes l and l ^ 32 hold the two halves of the head rows of one column: one
-  // cross-half swap gives every lane both (p of lane l & 31 plus p of lane l | 32)
+  return p;
+}
+
+// Score of this lane's column (key) against the query, before the key scale.
+// Lanes l and l+32 return the same value: the lower half's partial plus the upper
+// half's, after one cross-half swap.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
+  const float p = tile_partial<DT, D, HT>(f, b);
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(p), __float_as_uint(p), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Scores of two tiles of 32 keys at once: lane l < 32 returns the score of column l
+// of tile A, lane l >= 32 that of column l - 32 of tile B.  One swap exchanges the
+// upper half of A's partials with the lower half of B's, so each lane adds the
+// lower-half partial and the upper-half partial of its column: the same two fp32
+// values, added once, as score_tile, hence the same bits.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float score_tile_pair(const QueryFrag<DT, D, HT>& f, const uint32_t* bA,
+                                                 const uint32_t* bB) {
+  const float pA = tile_partial<DT, D, HT>(f, bA);
+  const float pB = tile_partial<DT, D, HT>(f, bB);
+  // after the swap: r[0] = [pA lanes 0..31, pB lanes 0..31], r[1] = [pA lanes 32..63, pB lanes 32..63]
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pA), __float_as_uint(pB), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
@@ -656,71 +678,129 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
   return __builtin_amdgcn_make_buffer_rsrc(u, (short)0, __builtin_amdgcn_readfirstlane(bytes), BUF_WORD3);
 }
 
+// LDS of one staged scorer: two stage buffers of rows and their scales.  The two
+// buffers are separate arrays so that the compiler can tell a load into one from a
+// read of the other (and need not wait for the next stage's loads before reading the
+// current stage).
+template <int DT, int D>
+struct StageLds {
+  u32x4 rows0[Stage<DT, D>::CHUNKS];
+  u32x4 rows1[Stage<DT, D>::CHUNKS];
+  float sc0[Stage<DT, D>::SR];
+  float sc1[Stage<DT, D>::SR];
+};
+
 // Scores rows [0, nrows) of a dense run: row i at base + i * RB (16-byte aligned),
 // its scale at scale[i] (scale null: 1).  nrows * RB must fit in 31 bits.  Every
 // thread of the block calls, with uniform arguments; NW waves of 64 lanes.
-// sink(i, x): score of row i for this lane's column (i may be >= nrows; lanes
-// 32..63 repeat lanes 0..31).  tile: 2 * CHUNKS 16-byte vectors of LDS, tsc: 2 * SR
-// floats of LDS.  Rows past nrows read as zeros and are never sunk by the callers.
+// sink(i, x): score x of row i, called once per row by the lane that holds it (i may
+// be >= nrows: rows past the end read as zeros and the callers drop them).  When a
+// stage holds an even number of 32-row tiles and a half row fits in 16 registers,
+// tiles are scored in pairs and lane l holds row r0 + l of the pair; otherwise lanes
+// 0..31 hold the rows of one tile.
+// Stages go from memory straight to LDS (buffer loads with an LDS destination): each
+// lane loads the chunk whose swizzled LDS slot is its own, 64 consecutive slots per
+// wave and load, so no registers hold a stage in flight.  Stage s + 1 loads while
+// stage s is scored; even stages use buffer 0, odd stages buffer 1.
 template <int DT, int D, int HT, int NW, class Sink>
 __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, const uint8_t* base, const float* scale,
-                                             int nrows, u32x4* tile, float* tsc, Sink sink) {
+                                             int nrows, StageLds<DT, D>& lds, Sink sink) {
   using S = Stage<DT, D>;
   using G = Geo<DT, D>;
+  typedef __attribute__((address_space(3))) void lds_void;
   constexpr int NT = NW * 64;
   constexpr int CPT = S::CHUNKS / NT;
-  static_assert(S::CHUNKS % NT == 0, "stage chunks must split evenly over the block");
-  static_assert(S::SR <= NT, "one scale per thread");
-  const int tid = threadIdx.x, col = tid & 31, g = (tid >> 5) & 1;
+  constexpr int TPS = S::SR / 32;            // 32-row tiles per stage
+  constexpr bool PAIR = TPS % 2 == 0 && G::HW <= 16;
+  static_assert(S::CHUNKS % (NT) == 0, "stage chunks must split evenly over the block");
+  static_assert(S::SR <= NT && (S::SR % 64 == 0 || S::SR == 32), "stage scales: one per lane of whole waves");
+  // The swizzle key of row tt*32 + c equals that of row c (CPR <= 32, and for CPR = 8
+  // the key is the row over two), so tile tt's slots are tile 0's plus tt*32*CPR.
+  static_assert(S::CPR <= 32 && 32 % S::CPR == 0, "tile offsets independent of the swizzle");
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = tid & 31, g = (tid >> 5) & 1;
   const int nst = (nrows + S::SR - 1) / S::SR;
   if (nst == 0) return;
   const __amdgpu_buffer_rsrc_t rrow = buffer_rsrc(base, nrows * S::RB);
   const __amdgpu_buffer_rsrc_t rscl = buffer_rsrc(scale, scale ? nrows * 4 : 0);
-  // this thread's chunks: byte offset inside a stage, and LDS slot
-  int voff[CPT], lslot[CPT];
+  // load k of this wave fills LDS slots (k * NW + wave) * 64 + lane of a stage buffer;
+  // the slot's row r and swizzled chunk give the source chunk (the swizzle is an XOR,
+  // its own inverse)
+  int voff[CPT];
 #pragma unroll
   for (int k = 0; k < CPT; ++k) {
-    const int c = k * NT + tid;
-    voff[k] = (c / S::CPR) * S::RB + (c % S::CPR) * 16;
-    lslot[k] = stage_slot<S::CPR>(c / S::CPR, c % S::CPR);
+    const int slot = (k * NW + wave) * 64 + lane;
+    const int r = slot / S::CPR;
+    const int key = (S::CPR == 8) ? (IVFTK_SWZ8(r)) : r;
+    voff[k] = r * S::RB + (((slot % S::CPR) ^ (key & (S::CPR - 1))) * 16);
   }
-  u32x4 reg[CPT];
-  float rsc = 1.0f;
-  auto gload = [&](int st) {
+  // LDS slots of this lane's operand chunks in tile 0
+  int rslot[G::HW / 4];
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) reg[k] = __builtin_amdgcn_raw_buffer_load_b128(rrow, voff[k], st * S::SR * S::RB, 0);
-    if (scale && tid < S::SR) rsc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rscl, tid * 4, st * S::SR * 4, 0));
+  for (int i = 0; i < G::HW / 4; ++i) rslot[i] = stage_slot<S::CPR>(col, g * (S::CPR / 2) + i);
+  if (!scale) {
+    for (int i = tid; i < S::SR; i += NT) {
+      lds.sc0[i] = 1.0f;
+      lds.sc1[i] = 1.0f;
+    }
+  }
+  auto dma = [&](int st, u32x4* rows, float* sc) {
+#pragma unroll
+    for (int k = 0; k < CPT; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rrow, (lds_void*)(rows + (k * NW + wave) * 64), 16, voff[k],
+                                               st * S::SR * S::RB, 0, 0);
+    if (scale && wave * 64 < S::SR)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rscl, (lds_void*)(sc + wave * 64), 4, (wave * 64 + lane) * 4,
+                                               st * S::SR * 4, 0, 0);
   };
-  auto lstore = [&](int b) {
+  auto operand = [&](uint32_t* bf, const u32x4* tb, int tt) {
 #pragma unroll
-    for (int k = 0; k < CPT; ++k) tile[b * S::CHUNKS + lslot[k]] = reg[k];
-    if (tid < S::SR) tsc[b * S::SR + tid] = rsc;
+    for (int i = 0; i < G::HW / 4; ++i) {
+      const u32x4 v = tb[tt * 32 * S::CPR + rslot[i]];
+      bf[4 * i + 0] = v.x;
+      bf[4 * i + 1] = v.y;
+      bf[4 * i + 2] = v.z;
+      bf[4 * i + 3] = v.w;
+    }
   };
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int st = 0; st < nst; ++st) {
-    const int b = st & 1;
-    if (st + 1 < nst) gload(st + 1);
+  auto compute = [&](int st, const u32x4* tb, const float* sb) {
+    if constexpr (PAIR) {
 #pragma unroll
-    for (int tt = 0; tt < S::SR / 32; ++tt) {
-      const int r0 = st * S::SR + tt * 32;
-      if (r0 < nrows) {
-        const int r = tt * 32 + col;
-        uint32_t bf[G::HW];
-#pragma unroll
-        for (int i = 0; i < G::HW / 4; ++i) {
-          const u32x4 v = tile[b * S::CHUNKS + stage_slot<S::CPR>(r, g * (S::CPR / 2) + i)];
-          bf[4 * i + 0] = v.x;
-          bf[4 * i + 1] = v.y;
-          bf[4 * i + 2] = v.z;
-          bf[4 * i + 3] = v.w;
+      for (int tt = 0; tt < TPS; tt += 2) {
+        const int r0 = st * S::SR + tt * 32;
+        if (r0 < nrows) {
+          uint32_t bA[G::HW], bB[G::HW];
+          operand(bA, tb, tt);
+          operand(bB, tb, tt + 1);
+          const float x = score_tile_pair<DT, D, HT>(f, bA, bB) * sb[tt * 32 + lane];
+          sink(r0 + lane, x);
         }
-        const float x = score_tile<DT, D, HT>(f, bf) * tsc[b * S::SR + r];
-        sink(r0 + col, x);
+      }
+    } else {
+#pragma unroll
+      for (int tt = 0; tt < TPS; ++tt) {
+        const int r0 = st * S::SR + tt * 32;
+        if (r0 < nrows) {
+          uint32_t bf[G::HW];
+          operand(bf, tb, tt);
+          const float x = score_tile<DT, D, HT>(f, bf) * sb[tt * 32 + col];
+          if (lane < 32) sink(r0 + col, x);
+        }
       }
     }
-    if (st + 1 < nst) lstore(b ^ 1);
+  };
+  // vmcnt(0) before each barrier: this wave's loads into LDS have landed
+  dma(0, lds.rows0, lds.sc0);
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __syncthreads();
+  for (int st = 0; st < nst; st += 2) {
+    if (st + 1 < nst) dma(st + 1, lds.rows1, lds.sc1);
+    compute(st, lds.rows0, lds.sc0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    __syncthreads();
+    if (st + 1 >= nst) break;
+    if (st + 2 < nst) dma(st + 2, lds.rows0, lds.sc0);
+    compute(st + 1, lds.rows1, lds.sc1);
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
 }

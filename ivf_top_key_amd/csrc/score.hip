@@ -15,14 +15,18 @@ namespace ivftk {
 // ---------------------------------------------------------------------------
 // exhaustive scores: block = 4 waves = 4 queries, one chunk of keys
 // ---------------------------------------------------------------------------
+// Three waves per SIMD where a half row fits in 16 registers (E4M3 and bf16 at d = 64,
+// fp32 at d = 32) and there are at most 64 heads; otherwise the compiler's choice.
 template <int DT, int D, int HT>
-__global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
+constexpr int score_waves() { return (Geo<DT, D>::HW <= 16 && HT <= 2) ? 3 : 1; }
+
+template <int DT, int D, int HT>
+__global__ __launch_bounds__(256, (score_waves<DT, D, HT>())) void k_exh_score(ExhParams p) {
   using G = Geo<DT, D>;
   using S = Stage<DT, D>;
   __shared__ float wq_s[4][HT * 32];
-  __shared__ u32x4 tile[2 * S::CHUNKS];
-  __shared__ float tsc[2 * S::SR];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ StageLds<DT, D> stage;
+  const int wave = threadIdx.x >> 6;
   const int tl = blockIdx.x * 4 + wave;
   const bool active = tl < p.Tb;
   const int tc = p.t0 + (active ? tl : p.Tb - 1);   // idle waves still stage rows
@@ -41,10 +45,10 @@ __global__ __launch_bounds__(256) void k_exh_score(ExhParams p) {
   load_query_wregs<DT, D, HT>(f, wq_s[wave]);
   float* out = p.ws + (size_t)(active ? tl : 0) * p.ld;
   score_staged<DT, D, HT, 4>(
-      f, p.keys + (size_t)j0 * G::RB, DT == DT_E4M3 ? p.kscale + j0 : nullptr, (int)(j1 - j0), tile, tsc,
+      f, p.keys + (size_t)j0 * G::RB, DT == DT_E4M3 ? p.kscale + j0 : nullptr, (int)(j1 - j0), stage,
       [&](int i, float x) {
         const int64_t j = j0 + i;
-        if (lane < 32 && j < j_end) out[j] = x;
+        if (j < j_end) out[j] = x;
       });
 }
 
@@ -317,12 +321,11 @@ __device__ __forceinline__ StoreView epoch_store(const RouteParams& p, int r) { 
 // representative scores: block = 4 queries, one chunk of slots
 // ---------------------------------------------------------------------------
 template <int DT, int D, int HT>
-__global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
+__global__ __launch_bounds__(256, (score_waves<DT, D, HT>())) void k_rep_score(RouteParams p, int chunk) {
   using G = Geo<DT, D>;
   using S = Stage<DT, D>;
   __shared__ float wq_s[4][HT * 32];
-  __shared__ u32x4 tile[2 * S::CHUNKS];
-  __shared__ float tsc[2 * S::SR];
+  __shared__ StageLds<DT, D> stage;
   __shared__ int s_r[4], s_cvis[4];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, col = lane & 31;
   const int t = blockIdx.x * 4 + wave;
@@ -364,10 +367,10 @@ __global__ __launch_bounds__(256) void k_rep_score(RouteParams p, int chunk) {
     auto run = [&](const uint8_t* rep, const float* rsc, int a, int b) {
       if (a >= b) return;
       score_staged<DT, D, HT, 4>(
-          f, rep + (size_t)a * G::RB, DT == DT_E4M3 ? rsc + a : nullptr, b - a, tile, tsc,
+          f, rep + (size_t)a * G::RB, DT == DT_E4M3 ? rsc + a : nullptr, b - a, stage,
           [&](int i, float x) {
             const int s = a + i;
-            if (lane < 32 && s < own_end) out[s] = x;
+            if (s < own_end) out[s] = x;
           });
     };
     run(ep.rep, ep.rsc, s0, min(s1, split));
