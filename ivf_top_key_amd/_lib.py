@@ -74,11 +74,13 @@ SIGNATURES = [
 _lib = None
 
 
-def load(path: str = LIB_PATH) -> ctypes.CDLL:
-    """Load libivftk.so; raises ImportError when it has not been built."""
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libivftk.so (or the build named by IVFTK_LIBRARY, e.g. the host
+    AddressSanitizer build); raises ImportError when it has not been built."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("IVFTK_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m ivf_top_key_amd.build` "
                           "(hipcc, gfx950); there is no fallback implementation")

@@ -243,8 +243,9 @@ int idx_create(const idx_config* cfg, void* stream, idx_index** out) {
   ix->cand_cap = (int)round_up(std::max<int64_t>(c.max_budget, (int64_t)c.n_sink + c.window), 32);
   ix->n_tiles_cap = (int)((ix->member_cap + TILE - 1) / TILE);
   if (ix->slot_cap > 8192) {
+    const long long slots = (long long)ix->slot_cap;
     delete ix;
-    return fail(IDX_ECAPACITY, "max_keys allows %lld clusters; at most 8192 are routed", (long long)(ix->slot_cap));
+    return fail(IDX_ECAPACITY, "max_keys allows %lld clusters; at most 8192 are routed", slots);
   }
   if (!rescore_fits(ix->cand_cap, c.max_k)) {
     delete ix;

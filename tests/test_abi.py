@@ -66,6 +66,18 @@ def test_create_rejects_bad_config(lib, over, code):
     assert lib.idx_last_error()
 
 
+def test_create_valid_config_on_any_host(lib):
+    """A valid configuration either creates an index (a GPU is present) or fails
+    with ENOMEM / EDEVICE and releases what it allocated (no GPU)."""
+    h = ctypes.c_void_p()
+    rc = lib.idx_create(ctypes.byref(_cfg(max_keys=1 << 16, max_queries=64)), None, ctypes.byref(h))
+    assert rc in (0, -2, -3), lib.idx_last_error()
+    if rc == 0:
+        assert lib.idx_destroy(h) == 0
+    else:
+        assert h.value is None and lib.idx_last_error()
+
+
 def test_calls_on_null_handle(lib):
     assert lib.idx_build_seal(None, None, None, 0, None) == -1
     assert lib.idx_refit(None, None, None, None) == -1
