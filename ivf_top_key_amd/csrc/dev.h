@@ -1,7 +1,8 @@
 // Device-side building blocks shared by every kernel of the library (gfx950, wave64).
 //
-// * Stored formats: fp32, bf16, OCP E4M3 (e4m3fn).  Decoding is exact; encoding is
-//   round-to-nearest-even, saturating at +-448 for E4M3.
+// * Stored formats: fp32, bf16, OCP E4M3 (e4m3fn).  Decoding is exact (E4M3 through
+//   the hardware conversion); encoding is round-to-nearest-even, saturating at +-448
+//   for E4M3.
 // * Composite sort keys: (order-preserving bits of an fp32 score) << 32 | ~position,
 //   so that a larger key means a higher score and, among equal scores, a lower
 //   position (the tie rule of the top-k and of cluster ranking).
@@ -42,15 +43,16 @@ struct Elem<DT_E4M3> { static constexpr int bytes = 1; };
 // stored formats
 // ---------------------------------------------------------------------------
 
-// E4M3 code -> fp32 (exact).  Exponent field 0 is subnormal: m * 2^-9.  Both
-// forms are computed and one selected, so no branch separates the loads of a row.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t code) {
-  const uint32_t sign = (code & 0x80u) << 24;
-  const uint32_t e = (code >> 3) & 0xFu;
-  const uint32_t m = code & 7u;
-  const float sub = __uint_as_float(__float_as_uint((float)m * 0x1p-9f) | sign);
-  const float nrm = __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
-  return e == 0 ? sub : nrm;
+// E4M3 code (low byte of the word) -> fp32 (exact).  gfx950's conversion instructions
+// decode the OCP E4M3 format (bias 7, exponent field 0 subnormal: m * 2^-9, no
+// infinities) exactly for every finite code; the NaN codes are never stored.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t code) { return __builtin_amdgcn_cvt_f32_fp8((int)code, 0); }
+
+// The four E4M3 codes of a word (byte b is element b) -> fp32, two per instruction.
+__device__ __forceinline__ void e4m3x4_to_f32(uint32_t word, float& x0, float& x1, float& x2, float& x3) {
+  const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, false);
+  const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)word, true);
+  x0 = lo[0], x1 = lo[1], x2 = hi[0], x3 = hi[1];
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
@@ -111,8 +113,36 @@ __device__ __forceinline__ void load_row_f32(float (&x)[N], const uint8_t* row, 
       x[i] = __uint_as_float(w[i]);
     } else if constexpr (DT == DT_BF16) {
       x[i] = bf16_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu);
-    } else {
-      x[i] = e4m3_to_f32((w[i >> 2] >> (8 * (i & 3))) & 0xFFu) * sk;
+    }
+  }
+  if constexpr (DT == DT_E4M3) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      e4m3x4_to_f32(w[i >> 2], x[i], x[i + 1], x[i + 2], x[i + 3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[i + u] = x[i + u] * sk;
+    }
+  }
+}
+
+// The elements of one 16-byte chunk of a stored row as fp32 times sk (sk = 1 for the
+// unscaled formats).
+template <int DT>
+__device__ __forceinline__ void chunk_to_f32(const uint32_t (&wds)[4], float (&x)[16 / Elem<DT>::bytes], float sk) {
+#pragma unroll
+  for (int e = 0; e < 16 / Elem<DT>::bytes; ++e) {
+    if constexpr (DT == DT_F32) {
+      x[e] = __uint_as_float(wds[e]);
+    } else if constexpr (DT == DT_BF16) {
+      x[e] = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
+    }
+  }
+  if constexpr (DT == DT_E4M3) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      e4m3x4_to_f32(wds[q], x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[4 * q + u] = x[4 * q + u] * sk;
     }
   }
 }

@@ -90,17 +90,11 @@ __device__ __forceinline__ float sqdist_row(const uint8_t* row, float sk, const 
       cv[e + 2] = c4.z;
       cv[e + 3] = c4.w;
     }
+    float xv[EPC];
+    chunk_to_f32<DT>(wds, xv, sk);
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
-      float v;
-      if constexpr (DT == DT_F32) {
-        v = __uint_as_float(wds[e]);
-      } else if constexpr (DT == DT_BF16) {
-        v = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-      } else {
-        v = e4m3_to_f32((wds[e >> 2] >> (8 * (e & 3))) & 0xFFu) * sk;
-      }
-      const float t = v - cv[e];
+      const float t = xv[e] - cv[e];
       acc = acc + t * t;
     }
   }

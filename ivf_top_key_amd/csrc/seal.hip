@@ -1,5 +1,5 @@
 // Seal: size-capped k-means of one window of W keys into C = W/cluster_size clusters
-// (one block per window, one thread per key).
+// (one block per window, one thread per key; the window's keys staged in LDS).
 //
 // AttentionIndex, paper-daily.com explainer, "索引怎么边算边建？" item 2: each time
 // the open window holds W keys it is clustered and the clusters are appended,
@@ -16,10 +16,19 @@
 // greedy walk over (D, key, cluster) triples in ascending order, which gives a key
 // to a cluster while the key is free and the cluster holds fewer than `cap` keys.
 // (When nearest assignment respects the cap the walk returns exactly it: every key
-// meets its nearest cluster first and that cluster cannot be full yet.)  The
-// iterations stop early once an assignment repeats: from there on every iteration
-// would reproduce the same members and centroids, so the result equals the one
-// after the full iteration count.
+// meets its nearest cluster first and that cluster cannot be full yet.)
+// The walk's result is computed here by deferred acceptance: each key proposes to its
+// clusters in (D, cluster) order; a cluster with more than `cap` proposals keeps the
+// `cap` first in (D, key) order and turns the rest away, and those move on to their
+// next cluster, until no cluster is over its cap.  The two agree: the preferences of
+// both sides come from the one strict order of the triples, and under such
+// preferences exactly one assignment is stable (no key and cluster that would both
+// rather have each other than what they hold).  The walk ends in a stable assignment
+// (a key it passes over meets only clusters already full of earlier triples), and so
+// does deferred acceptance; with cap * C >= W both place every key.
+// The iterations stop early once an assignment repeats: from there on every iteration
+// would reproduce the same members and centroids, so the result equals the one after
+// the full iteration count.
 #include "dispatch.h"
 #include "launch.h"
 #include "params.h"
@@ -27,168 +36,207 @@
 namespace ivftk {
 
 constexpr int SEAL_MAXW = 1024;
-constexpr int SEAL_SORT = 8192;
 
-template <int DT, int D>
-__device__ __forceinline__ float key_value(const SealParams& p, int64_t pos, int i) {
-  const uint8_t* row = p.keys + (size_t)pos * (D * Elem<DT>::bytes);
-  float v = load_elem<DT>(row, i);
-  if constexpr (DT == DT_E4M3) v = v * p.kscale[pos];
-  return v;
+// The elements of one 32-bit word of a stored row as fp32 times sk (sk = 1 for the
+// unscaled formats).
+template <int DT>
+__device__ __forceinline__ void word_to_f32(uint32_t w, float (&x)[4 / Elem<DT>::bytes], float sk) {
+  if constexpr (DT == DT_F32) {
+    x[0] = __uint_as_float(w);
+  } else if constexpr (DT == DT_BF16) {
+    x[0] = bf16_to_f32(w & 0xFFFFu);
+    x[1] = bf16_to_f32(w >> 16);
+  } else {
+    e4m3x4_to_f32(w, x[0], x[1], x[2], x[3]);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) x[u] = x[u] * sk;
+  }
 }
 
 template <int DT, int D, int CS>
 __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   constexpr int RB = D * Elem<DT>::bytes;
-  constexpr int EPC = 16 / Elem<DT>::bytes;   // elements per 16-byte load
+  constexpr int EPC = 16 / Elem<DT>::bytes;   // elements per 16-byte chunk
+  constexpr int CPR = RB / 16;                // chunks per row
+  constexpr int DPW = 4 / Elem<DT>::bytes;    // elements per 32-bit word
+  constexpr int QPR = D / DPW;                // words per row
+  // The window's keys are staged in LDS when they fit in 128 KB (row chunk ch of key
+  // m at slot m*CPR + (ch ^ (m & (CPR-1))), so that the rows read by consecutive
+  // threads fall in different banks).
+  constexpr bool STAGE = SEAL_MAXW * RB <= 131072;
+  __shared__ uint4 kst[STAGE ? SEAL_MAXW * CPR : 1];
+  __shared__ float ksc[(STAGE && DT == DT_E4M3) ? SEAL_MAXW : 1];
   __shared__ float cent[CS * D];
-  __shared__ int cnt[CS], clo[CS];
+  __shared__ int cnt[CS], clo[CS], plo[CS], pfill[CS];
   __shared__ uint32_t amax[CS];
   __shared__ int wcnt[16 * CS];
   __shared__ int member[SEAL_MAXW];
-  __shared__ int asg[SEAL_MAXW];
-  __shared__ int first_lane[SEAL_MAXW];
-  __shared__ uint64_t sortbuf[SEAL_SORT];
+  __shared__ uint64_t prop[SEAL_MAXW];
   __shared__ int s_over;
+  __shared__ uint32_t s_dirty;
   const int tid = threadIdx.x, bd = blockDim.x, lane = tid & 63, wv = tid >> 6, nwv = bd >> 6;
   const int W = p.W, cap = p.cap;
   const int w = p.w0 + blockIdx.x;
   const int64_t base = (int64_t)p.S + (int64_t)w * W;
+  const uint8_t* const wrows = p.keys + (size_t)base * RB;
 
-  for (int idx = tid; idx < CS * D; idx += bd) {
-    const int c = idx / D, i = idx % D;
-    cent[idx] = key_value<DT, D>(p, base + ((2 * c + 1) * W) / (2 * CS), i);
+  // the window's rows into LDS: chunk c of the window (row c / CPR) by thread c mod bd,
+  // all loads issued before the stores
+  // (indices clamped into the window, stores masked, so the loads are unconditional)
+  if constexpr (STAGE) {
+    const int nch = W * CPR;
+    for (int c0 = 0; c0 < nch; c0 += 4 * bd) {
+      uint4 v[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[k] = reinterpret_cast<const uint4*>(wrows)[min(c0 + k * bd + tid, nch - 1)];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int c = c0 + k * bd + tid;
+        const int m = c / CPR, ch = c % CPR;
+        if (c < nch) kst[m * CPR + (ch ^ (m & (CPR - 1)))] = v[k];
+      }
+    }
+    if constexpr (DT == DT_E4M3) {
+      if (tid < W) ksc[tid] = p.kscale[base + tid];
+    }
   }
-  __syncthreads();
+  // chunk ch, word q, scale of window key m
+  auto chunk = [&](int m, int ch) -> uint4 {
+    if constexpr (STAGE) {
+      return kst[m * CPR + (ch ^ (m & (CPR - 1)))];
+    } else {
+      return reinterpret_cast<const uint4*>(wrows + (size_t)m * RB)[ch];
+    }
+  };
+  auto word = [&](int m, int q) -> uint32_t {
+    if constexpr (STAGE) {
+      return reinterpret_cast<const uint32_t*>(kst + m * CPR + ((q >> 2) ^ (m & (CPR - 1))))[q & 3];
+    } else {
+      return reinterpret_cast<const uint32_t*>(wrows + (size_t)m * RB)[q];
+    }
+  };
+  auto key_scale = [&](int m) -> float {
+    if constexpr (DT != DT_E4M3) return 1.0f;
+    else if constexpr (STAGE) return ksc[m];
+    else return p.kscale[base + m];
+  };
 
+  __syncthreads();
+  for (int idx = tid; idx < CS * QPR; idx += bd) {
+    const int c = idx / QPR, q = idx % QPR;
+    const int m = ((2 * c + 1) * W) / (2 * CS);
+    float x[DPW];
+    word_to_f32<DT>(word(m, q), x, key_scale(m));
+#pragma unroll
+    for (int e = 0; e < DPW; ++e) cent[c * D + q * DPW + e] = x[e];
+  }
+
+  // A cluster whose members did not change keeps the same mean, bit for bit, so its
+  // distances from the previous iteration still hold: distances and means are
+  // recomputed only for the clusters in s_dirty (all of them at first).
   int prev_a = tid < W ? -2 : -1;   // this key's assignment in the previous iteration
+  float acc[CS];                    // this key's distances, kept across iterations
+#pragma unroll
+  for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
+  if (tid == 0) s_dirty = (1u << CS) - 1u;
+  __syncthreads();
   for (int it = 0; it < p.iters; ++it) {
+    int a = -1;   // this key's cluster in this iteration
     if (p.positional) {
       // ---- position blocks: no distances, the means below are the centroids ----
-      if (tid < W) asg[tid] = tid / (W / CS);
-      __syncthreads();
+      if (tid < W) a = tid / (W / CS);
     } else {
-      // ---- distances to every centroid, nearest ----
-      float acc[CS];
-#pragma unroll
-      for (int c = 0; c < CS; ++c) acc[c] = 0.0f;
-      int best = 0;
+      // ---- distances to the changed centroids, nearest ----
+      const uint32_t dirty = s_dirty;
+      int tgt = 0;
       if (tid < W) {
-        const uint8_t* row = p.keys + (size_t)(base + tid) * RB;
-        float sk = 1.0f;
-        if constexpr (DT == DT_E4M3) sk = p.kscale[base + tid];
-        for (int i0 = 0; i0 < D; i0 += EPC) {
-          const uint4 raw = *reinterpret_cast<const uint4*>(row + i0 * Elem<DT>::bytes);
+        const float sk = key_scale(tid);
+#pragma unroll
+        for (int c = 0; c < CS; ++c)
+          if ((dirty >> c) & 1u) acc[c] = 0.0f;
+        for (int ch = 0; ch < CPR; ++ch) {
+          const uint4 raw = chunk(tid, ch);
           const uint32_t wds[4] = {raw.x, raw.y, raw.z, raw.w};
+          float xv[EPC];
+          chunk_to_f32<DT>(wds, xv, sk);
 #pragma unroll
-          for (int e = 0; e < EPC; ++e) {
-            float xi;
-            if constexpr (DT == DT_F32) {
-              xi = __uint_as_float(wds[e]);
-            } else if constexpr (DT == DT_BF16) {
-              xi = bf16_to_f32((wds[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
-            } else {
-              xi = e4m3_to_f32((wds[e >> 2] >> (8 * (e & 3))) & 0xFFu) * sk;
-            }
+          for (int c = 0; c < CS; ++c) {
+            if (!((dirty >> c) & 1u)) continue;
+            float s = acc[c];
 #pragma unroll
-            for (int c = 0; c < CS; ++c) {
-              const float t = xi - cent[c * D + i0 + e];
-              acc[c] = acc[c] + t * t;
+            for (int e = 0; e < EPC; ++e) {
+              const float t = xv[e] - cent[c * D + ch * EPC + e];
+              s = s + t * t;
             }
+            acc[c] = s;
           }
         }
+        float bv = acc[0];
 #pragma unroll
         for (int c = 1; c < CS; ++c)
-          if (acc[c] < acc[best]) best = c;
+          if (acc[c] < bv) bv = acc[c], tgt = c;
       }
-      if (tid < CS) cnt[tid] = 0;
-      if (tid == 0) s_over = 0;
-      __syncthreads();
-      if (tid < W) atomicAdd(&cnt[best], 1);
-      __syncthreads();
-      if (tid < CS && cnt[tid] > cap) s_over = 1;
-      __syncthreads();
-
-      if (!s_over) {
-        if (tid < W) asg[tid] = best;
-      } else {
-        // ---- greedy walk over all (D, key, cluster) triples ----
-        const int ntr = W * CS;
-        const int P2 = next_pow2(ntr);
-        if (tid < W) {
-#pragma unroll
-          for (int c = 0; c < CS; ++c)
-            sortbuf[tid * CS + c] = ((uint64_t)__float_as_uint(acc[c]) << 32) | (uint32_t)(tid * CS + c);
-        }
-        for (int i = ntr + tid; i < P2; i += bd) sortbuf[i] = ~0ull;
-        for (int j = tid; j < W; j += bd) {
-          asg[j] = -1;
-          first_lane[j] = 64;
-        }
+      auto count_targets = [&]() {
         if (tid < CS) cnt[tid] = 0;
+        if (tid == 0) s_over = 0;
         __syncthreads();
-        bitonic_sort_asc(sortbuf, P2);
-        if (tid < 64) {
-          int placed = 0;
-          for (int st = 0; st < ntr && placed < W; st += 64) {
-            const int ti = st + lane;
-            const bool valid = ti < ntr;
-            const uint32_t id = valid ? (uint32_t)sortbuf[ti] : 0u;
-            const int j = (int)(id / CS), c = (int)(id % CS);
-            const bool elig = valid && asg[j] < 0 && cnt[c] < cap;
-            bool conflict = false;
-#pragma unroll
-            for (int cc = 0; cc < CS; ++cc) {
-              const int pend = __popcll(__ballot(elig && c == cc));
-              const int have = cnt[cc];
-              if (have < cap && have + pend > cap) conflict = true;
-            }
-            if (!conflict) {
-              if (elig) atomicMin(&first_lane[j], lane);
-              __builtin_amdgcn_wave_barrier();
-              const bool win = elig && first_lane[j] == lane;
-              __builtin_amdgcn_wave_barrier();
-              if (elig) first_lane[j] = 64;
-              if (win) asg[j] = c;
-#pragma unroll
-              for (int cc = 0; cc < CS; ++cc) {
-                const int add = __popcll(__ballot(win && c == cc));
-                if (lane == 0) cnt[cc] += add;
-              }
-              placed += __popcll(__ballot(win));
-              __builtin_amdgcn_wave_barrier();
-            } else {
-              // a cluster fills inside this group: decide the 64 triples one by one in
-              // order, with the state in registers (lane cc holds cluster cc's count)
-              const bool free0 = valid && asg[j] < 0;
-              int hv = lane < CS ? cnt[lane] : 0;
-              bool taken = false, win = false;
-              for (int q = 0; q < 64; ++q) {
-                const int jq = __shfl(j, q), cq = __shfl(c, q);
-                const bool fq = __shfl((int)(free0 && !taken), q) != 0;
-                const bool ok = fq && __shfl(hv, cq) < cap;   // uniform across the wave
-                if (ok) {
-                  if (lane == q) win = true;
-                  if (j == jq) taken = true;
-                  if (lane == cq) hv += 1;
-                }
-              }
-              if (win) asg[j] = c;
-              if (lane < CS) cnt[lane] = hv;
-              placed += __popcll(__ballot(win));
-              __builtin_amdgcn_wave_barrier();
-            }
+        if (tid < W) atomicAdd(&cnt[tgt], 1);
+        __syncthreads();
+        if (tid < CS && cnt[tid] > cap) s_over = 1;
+        __syncthreads();
+      };
+      count_targets();
+
+      // ---- deferred acceptance while a cluster is over its cap.  Every key always
+      // targets one cluster; a key's proposal ranks in its cluster by (D, key). ----
+      uint32_t refused = 0;   // clusters that turned this key away
+      for (int round = 0; round < W * CS && s_over; ++round) {
+        if (tid == 0) {
+          int run = 0;
+          for (int c = 0; c < CS; ++c) {
+            plo[c] = run;
+            pfill[c] = 0;
+            if (cnt[c] > cap) run += cnt[c];
           }
         }
         __syncthreads();
+        const bool contested = tid < W && cnt[tgt] > cap;
+        float dt = acc[0];
+#pragma unroll
+        for (int c = 1; c < CS; ++c)
+          if (tgt == c) dt = acc[c];
+        const uint64_t v = ((uint64_t)__float_as_uint(dt) << 32) | (uint32_t)tid;
+        if (contested) prop[plo[tgt] + atomicAdd(&pfill[tgt], 1)] = v;
+        __syncthreads();
+        if (contested) {
+          const uint64_t* L = prop + plo[tgt];
+          const int n = cnt[tgt];
+          int ahead = 0;
+          for (int r = 0; r < n; ++r) ahead += L[r] < v ? 1 : 0;
+          if (ahead >= cap) {
+            // turned away: the next cluster in this key's (D, cluster) order
+            refused |= 1u << tgt;
+            int nb = -1;
+            float nv = 0.0f;
+#pragma unroll
+            for (int c = 0; c < CS; ++c)
+              if (!((refused >> c) & 1u) && (nb < 0 || acc[c] < nv)) nb = c, nv = acc[c];
+            if (nb >= 0) tgt = nb;
+          }
+        }
+        __syncthreads();
+        count_targets();
       }
+      if (tid < W) a = tgt;
     }
 
     // ---- stop at a fixed point: an unchanged assignment gives the same members and
     // means as the previous iteration, hence the same centroids and again the same
     // assignment, so the remaining iterations would change nothing ----
-    const int a = tid < W ? asg[tid] : -1;
+    if (tid == 0) s_dirty = 0u;
     if (!__syncthreads_or(a != prev_a)) break;
+    // clusters that gained or lost a member get a new mean (and new distances)
+    if (a != prev_a) atomicOr(&s_dirty, (a >= 0 ? 1u << a : 0u) | (prev_a >= 0 ? 1u << prev_a : 0u));
     prev_a = a;
 
     // ---- stable member lists: ascending position within each cluster ----
@@ -221,23 +269,44 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
     if (tid < W) member[clo[a] + wcnt[wv * CS + a] + myrank] = tid;
     __syncthreads();
 
-    // ---- means (empty clusters keep their centroid) ----
-    for (int idx = tid; idx < CS * D; idx += bd) {
-      const int c = idx / D, i = idx % D;
+    // ---- means of the changed clusters (empty clusters keep their centroid): one
+    // thread per (cluster, 32-bit word of a row) ----
+    const uint32_t dirty = s_dirty;
+    for (int idx = tid; idx < CS * QPR; idx += bd) {
+      const int c = idx / QPR, q = idx % QPR;
       const int nc = cnt[c];
-      if (nc > 0) {
+      if (nc > 0 && ((dirty >> c) & 1u)) {
         const int* mem = member + clo[c];
-        float s = 0.0f;
+        float s[DPW];
+#pragma unroll
+        for (int e = 0; e < DPW; ++e) s[e] = 0.0f;
         int r = 0;
         for (; r + 8 <= nc; r += 8) {
-          float v[8];
+          uint32_t wd[8];
+          float sk[8];
 #pragma unroll
-          for (int u = 0; u < 8; ++u) v[u] = key_value<DT, D>(p, base + mem[r + u], i);
+          for (int u = 0; u < 8; ++u) {
+            const int m = mem[r + u];
+            wd[u] = word(m, q);
+            sk[u] = key_scale(m);
+          }
 #pragma unroll
-          for (int u = 0; u < 8; ++u) s = s + v[u];
+          for (int u = 0; u < 8; ++u) {
+            float x[DPW];
+            word_to_f32<DT>(wd[u], x, sk[u]);
+#pragma unroll
+            for (int e = 0; e < DPW; ++e) s[e] = s[e] + x[e];
+          }
         }
-        for (; r < nc; ++r) s = s + key_value<DT, D>(p, base + mem[r], i);
-        cent[idx] = s / (float)nc;
+        for (; r < nc; ++r) {
+          const int m = mem[r];
+          float x[DPW];
+          word_to_f32<DT>(word(m, q), x, key_scale(m));
+#pragma unroll
+          for (int e = 0; e < DPW; ++e) s[e] = s[e] + x[e];
+        }
+#pragma unroll
+        for (int e = 0; e < DPW; ++e) cent[c * D + q * DPW + e] = s[e] / (float)nc;
       }
     }
     __syncthreads();
