@@ -71,7 +71,8 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   __shared__ uint32_t amax[CS];
   __shared__ int wcnt[16 * CS];
   __shared__ int member[SEAL_MAXW];
-  __shared__ uint64_t prop[SEAL_MAXW];
+  __shared__ float msc[DT == DT_E4M3 ? SEAL_MAXW : 1];   // member scales, in member order
+  __shared__ __align__(16) uint64_t prop[SEAL_MAXW + 8 * CS];
   __shared__ int s_over;
   __shared__ uint32_t s_dirty;
   const int tid = threadIdx.x, bd = blockDim.x, lane = tid & 63, wv = tid >> 6, nwv = bd >> 6;
@@ -191,12 +192,14 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
       // targets one cluster; a key's proposal ranks in its cluster by (D, key). ----
       uint32_t refused = 0;   // clusters that turned this key away
       for (int round = 0; round < W * CS && s_over; ++round) {
+        // each over-full cluster's proposals in a list of its own, padded to a multiple
+        // of 8 with entries that rank behind every proposal
         if (tid == 0) {
           int run = 0;
           for (int c = 0; c < CS; ++c) {
             plo[c] = run;
             pfill[c] = 0;
-            if (cnt[c] > cap) run += cnt[c];
+            if (cnt[c] > cap) run += (cnt[c] + 7) & ~7;
           }
         }
         __syncthreads();
@@ -207,12 +210,26 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
           if (tgt == c) dt = acc[c];
         const uint64_t v = ((uint64_t)__float_as_uint(dt) << 32) | (uint32_t)tid;
         if (contested) prop[plo[tgt] + atomicAdd(&pfill[tgt], 1)] = v;
+        if (tid < 8 * CS) {
+          const int c = tid >> 3, n = cnt[c];
+          if (n > cap && n + (tid & 7) < ((n + 7) & ~7)) prop[plo[c] + n + (tid & 7)] = ~0ull;
+        }
         __syncthreads();
         if (contested) {
-          const uint64_t* L = prop + plo[tgt];
-          const int n = cnt[tgt];
+          // proposals ahead of this one in (D, key) order, 8 per step
+          const uint4* L = reinterpret_cast<const uint4*>(prop + plo[tgt]);
+          const int n8 = (cnt[tgt] + 7) >> 3;
           int ahead = 0;
-          for (int r = 0; r < n; ++r) ahead += L[r] < v ? 1 : 0;
+          for (int r = 0; r < n8; ++r) {
+            uint4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = L[4 * r + u];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              ahead += ((((uint64_t)x[u].y << 32) | x[u].x) < v) ? 1 : 0;
+              ahead += ((((uint64_t)x[u].w << 32) | x[u].z) < v) ? 1 : 0;
+            }
+          }
           if (ahead >= cap) {
             // turned away: the next cluster in this key's (D, cluster) order
             refused |= 1u << tgt;
@@ -266,7 +283,11 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
       }
     }
     __syncthreads();
-    if (tid < W) member[clo[a] + wcnt[wv * CS + a] + myrank] = tid;
+    if (tid < W) {
+      const int r = clo[a] + wcnt[wv * CS + a] + myrank;
+      member[r] = tid;
+      if constexpr (DT == DT_E4M3) msc[r] = key_scale(tid);
+    }
     __syncthreads();
 
     // ---- means of the changed clusters (empty clusters keep their centroid): one
@@ -286,9 +307,9 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
           float sk[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            const int m = mem[r + u];
-            wd[u] = word(m, q);
-            sk[u] = key_scale(m);
+            wd[u] = word(mem[r + u], q);
+            if constexpr (DT == DT_E4M3) sk[u] = msc[clo[c] + r + u];
+            else sk[u] = 1.0f;
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -299,9 +320,8 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
           }
         }
         for (; r < nc; ++r) {
-          const int m = mem[r];
           float x[DPW];
-          word_to_f32<DT>(word(m, q), x, key_scale(m));
+          word_to_f32<DT>(word(mem[r], q), x, DT == DT_E4M3 ? msc[clo[c] + r] : 1.0f);
 #pragma unroll
           for (int e = 0; e < DPW; ++e) s[e] = s[e] + x[e];
         }
