@@ -304,32 +304,43 @@ int idx_route_topk_pos(idx_index* ix, const void* q, const float* q_scale, const
 /* Exhaustive selection, the method's baseline and the reference answer for recall
  * (paper-daily explainer, "它到底在解决什么问题？": the indexer scores every earlier
  * key and keeps the top k).
- * Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass. */
+ * Workspace bytes idx_exhaustive_topk needs to handle `T` queries in one pass, for
+ * every format and every k: per query one row of sample scores (one key in 64 of
+ * the prefix, at most 16384) and a list of up to 16384 survivors, plus the sample's
+ * rows and room for one full fp32 score row. */
 int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T);
 
 /* Exhaustive top-k (stateless): query t at position q_pos0 + t scores keys
- * [0, q_pos0 + t] of `keys` and keeps the top k.
+ * [0, q_pos0 + t] of `keys` and keeps the top k (score descending, ties to the lower
+ * position; a prefix shorter than k pads with -1 / -inf).
  *   keys: device [n_keys, d]; k_scale: device [n_keys] for E4M3 else NULL;
- *   q, q_scale, w as in idx_route_topk; q_pos0 + T <= n_keys; 1 <= k <= 4096.
+ *   q, q_scale, w as in idx_route_topk; q_pos0 + T <= n_keys, q_pos0 + T < 2^31;
+ *   1 <= k <= 4096.
  *   workspace: device scratch of workspace_bytes >= idx_exhaustive_workspace_bytes(n_keys, 1);
  *   queries are processed in as many passes as the workspace requires.
- * Scores are bit-identical to the rescoring of idx_route_topk for the same (q, k). */
+ * No score row is written in the common case: a sample of the keys sets a threshold
+ * per query, the full pass keeps only the scores at or above it, and those are
+ * sorted.  A query whose survivors are fewer than min(k, prefix) or more than the
+ * survivor list holds (heavy exact ties, for instance) is redone through a full
+ * score row.  The call waits for `stream` once per pass, to read how many queries
+ * need that.  Scores are bit-identical to the rescoring of idx_route_topk for the
+ * same (q, k). */
 int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
                         int32_t dim, const void* q, const float* q_scale, const float* w, int64_t q_pos0,
                         int32_t T, int32_t k, int32_t* topk_idx, float* topk_score, void* workspace,
                         int64_t workspace_bytes, void* stream);
 
-/* idx_exhaustive_topk for callers that cannot allocate device memory (code under
- * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
- * kernels and the same results, bit for bit, with the score rows kept in a device
- * array that the library holds on every GPU it runs on, IDX_NOALLOC_SCRATCH_BYTES
- * per GPU, until the process ends.  The call allocates nothing.  Queries run in
- * passes of as many score rows (round_up(q_pos0 + T, 64) fp32 each) as the array
- * holds.  Every call on one GPU shares that GPU's array: calls that overlap on one
- * GPU (other streams, other threads) race and must be ordered by the caller.
- * Errors: as idx_exhaustive_topk, and ECAPACITY when a single score row exceeds
- * the array (q_pos0 + T > 33,554,432 keys); EDEVICE if the array's address cannot
- * be obtained. */
+/* idx_exhaustive_topk for callers that cannot allocate device memory (tight serving
+ * loops, harnesses that forbid hipMalloc): the same kernels and the same results,
+ * bit for bit, with the workspace kept in a device array that the library holds on
+ * every GPU it runs on, IDX_NOALLOC_SCRATCH_BYTES per GPU, until the process ends.
+ * The call allocates nothing; like idx_exhaustive_topk it waits for `stream` once
+ * per pass.  Queries run in passes of as many as the array holds.  Every call on one
+ * GPU shares that GPU's array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.
+ * Errors: as idx_exhaustive_topk, and ECAPACITY when one query's pass exceeds the
+ * array (prefixes beyond about 31 million keys: the fallback's full fp32 score row
+ * is the largest part); EDEVICE if the array's address cannot be obtained. */
 #define IDX_NOALLOC_SCRATCH_BYTES (128ll << 20)
 int idx_exhaustive_topk_noalloc(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype,
                                 int32_t heads, int32_t dim, const void* q, const float* q_scale, const float* w,

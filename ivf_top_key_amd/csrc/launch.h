@@ -8,8 +8,12 @@
 
 namespace ivftk {
 
-hipError_t launch_exh_score(const ExhParams& p, int dtype, int dim, int ht, int64_t n_max, hipStream_t s);
+enum { EXH_ROWS = 0, EXH_SAMPLE = 1, EXH_STREAM = 2 };
+hipError_t launch_exh_score(const ExhParams& p, int mode, int dtype, int dim, int ht, int64_t n_max, hipStream_t s);
 hipError_t launch_topk_rows(const ExhParams& p, hipStream_t s);
+hipError_t launch_exh_gather(const ExhParams& p, int rb, int64_t ns, hipStream_t s);
+hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s);
+hipError_t launch_exh_finalize(const ExhParams& p, hipStream_t s);
 hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s);
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s);
 hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s);

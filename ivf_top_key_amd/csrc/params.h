@@ -104,13 +104,26 @@ struct ExhParams {
   int H;
   int64_t q_pos0;
   int t0;              // first query of this pass
-  int Tb;              // queries in this pass
-  float* ws;           // [Tb, ld] scores
+  int Tb;              // query rows in this pass
+  const int* tlist;    // row tl is query t0 + tlist[tl] (null: t0 + tl)
+  float* ws;           // [Tb, ld] scores (materialized rows)
   int64_t ld;
   int kchunk;          // keys per block of the score kernel
   int k;
   int* topk_idx;       // [T, k] (row t0 + tl)
   float* topk_score;
+  // streamed selection
+  int stride, soff;    // sample: keys soff, soff + stride, soff + 2 stride, ...
+  const uint8_t* skeys;   // the sample's rows, dense
+  const float* sscale;
+  float* srow;         // [Tb, sld] sample scores
+  int64_t sld;
+  int aim;             // survivors a threshold aims at
+  uint32_t* tau;       // [Tb] order-key threshold
+  int* cnt;            // [Tb] scores at or above tau (all of them, also past caps)
+  uint64_t* surv;      // [Tb, caps] composites of the survivors
+  int caps;
+  int* failed;         // [1 + Tb]: count, then the rows the fallback handles
 };
 
 // Seal of windows [w0, w0 + gridDim.x).

@@ -729,36 +729,130 @@ int exhaustive_check(const void* keys, const float* k_scale, int64_t n_keys, int
   if (k < 1 || k > 4096) return fail(IDX_EINVAL, "k must be 1..4096");
   if (q_pos0 < 0) return fail(IDX_EINVAL, "q_pos0 must be >= 0");
   if (q_pos0 + T > n_keys) return fail(IDX_ECAUSAL, "query position beyond n_keys");
+  if (q_pos0 + T > INT32_MAX) return fail(IDX_EINVAL, "positions must fit in int32");
   return IDX_OK;
 }
 
-// The exhaustive passes: as many queries per pass as `ws_bytes` of score rows hold.
+// Layout of an exhaustive workspace (byte offsets from its start, 256-aligned):
+//   [failed list: 1 + Tb ints][sample rows][sample scales]            per call
+//   [sample scores: Tb x sld][tau: Tb][count: Tb][survivors: Tb x caps]  per pass
+// The fallback's score rows reuse everything from the sample scores on.
+struct ExhPlan {
+  int stride = 64, soff = 32, caps = 8192, aim = 0;
+  int64_t ns = 0, sld = 0, ld = 0;
+  int64_t off_skeys = 0, off_sscale = 0, off_srow = 0, off_tau = 0, off_cnt = 0, off_surv = 0, end = 0;
+};
+
+int64_t align256(int64_t x) { return round_up(x, 256); }
+
+// n_all: the longest prefix of the call; rb: bytes per key row; Tb: rows per pass.
+ExhPlan exh_plan(int64_t n_all, int k, int rb, int64_t Tb) {
+  ExhPlan pl;
+  pl.stride = (int)std::max<int64_t>(64, (n_all + 16383) / 16384);   // at most 16384 sample keys
+  pl.soff = pl.stride / 2;
+  pl.caps = k > 2048 ? 16384 : 8192;
+  pl.aim = (int)std::min<int64_t>(std::max<int64_t>(2ll * k, 32ll * pl.stride), pl.caps / 2);
+  pl.ns = n_all > pl.soff ? (n_all - pl.soff + pl.stride - 1) / pl.stride : 0;
+  pl.sld = round_up(std::max<int64_t>(pl.ns, 1), 64);
+  pl.ld = round_up(n_all, 64);
+  pl.off_skeys = align256((1 + Tb) * 4);
+  pl.off_sscale = pl.off_skeys + align256(pl.ns * rb);
+  pl.off_srow = pl.off_sscale + align256(pl.ns * 4);
+  pl.off_tau = pl.off_srow + align256(Tb * pl.sld * 4);
+  pl.off_cnt = pl.off_tau + align256(Tb * 4);
+  pl.off_surv = pl.off_cnt + align256(Tb * 4);
+  pl.end = std::max(pl.off_surv + Tb * pl.caps * 8, pl.off_srow + pl.ld * 4);   // room for one fallback row
+  return pl;
+}
+
+// Bytes a pass of Tb rows needs (the sizes the workspace query promises cover every
+// format and k: 512-byte rows, 16384 survivors).
+int64_t exh_bytes(int64_t n_all, int k, int rb, int64_t Tb) { return exh_plan(n_all, k, rb, Tb).end; }
+
+// The exhaustive passes: as many queries per pass as `ws_bytes` hold (exh_plan).  After
+// each pass the call reads how many rows need the fallback (a wait on the stream);
+// those run through materialized score rows, as many at a time as the workspace
+// holds.
 int exhaustive_passes(const void* keys, const float* k_scale, int32_t dtype, int32_t heads, int32_t dim, const void* q,
                       const float* q_scale, const float* w, int64_t q_pos0, int32_t T, int32_t k, int32_t* topk_idx,
-                      float* topk_score, float* ws, int64_t ws_bytes, hipStream_t s) {
-  const int64_t ld = round_up(q_pos0 + T, 64);
-  const int Tb_max = (int)std::min<int64_t>(T, ws_bytes / (ld * (int64_t)sizeof(float)));
-  for (int t0 = 0; t0 < T; t0 += Tb_max) {
-    ExhParams p{};
-    p.keys = static_cast<const uint8_t*>(keys);
-    p.kscale = dtype == IDX_E4M3 ? k_scale : nullptr;
-    p.q = static_cast<const uint8_t*>(q);
-    p.qscale = dtype == IDX_E4M3 ? q_scale : nullptr;
-    p.w = w;
-    p.H = heads;
-    p.q_pos0 = q_pos0;
+                      float* topk_score, void* ws, int64_t ws_bytes, hipStream_t s) {
+  const int64_t n_all = q_pos0 + T;
+  const int rb = dim * elem_bytes(dtype);
+  int64_t Tb_max = T;
+  while (Tb_max > 1 && exh_bytes(n_all, k, rb, Tb_max) > ws_bytes) Tb_max = std::max<int64_t>(1, Tb_max / 2);
+  if (exh_bytes(n_all, k, rb, Tb_max) > ws_bytes)
+    return fail(IDX_EINVAL, "workspace too small: %lld bytes, need >= %lld", (long long)ws_bytes,
+                (long long)exh_bytes(n_all, k, rb, 1));
+  while (Tb_max < T && exh_bytes(n_all, k, rb, Tb_max + 1) <= ws_bytes) ++Tb_max;   // grow back after halving
+  const ExhPlan pl = exh_plan(n_all, k, rb, Tb_max);
+  uint8_t* const wb = static_cast<uint8_t*>(ws);
+  int* const failed = reinterpret_cast<int*>(wb);
+  const int HT = head_tiles(heads);
+  auto dev_fail = [&](hipError_t e) { return fail(IDX_EDEVICE, "exhaustive launch: %s", hipGetErrorString(e)); };
+
+  ExhParams p{};
+  p.keys = static_cast<const uint8_t*>(keys);
+  p.kscale = dtype == IDX_E4M3 ? k_scale : nullptr;
+  p.q = static_cast<const uint8_t*>(q);
+  p.qscale = dtype == IDX_E4M3 ? q_scale : nullptr;
+  p.w = w;
+  p.H = heads;
+  p.q_pos0 = q_pos0;
+  p.kchunk = 8192;
+  p.k = k;
+  p.topk_idx = topk_idx;
+  p.topk_score = topk_score;
+  p.stride = pl.stride;
+  p.soff = pl.soff;
+  p.skeys = wb + pl.off_skeys;
+  p.sscale = reinterpret_cast<const float*>(wb + pl.off_sscale);
+  p.srow = reinterpret_cast<float*>(wb + pl.off_srow);
+  p.sld = pl.sld;
+  p.aim = pl.aim;
+  p.tau = reinterpret_cast<uint32_t*>(wb + pl.off_tau);
+  p.cnt = reinterpret_cast<int*>(wb + pl.off_cnt);
+  p.surv = reinterpret_cast<uint64_t*>(wb + pl.off_surv);
+  p.caps = pl.caps;
+  p.failed = failed;
+  std::vector<int> rows;
+  for (int t0 = 0; t0 < T; t0 += (int)Tb_max) {
     p.t0 = t0;
-    p.Tb = std::min(Tb_max, T - t0);
-    p.ws = ws;
-    p.ld = ld;
-    p.kchunk = 8192;
-    p.k = k;
-    p.topk_idx = topk_idx;
-    p.topk_score = topk_score;
+    p.Tb = (int)std::min<int64_t>(Tb_max, T - t0);
+    p.tlist = nullptr;
     const int64_t n_batch = q_pos0 + t0 + p.Tb;
-    hipError_t e = launch_exh_score(p, dtype, dim, head_tiles(heads), n_batch, s);
-    if (e == hipSuccess) e = launch_topk_rows(p, s);
-    if (e != hipSuccess) return fail(IDX_EDEVICE, "exhaustive launch: %s", hipGetErrorString(e));
+    const int64_t ns_batch = n_batch > pl.soff ? (n_batch - pl.soff + pl.stride - 1) / pl.stride : 0;
+    // the sample rows are gathered again each pass: a fallback overwrites nothing
+    // before them, but one pass's gather covers only its own prefixes
+    hipError_t e = launch_exh_gather(p, rb, ns_batch, s);
+    if (e == hipSuccess && ns_batch > 0) e = launch_exh_score(p, EXH_SAMPLE, dtype, dim, HT, ns_batch, s);
+    if (e == hipSuccess) e = launch_exh_threshold(p, s);
+    if (e == hipSuccess) e = launch_exh_score(p, EXH_STREAM, dtype, dim, HT, n_batch, s);
+    if (e == hipSuccess) e = launch_exh_finalize(p, s);
+    if (e != hipSuccess) return dev_fail(e);
+    int n_failed = 0;
+    e = hipMemcpyAsync(&n_failed, failed, sizeof(int), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return dev_fail(e);
+    if (n_failed <= 0) continue;
+    // ---- fallback: the listed rows through materialized score rows, in position order ----
+    rows.assign(n_failed, 0);
+    e = hipMemcpy(rows.data(), failed + 1, (size_t)n_failed * sizeof(int), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return dev_fail(e);
+    std::sort(rows.begin(), rows.end());
+    e = hipMemcpy(failed + 1, rows.data(), (size_t)n_failed * sizeof(int), hipMemcpyHostToDevice);
+    if (e != hipSuccess) return dev_fail(e);
+    const int per = (int)std::max<int64_t>(1, (ws_bytes - pl.off_srow) / (pl.ld * 4));
+    ExhParams f = p;
+    f.ws = reinterpret_cast<float*>(wb + pl.off_srow);
+    f.ld = pl.ld;
+    for (int r0 = 0; r0 < n_failed; r0 += per) {
+      f.tlist = failed + 1 + r0;
+      f.Tb = std::min(per, n_failed - r0);
+      const int64_t n_rows = q_pos0 + t0 + rows[r0 + f.Tb - 1] + 1;
+      e = launch_exh_score(f, EXH_ROWS, dtype, dim, HT, n_rows, s);
+      if (e == hipSuccess) e = launch_topk_rows(f, s);
+      if (e != hipSuccess) return dev_fail(e);
+    }
   }
   return IDX_OK;
 }
@@ -769,7 +863,7 @@ extern "C" {
 
 int64_t idx_exhaustive_workspace_bytes(int64_t n_keys, int32_t T) {
   if (n_keys < 1 || T < 1) return 0;
-  return (int64_t)T * round_up(n_keys, 64) * (int64_t)sizeof(float);
+  return exh_bytes(n_keys, 4096, 512, T);
 }
 
 int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
@@ -780,11 +874,8 @@ int idx_exhaustive_topk(const void* keys, const float* k_scale, int64_t n_keys, 
   if (int e = exhaustive_check(keys, k_scale, n_keys, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx))
     return e;
   if (!workspace) return fail(IDX_EINVAL, "null pointer argument");
-  const int64_t per_query = round_up(q_pos0 + T, 64) * (int64_t)sizeof(float);
-  if (workspace_bytes < per_query) return fail(IDX_EINVAL, "workspace too small: %lld bytes, need >= %lld",
-                                               (long long)workspace_bytes, (long long)per_query);
   return exhaustive_passes(keys, k_scale, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx, topk_score,
-                           static_cast<float*>(workspace), workspace_bytes, (hipStream_t)stream);
+                           workspace, workspace_bytes, (hipStream_t)stream);
 }
 
 int idx_exhaustive_topk_noalloc(const void* keys, const float* k_scale, int64_t n_keys, int32_t dtype, int32_t heads,
@@ -793,10 +884,10 @@ int idx_exhaustive_topk_noalloc(const void* keys, const float* k_scale, int64_t 
   g_err.clear();
   if (int e = exhaustive_check(keys, k_scale, n_keys, dtype, heads, dim, q, q_scale, w, q_pos0, T, k, topk_idx))
     return e;
-  const int64_t per_query = round_up(q_pos0 + T, 64) * (int64_t)sizeof(float);
-  if (per_query > (int64_t)IDX_NOALLOC_SCRATCH_BYTES)
-    return fail(IDX_ECAPACITY, "a score row of %lld keys (%lld bytes) exceeds the %lld-byte scratch array",
-                (long long)(q_pos0 + T), (long long)per_query, (long long)IDX_NOALLOC_SCRATCH_BYTES);
+  const int64_t need = exh_bytes(q_pos0 + T, k, dim * elem_bytes(dtype), 1);
+  if (need > (int64_t)IDX_NOALLOC_SCRATCH_BYTES)
+    return fail(IDX_ECAPACITY, "a pass over %lld keys needs %lld bytes, more than the %lld-byte scratch array",
+                (long long)(q_pos0 + T), (long long)need, (long long)IDX_NOALLOC_SCRATCH_BYTES);
   int dev = 0;
   float* ws = scratch_on_current_device(&dev);
   if (!ws) return IDX_EDEVICE;

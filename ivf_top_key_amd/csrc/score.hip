@@ -1,5 +1,6 @@
-// Indexer scoring kernels: exhaustive scores, representative scores, candidate
-// rescoring with the top-k selection, and the top-k of exhaustive score rows.
+// Indexer scoring kernels: exhaustive scores (streamed, and in rows for the
+// fallback), representative scores, candidate rescoring with the top-k selection,
+// and the top-k of exhaustive score rows.
 //
 // Score (AttentionIndex, paper-daily.com explainer, "它到底在解决什么问题？"):
 //   s(t, j) = sum_h w[t,h] * ReLU(q[t,h] . k[j]); with E4M3, the per-(t,h) query
@@ -13,54 +14,200 @@
 namespace ivftk {
 
 // ---------------------------------------------------------------------------
-// exhaustive scores: block = 4 waves = 4 queries, one chunk of keys
+// exhaustive scores: block = 4 waves = 4 query rows, one chunk of keys
 // ---------------------------------------------------------------------------
 // Three waves per SIMD where a half row fits in 16 registers (E4M3 and bf16 at d = 64,
 // fp32 at d = 32) and there are at most 64 heads; otherwise the compiler's choice.
 template <int DT, int D, int HT>
 constexpr int score_waves() { return (Geo<DT, D>::HW <= 16 && HT <= 2) ? 3 : 1; }
 
-template <int DT, int D, int HT>
+// Query of row r of a pass.
+__device__ __forceinline__ int exh_query(const ExhParams& p, int r) { return p.t0 + (p.tlist ? p.tlist[r] : r); }
+
+// Keys of the scored run that query t sees: its prefix, or (EXH_SAMPLE) the sample
+// keys inside its prefix.
+template <int MODE>
+__device__ __forceinline__ int64_t exh_run_len(const ExhParams& p, int t) {
+  const int64_t n = p.q_pos0 + t + 1;
+  if constexpr (MODE == EXH_SAMPLE) return n > p.soff ? (n - p.soff + p.stride - 1) / p.stride : 0;
+  else return n;
+}
+
+// EXH_ROWS: score rows into p.ws; EXH_SAMPLE: the sample's scores into p.srow;
+// EXH_STREAM: no rows, only the scores at or above the row's threshold p.tau[tl]
+// (with their positions) into p.surv, counted in p.cnt.
+template <int DT, int D, int HT, int MODE>
 __global__ __launch_bounds__(256, (score_waves<DT, D, HT>())) void k_exh_score(ExhParams p) {
   using G = Geo<DT, D>;
-  using S = Stage<DT, D>;
   __shared__ float wq_s[4][HT * 32];
   __shared__ StageLds<DT, D> stage;
-  const int wave = threadIdx.x >> 6;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int tl = blockIdx.x * 4 + wave;
   const bool active = tl < p.Tb;
-  const int tc = p.t0 + (active ? tl : p.Tb - 1);   // idle waves still stage rows
+  const int tr = active ? tl : p.Tb - 1;   // idle waves still stage rows
+  const int tc = exh_query(p, tr);
   load_query_weights<HT>(wq_s[wave], p.w + (size_t)tc * p.H, p.qscale ? p.qscale + (size_t)tc * p.H : nullptr, p.H);
   // the block's rows: keys [j0, j1) with j1 bounded by its longest prefix
-  const int t_last = p.t0 + min(blockIdx.x * 4 + 3, p.Tb - 1);
+  int64_t n_max = 0;
+  for (int u = 0; u < 4; ++u) {
+    const int64_t n = exh_run_len<MODE>(p, exh_query(p, min((int)blockIdx.x * 4 + u, p.Tb - 1)));
+    n_max = n > n_max ? n : n_max;
+  }
   const int64_t j0 = (int64_t)blockIdx.y * p.kchunk;
-  const int64_t n_max = p.q_pos0 + t_last + 1;
   const int64_t j1 = (j0 + p.kchunk < n_max) ? j0 + p.kchunk : n_max;
   __syncthreads();
   if (j0 >= j1) return;
-  const int64_t n_own = p.q_pos0 + tc + 1;
+  const int64_t n_own = exh_run_len<MODE>(p, tc);
   const int64_t j_end = active ? (j1 < n_own ? j1 : n_own) : j0;
   QueryFrag<DT, D, HT> f;
   load_query<DT, D, HT>(f, p.q + (size_t)tc * p.H * G::RB, p.H);
   load_query_wregs<DT, D, HT>(f, wq_s[wave]);
-  float* out = p.ws + (size_t)(active ? tl : 0) * p.ld;
-  score_staged<DT, D, HT, 4>(
-      f, p.keys + (size_t)j0 * G::RB, DT == DT_E4M3 ? p.kscale + j0 : nullptr, (int)(j1 - j0), stage,
-      [&](int i, float x) {
-        const int64_t j = j0 + i;
-        if (j < j_end) out[j] = x;
-      });
+  const uint8_t* run = MODE == EXH_SAMPLE ? p.skeys : p.keys;
+  const float* rsc = MODE == EXH_SAMPLE ? p.sscale : p.kscale;
+  const uint8_t* base = run + (size_t)j0 * G::RB;
+  const float* scl = DT == DT_E4M3 ? rsc + j0 : nullptr;
+  if constexpr (MODE == EXH_STREAM) {
+    const uint32_t tau = p.tau[tr];
+    int* const cnt = p.cnt + tr;
+    uint64_t* const sv = p.surv + (size_t)tr * p.caps;
+    const int caps = p.caps;
+    score_staged<DT, D, HT, 4>(f, base, scl, (int)(j1 - j0), stage, [&](int i, float x) {
+      const int64_t j = j0 + i;
+      const bool take = j < j_end && order_bits(x) >= tau;
+      const uint64_t m = __ballot(take);
+      if (m != 0ull) {   // rare: one atomic per wave for all of its lanes' survivors
+        const int leader = __builtin_ctzll(m);
+        int b = 0;
+        if (lane == leader) b = atomicAdd(cnt, __popcll(m));
+        b = __shfl(b, leader);
+        const int at = b + __popcll(m & ((1ull << lane) - 1ull));
+        if (take && at < caps) sv[at] = make_comp(x, (uint32_t)j);
+      }
+    });
+  } else {
+    float* out = MODE == EXH_SAMPLE ? p.srow + (size_t)tr * p.sld : p.ws + (size_t)tr * p.ld;
+    score_staged<DT, D, HT, 4>(f, base, scl, (int)(j1 - j0), stage, [&](int i, float x) {
+      const int64_t j = j0 + i;
+      if (j < j_end) out[j] = x;
+    });
+  }
 }
 
 template <int DT, int D, int HT>
-static hipError_t launch_exh_score_t(const ExhParams& p, int64_t n_max, hipStream_t s) {
+static hipError_t launch_exh_score_t(const ExhParams& p, int mode, int64_t n_max, hipStream_t s) {
   dim3 grid((p.Tb + 3) / 4, (unsigned)((n_max + p.kchunk - 1) / p.kchunk));
-  hipLaunchKernelGGL((k_exh_score<DT, D, HT>), grid, dim3(256), 0, s, p);
+  if (mode == EXH_SAMPLE) hipLaunchKernelGGL((k_exh_score<DT, D, HT, EXH_SAMPLE>), grid, dim3(256), 0, s, p);
+  else if (mode == EXH_STREAM) hipLaunchKernelGGL((k_exh_score<DT, D, HT, EXH_STREAM>), grid, dim3(256), 0, s, p);
+  else hipLaunchKernelGGL((k_exh_score<DT, D, HT, EXH_ROWS>), grid, dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
-hipError_t launch_exh_score(const ExhParams& p, int dtype, int dim, int ht, int64_t n_max, hipStream_t s) {
-  IVFTK_DISPATCH(launch_exh_score_t, dtype, dim, ht, p, n_max, s);
+hipError_t launch_exh_score(const ExhParams& p, int mode, int dtype, int dim, int ht, int64_t n_max, hipStream_t s) {
+  IVFTK_DISPATCH(launch_exh_score_t, dtype, dim, ht, p, mode, n_max, s);
+}
+
+// ---------------------------------------------------------------------------
+// streamed exhaustive selection
+// ---------------------------------------------------------------------------
+// The top k of a row are found without writing the row: (1) every stride-th key (the
+// sample) is scored; (2) a threshold tau per row is read off the sample, at the rank
+// where about `aim` (>= 2k) scores of the whole row are expected to reach it; (3) the
+// full scoring pass keeps only the scores >= tau, with their positions, and counts
+// them; (4) a row with at least min(k, prefix) and at most caps such scores holds its
+// whole answer among them (every score above the k-th, and every tie with it, reaches
+// tau), which is sorted; any other row goes to the fallback, which materializes the
+// row and selects from it.  A prefix of at most caps keys takes tau = 0 (all keys).
+
+// The sample's rows (and scales) in one dense run: sample s is key soff + s * stride.
+__global__ __launch_bounds__(256) void k_exh_gather(ExhParams p, int rb, int64_t ns, uint8_t* srows, float* sscale) {
+  const int cpr = rb / 16;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t smp = idx / cpr;
+  if (smp >= ns) return;
+  const int c = (int)(idx % cpr);
+  const int64_t pos = p.soff + smp * p.stride;
+  reinterpret_cast<uint4*>(srows + (size_t)smp * rb)[c] = reinterpret_cast<const uint4*>(p.keys + (size_t)pos * rb)[c];
+  if (p.kscale && c == 0) sscale[smp] = p.kscale[pos];
+}
+
+hipError_t launch_exh_gather(const ExhParams& p, int rb, int64_t ns, hipStream_t s) {
+  if (ns <= 0) return hipSuccess;
+  const int64_t threads = ns * (rb / 16);
+  hipLaunchKernelGGL(k_exh_gather, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, p, rb, ns,
+                     const_cast<uint8_t*>(p.skeys), const_cast<float*>(p.sscale));
+  return hipGetLastError();
+}
+
+constexpr int EXH_SAMPLE_CAP = 16384;   // sample scores one threshold block holds
+
+// tau of each row of the pass (one block per row); clears the row's count and, in
+// block 0, the fallback list.
+__global__ __launch_bounds__(1024) void k_exh_threshold(ExhParams p) {
+  __shared__ uint32_t sk[EXH_SAMPLE_CAP];
+  __shared__ Select32Scratch sc;
+  const int tl = blockIdx.x, tid = threadIdx.x;
+  const int t = exh_query(p, tl);
+  const int64_t n = p.q_pos0 + t + 1;
+  const int64_t ns = exh_run_len<EXH_SAMPLE>(p, t);
+  if (tid == 0) {
+    p.cnt[tl] = 0;
+    if (tl == 0) p.failed[0] = 0;
+  }
+  uint32_t tau = 0u;
+  if (n > p.caps && ns > 0 && ns <= EXH_SAMPLE_CAP) {
+    // about aim of the n scores reach the sample's r-th largest
+    const int64_t r = ((int64_t)p.aim * ns + n - 1) / n;
+    if (r <= ns) {
+      const float* row = p.srow + (size_t)tl * p.sld;
+      for (int64_t i = tid; i < ns; i += blockDim.x) sk[i] = order_bits(row[i]);
+      __syncthreads();
+      tau = radix_select32_desc(sk, (int)ns, (int)r, sc);
+    }
+  }
+  if (tid == 0) p.tau[tl] = tau;
+}
+
+hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_exh_threshold, dim3(p.Tb), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
+constexpr int EXH_CAPS_MAX = 16384;
+
+// The first K of a descending composite list of `avail` entries; missing entries
+// (zero composites or past avail) are -1 / -inf.
+__device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const uint64_t v = i < avail ? buf[i] : 0ull;
+    oi[i] = v ? (int)comp_id(v) : -1;
+    if (os) os[i] = v ? comp_score(v) : -__builtin_inff();
+  }
+}
+
+// Sort each row's survivors and write its top k, or list the row for the fallback.
+__global__ __launch_bounds__(1024) void k_exh_finalize(ExhParams p) {
+  __shared__ uint64_t buf[EXH_CAPS_MAX];
+  const int tl = blockIdx.x, tid = threadIdx.x;
+  const int t = exh_query(p, tl);
+  const int64_t n = p.q_pos0 + t + 1;
+  const int K = p.k;
+  const int c = p.cnt[tl];
+  const int need = n < K ? (int)n : K;
+  if (c < need || c > p.caps) {
+    if (tid == 0) p.failed[1 + atomicAdd(&p.failed[0], 1)] = tl;
+    return;
+  }
+  const int P2 = next_pow2(c);
+  const uint64_t* sv = p.surv + (size_t)tl * p.caps;
+  for (int i = tid; i < P2; i += blockDim.x) buf[i] = i < c ? sv[i] : 0ull;
+  __syncthreads();
+  bitonic_sort_desc(buf, P2);
+  write_topk(buf, P2, K, p.topk_idx + (size_t)t * K, p.topk_score ? p.topk_score + (size_t)t * K : nullptr);
+}
+
+hipError_t launch_exh_finalize(const ExhParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_exh_finalize, dim3(p.Tb), dim3(1024), 0, s, p);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -98,14 +245,6 @@ __device__ inline void block_find_digit(const int* hist, int nbins, int need, in
   __syncthreads();
 }
 
-__device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
-  for (int i = threadIdx.x; i < K; i += blockDim.x) {
-    const uint64_t v = i < avail ? buf[i] : 0ull;
-    oi[i] = v ? (int)comp_id(v) : -1;
-    if (os) os[i] = v ? comp_score(v) : -__builtin_inff();
-  }
-}
-
 __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
   __shared__ uint64_t buf[ROW_CAP];
   // the digit histograms share buf's memory: each is read to its last use (the
@@ -116,7 +255,7 @@ __global__ __launch_bounds__(1024) void k_topk_rows(ExhParams p) {
   __shared__ int wtmp[16];
   __shared__ int s_cnt, s_digit, s_above, s_in, s_taken;
   const int tid = threadIdx.x, bd = blockDim.x;
-  const int tl = blockIdx.x, t = p.t0 + tl;
+  const int tl = blockIdx.x, t = exh_query(p, tl);
   const int64_t n = p.q_pos0 + t + 1;
   const float* row = p.ws + (size_t)tl * p.ld;
   const int K = p.k;

@@ -118,7 +118,17 @@ def test_create_rejects_null_arguments(lib):
 
 
 def test_workspace_size(lib):
-    assert lib.idx_exhaustive_workspace_bytes(1000, 3) == 3 * 1024 * 4
+    """The streamed exhaustive selection keeps, per query, one row of sample scores
+    (every 64th key) and a survivor list, not a full score row; the workspace still
+    holds at least one full row for the fallback."""
+    n = 1 << 20
+    one = lib.idx_exhaustive_workspace_bytes(n, 1)
+    many = lib.idx_exhaustive_workspace_bytes(n, 1024)
+    assert one >= n * 4
+    assert many > one
+    assert many < 1024 * n * 4 // 10
+    per_query = (many - one) / 1023
+    assert (n // 64) * 4 <= per_query <= (n // 64) * 4 + 16384 * 8 + 1024
     assert lib.idx_exhaustive_workspace_bytes(0, 3) == 0
 
 

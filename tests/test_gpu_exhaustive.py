@@ -131,3 +131,30 @@ def test_exhaustive_all_equal_scores_long_rows():
     assert np.array_equal(ridx, np.tile(np.arange(k), (T, 1)))
     assert np.array_equal(idx.cpu().numpy(), ridx)
     assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)
+
+
+def test_exhaustive_fallback_and_streamed_rows_in_one_pass():
+    """Even rows have zero queries (every score 0: more than the survivor capacity reach
+    any threshold, so those rows take the materialized fallback); odd rows have integer
+    queries and stream.  Integer keys and queries make every score exact, so the result
+    equals the oracle's, positions and scores, in every row; a small workspace makes
+    several passes, each with its own fallback rows."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    rng = np.random.default_rng(7)
+    N, T, H, d, k = 30000, 10, 4, 32, 500
+    keys = rng.integers(-1, 2, (N, d)).astype(np.float32)
+    q = rng.integers(0, 3, (T, H, d)).astype(np.float32)
+    q[0::2] = 0.0
+    w = np.ones((T, H), np.float32)
+    q_pos0 = N - T
+    ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(N, 3) // 4, dtype=torch.float32, device="cuda")
+    say(f"exhaustive fallback mix N={N} T={T} k={k}")
+    idx, sc = ivf.idx_exhaustive_topk(to_dev(keys), None, "f32", H, to_dev(q), None, to_dev(w), q_pos0, k,
+                                      workspace=ws)
+    torch.cuda.synchronize()
+    ridx, rsc = exhaustive_topk(keys.astype(np.float64), q.astype(np.float64), w.astype(np.float64), q_pos0, k)
+    assert np.array_equal(ridx[0], np.arange(k))
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.array_equal(sc.cpu().numpy().astype(np.float64), rsc)

@@ -1,12 +1,13 @@
 """The no-allocation exhaustive entry point against the workspace one.
 
-idx_exhaustive_topk_noalloc runs the same kernels as idx_exhaustive_topk with the
-score rows in the library's per-GPU scratch array instead of a caller workspace,
-so its outputs must equal the workspace entry point's bit for bit.  Two calls in a
-row (the second smaller, on a different format) check that the array's contents
-from the previous call do not leak into the next; a 600K-key prefix makes the
-scratch array hold fewer rows than there are queries, so several passes run; a
-score row larger than the array is refused before any device work.
+idx_exhaustive_topk_noalloc runs the same kernels as idx_exhaustive_topk with its
+workspace (sample scores, survivor lists, the fallback's score rows) in the
+library's per-GPU scratch array instead of a caller workspace, so its outputs must
+equal the workspace entry point's bit for bit.  Two calls in a row (the second
+smaller, on a different format) check that the array's contents from the previous
+call do not leak into the next; 1500 queries over a 600K-key prefix are more than
+the array holds at once, so two passes run; a prefix whose pass exceeds the array
+is refused before any device work.
 """
 import numpy as np
 import pytest
@@ -53,8 +54,9 @@ def test_noalloc_matches_workspace_entry_point():
     say("no-alloc exhaustive: two calls, the second smaller; then a multi-pass prefix")
     _both(ivf, torch, "bf16", 20000, 300, 512, seed=1)
     _both(ivf, torch, "e4m3", 5000, 100, 256, seed=2)
-    # 600K keys: one score row is 2.4 MB, the 128 MiB array holds 55 of the 64 rows
-    _both(ivf, torch, "bf16", 600000, 64, 2048, seed=3)
+    # 600K bf16 keys, k = 2048: about 100 KB per query (a 9375-key sample row and 8192
+    # survivors), so the 128 MiB array holds about 1300 of the 1500 queries per pass
+    _both(ivf, torch, "bf16", 600000, 1500, 2048, seed=3)
 
 
 def test_noalloc_rejects_rows_beyond_the_array():
@@ -63,7 +65,7 @@ def test_noalloc_rejects_rows_beyond_the_array():
     ensure_built()
     lib = ivf.lib()
     p = ctypes.c_void_p(16)              # never dereferenced: the size check fails first
-    n = (128 << 20) // 4 + 64            # one score row longer than the array
+    n = (128 << 20) // 4 + 64            # the fallback's score row alone is longer than the array
     rc = lib.idx_exhaustive_topk_noalloc(p, None, n, 1, 64, 128, p, None, p, n - 1, 1, 8, p, None, None)
     assert rc == ivf.IDX_ECAPACITY
     assert "scratch" in ivf.idx_last_error()
