@@ -172,8 +172,6 @@ hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-constexpr int EXH_CAPS_MAX = 16384;
-
 // The first K of a descending composite list of `avail` entries; missing entries
 // (zero composites or past avail) are -1 / -inf.
 __device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
@@ -184,9 +182,13 @@ __device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi
   }
 }
 
-// Sort each row's survivors and write its top k, or list the row for the fallback.
+// Each row's top k from its survivors, or the row onto the fallback list: the k-th
+// largest survivor (a radix select over the survivor list in memory) bounds the k
+// survivors that are kept, which are then sorted.
 __global__ __launch_bounds__(1024) void k_exh_finalize(ExhParams p) {
-  __shared__ uint64_t buf[EXH_CAPS_MAX];
+  __shared__ uint64_t sel[4096];
+  __shared__ SelectScratch ss;
+  __shared__ int s_n;
   const int tl = blockIdx.x, tid = threadIdx.x;
   const int t = exh_query(p, tl);
   const int64_t n = p.q_pos0 + t + 1;
@@ -197,12 +199,24 @@ __global__ __launch_bounds__(1024) void k_exh_finalize(ExhParams p) {
     if (tid == 0) p.failed[1 + atomicAdd(&p.failed[0], 1)] = tl;
     return;
   }
-  const int P2 = next_pow2(c);
   const uint64_t* sv = p.surv + (size_t)tl * p.caps;
-  for (int i = tid; i < P2; i += blockDim.x) buf[i] = i < c ? sv[i] : 0ull;
+  const int m = c < K ? c : K;   // entries kept
+  const int P2 = next_pow2(m);
+  if (c <= K) {
+    for (int i = tid; i < P2; i += blockDim.x) sel[i] = i < c ? sv[i] : 0ull;
+  } else {
+    const uint64_t kth = radix_select_desc(sv, nullptr, c, K, ss);   // composites are unique
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    for (int i = tid; i < c; i += blockDim.x) {
+      const uint64_t v = sv[i];
+      if (v >= kth) sel[atomicAdd(&s_n, 1)] = v;
+    }
+    for (int i = K + tid; i < P2; i += blockDim.x) sel[i] = 0ull;
+  }
   __syncthreads();
-  bitonic_sort_desc(buf, P2);
-  write_topk(buf, P2, K, p.topk_idx + (size_t)t * K, p.topk_score ? p.topk_score + (size_t)t * K : nullptr);
+  bitonic_sort_desc(sel, P2);
+  write_topk(sel, P2, K, p.topk_idx + (size_t)t * K, p.topk_score ? p.topk_score + (size_t)t * K : nullptr);
 }
 
 hipError_t launch_exh_finalize(const ExhParams& p, hipStream_t s) {
