@@ -268,8 +268,8 @@ def main():
     # ---- exhaustive baseline + recall ----
     extra = {}
     if not args.no_exhaustive:
-        ws_q = 1024
-        ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(q_pos0 + T, ws_q) // 4, dtype=torch.float32, device=dev)
+        # one pass: the streamed selection needs about 200 KB per query, not a score row
+        ws = torch.empty(ivf.idx_exhaustive_workspace_bytes(q_pos0 + T, T) // 4, dtype=torch.float32, device=dev)
         e_idx = torch.empty((T, k), dtype=torch.int32, device=dev)
         e_sc = torch.empty((T, k), dtype=torch.float32, device=dev)
         ivf.idx_exhaustive_topk(keys, ks, dt, H, q, qs, w, q_pos0, k, e_idx, e_sc, workspace=ws)
