@@ -153,7 +153,6 @@ struct RefitParams {
   int64_t B_r;         // S + r*R
   StoreView prev;      // epoch r-1 (size/cent used; valid when r >= 2)
   const float* prev_drift;      // [slots of r-1]: centroid movement of epoch r-1's update
-  const float* prev_drift_max;  // device scalar
   StoreView seal;
   // per-key state, indexed by position
   int* assign;
@@ -183,6 +182,11 @@ struct RefitParams {
   int* ovf;            // keys whose candidate list overflowed: exact brute force
   int* ovf_count;
   int brute_ovf;       // 1: the brute-force kernel takes its keys from ovf
+  // certification of the keys of epoch r-1 (see refit.hip)
+  uint32_t* hkey;      // [(r-1)*Q] selection keys of the old slots' drifts
+  int* hlist;          // [r*Q] listed slots: the most-moved old slots, then the new ones
+  int* nlist;          // device scalar: listed slots
+  float* rest_drift;   // device scalar: largest drift of an unlisted live old slot
 };
 
 // Learned representatives of slots [slot0, slot0 + n_slots) of one store.

@@ -19,8 +19,13 @@
 //
 // Bound state per key (Hamerly): ub >= distance to its own warm centroid, lb <=
 // distance to every other live warm centroid.  After the update, drift[s] bounds
-// how far centroid s moved; the next refit widens ub by drift[own] and shrinks lb by
-// the largest drift.
+// how far centroid s moved.  A single lower bound shrunk by the largest drift
+// certifies almost nothing here (a few centroids move far in every update), so the
+// next refit lists the most-moved quarter of the old slots together with the new
+// ones: a key keeps its slot when its distance (ub widened by its own slot's drift,
+// else exact) is below A - E for every listed slot (the matrix-core screen below) and
+// below lb shrunk by the largest drift of an unlisted slot.  Every other key, and
+// every new key, is screened against all slots.
 #include "dispatch.h"
 #include "launch.h"
 #include "params.h"
@@ -139,59 +144,40 @@ __global__ void k_refit_begin(RefitParams p) {
   if (threadIdx.x == 0) p.tile_cmax[0] = 0u;
 }
 
-// keys that were assigned by epoch r-1: test the bounds against the new centres
-template <int DT, int D>
-__global__ __launch_bounds__(256) void k_refit_old(RefitParams p) {
-  __shared__ float tile[REFIT_TILE_SLOTS * D];
-  __shared__ int alive[REFIT_TILE_SLOTS];
-  const int64_t x = p.S + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const bool active = x < p.B_prev;
-  float xv[D];
-  int a = 0;
-  float u1 = 0.0f, l1 = 0.0f;
-  if (active) {
-    load_key_f32<DT, D>(xv, p, x);
-    a = min(max(p.assign[x], 0), (p.r - 1) * p.Q - 1);
-    u1 = (p.ub[x] + p.prev_drift[a]) * (1.0f + EPS_B);
-    l1 = __builtin_fmaxf(p.lb[x] - *p.prev_drift_max, 0.0f) * (1.0f - EPS_B);
+// The slots listed for certifying the keys of epoch r-1: the m live old slots that
+// moved most in the last update (m = a quarter of the old slots, rounded up to a
+// whole tile, at least 32), then the Q new ones.  rest_drift bounds the drift of
+// every live old slot left out.
+__global__ __launch_bounds__(1024) void k_refit_hsel(RefitParams p) {
+  __shared__ Select32Scratch sc;
+  __shared__ int s_alive, s_n;
+  const int tid = threadIdx.x;
+  const int n_old = (p.r - 1) * p.Q;
+  if (tid == 0) {
+    s_alive = 0;
+    s_n = 0;
   }
-  float dnew = __builtin_inff();
-  const int n0 = (p.r - 1) * p.Q, n1 = p.r * p.Q;
-  for (int t0 = n0; t0 < n1; t0 += REFIT_TILE_SLOTS) {
-    const int nt = min(REFIT_TILE_SLOTS, n1 - t0);
-    __syncthreads();
-    load_cent_tile<D>(tile, nt, [&](int c) { return p.seal.cent + (size_t)(t0 + c) * D; });
-    for (int i = threadIdx.x; i < nt; i += blockDim.x) alive[i] = p.seal.size[t0 + i] > 0;
-    __syncthreads();
-    if (active) {
-      int c = 0;
-      for (; c + 4 <= nt; c += 4) {
-        float d4[4];
-        sqdist4<D>(xv, tile + c * D, d4[0], d4[1], d4[2], d4[3]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (alive[c + u]) dnew = __builtin_fminf(dnew, d4[u]);
-      }
-      for (; c < nt; ++c) {
-        if (!alive[c]) continue;
-        dnew = __builtin_fminf(dnew, sqdist<D>(xv, tile + c * D));
-      }
-    }
+  __syncthreads();
+  int alive = 0;
+  for (int s = tid; s < n_old; s += blockDim.x) {
+    const bool a = p.prev.size[s] > 0;
+    // drifts are >= 0, so their bits order like their values; 0 marks a dead slot
+    p.hkey[s] = a ? __float_as_uint(p.prev_drift[s]) + 1u : 0u;
+    alive += a ? 1 : 0;
   }
-  if (!active) return;
-  const float ub2 = u1 * u1 * (1.0f + EPS_D);
-  const float lb2 = l1 * l1 * (1.0f - EPS_D);
-  bool keep = ub2 < lb2 && ub2 < dnew;
-  if (!keep) {
-    const float da = sqdist<D>(xv, p.prev.cent + (size_t)a * D);
-    keep = da < lb2 && da < dnew;
-    if (keep) u1 = __builtin_sqrtf(da) * (1.0f + EPS_B);
-  }
-  if (keep) {
-    p.ub[x] = u1;
-    p.lb[x] = __builtin_fminf(l1, __builtin_sqrtf(dnew) * (1.0f - EPS_B));
-  } else {
-    p.work[atomicAdd(p.work_count, 1)] = (int)x;
+  if (alive) atomicAdd(&s_alive, alive);
+  __syncthreads();
+  const int m = min(n_old, max(32, (n_old / 4 + 31) / 32 * 32));
+  uint32_t T = 0u;   // listed: live slots with key > T
+  if (s_alive > m) T = radix_select32_desc(p.hkey, n_old, m + 1, sc);
+  for (int s = tid; s < n_old; s += blockDim.x)
+    if (p.hkey[s] > T) p.hlist[atomicAdd(&s_n, 1)] = s;
+  __syncthreads();
+  const int nh = s_n;
+  for (int i = tid; i < p.Q; i += blockDim.x) p.hlist[nh + i] = n_old + i;
+  if (tid == 0) {
+    *p.nlist = nh + p.Q;
+    *p.rest_drift = T > 0u ? __uint_as_float(T - 1u) : 0.0f;
   }
 }
 
@@ -299,7 +285,7 @@ constexpr int SCR_LIST = 8;   // candidate entries per lane (each half-wave sees
 // merge, the survivors are evaluated exactly, and the bounds for the next refit are
 // ub = exact best, lb = min(second-best exact survivor, Aout - E) (every other slot
 // has D >= A - E >= Aout - E).
-template <int DT, int D>
+template <int DT, int D, bool CERT>
 __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
   using GB = Geo<DT_BF16, D>;
   constexpr int CPR = GB::RB / 16;
@@ -309,40 +295,49 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
   // two tile buffers: the loads of tile t+1 are in flight while tile t is contracted
   __shared__ u32x4 ctile[2][TCH];
   __shared__ float cn[2][32];
+  __shared__ int csl[2][CERT ? 32 : 1];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31, g = (lane >> 5) & 1;
   const int64_t n_new = p.B_r - p.B_prev;
-  const int64_t total = n_new + *p.work_count;
+  const int64_t total = CERT ? p.B_prev - p.S : n_new + *p.work_count;
   const int nslots = p.r * p.Q;
-  const int ntl = (nslots + 31) / 32;
+  const int nL = CERT ? *p.nlist : nslots;   // slots screened: the list, or all
+  const int ntl = (nL + 31) / 32;
+  auto slot_of = [&](int li) { return CERT ? p.hlist[li] : li; };
   const float cmr = __builtin_sqrtf(__uint_as_float(p.tile_cmax[0])) * (1.0f + 1e-6f);
-  auto gload = [&](int tl, u32x4 (&r)[CPT], float& cr) {
+  auto gload = [&](int tl, u32x4 (&r)[CPT], float& cr, int& ci) {
     const int t0 = tl * 32;
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int c = k * 256 + tid;
       const int h = c / (32 * CPR), cc = c % (32 * CPR);
-      const int sl = min(t0 + cc / CPR, nslots - 1) + h * nslots;
+      const int sl = slot_of(min(t0 + cc / CPR, nL - 1)) + h * nslots;
       r[k] = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint8_t*>(p.cbf) + (size_t)sl * GB::RB +
                                              (cc % CPR) * 16);
     }
-    cr = (tid < 32 && t0 + tid < nslots) ? p.cnrm[t0 + tid] : __builtin_inff();
+    ci = (tid < 32 && t0 + tid < nL) ? slot_of(t0 + tid) : -1;
+    cr = ci >= 0 ? p.cnrm[ci] : __builtin_inff();
   };
-  auto lstore = [&](int b, const u32x4 (&r)[CPT], float cr) {
+  auto lstore = [&](int b, const u32x4 (&r)[CPT], float cr, int ci) {
 #pragma unroll
     for (int k = 0; k < CPT; ++k) {
       const int c = k * 256 + tid;
       const int h = c / (32 * CPR), cc = c % (32 * CPR);
       ctile[b][h * 32 * CPR + stage_slot<CPR>(cc / CPR, cc % CPR)] = r[k];
     }
-    if (tid < 32) cn[b][tid] = cr;
+    if (tid < 32) {
+      cn[b][tid] = cr;
+      if constexpr (CERT) csl[b][tid] = ci;
+    }
   };
   for (int64_t base = (int64_t)blockIdx.x * 128; base < total; base += (int64_t)gridDim.x * 128) {
     const int64_t item = base + wave * 32 + col;
     const bool active = item < total;
     int64_t x = p.S;
-    if (item < n_new) x = p.B_prev + item;
+    if (CERT) x = p.S + item;
+    else if (item < n_new) x = p.B_prev + item;
     else if (item < total) x = (int64_t)p.work[item - n_new];
-    x = min(max(x, (int64_t)p.S), p.B_r - 1);
+    x = min(max(x, (int64_t)p.S), (CERT ? p.B_prev : p.B_r) - 1);
+    const int own = CERT ? min(max(p.assign[x], 0), (p.r - 1) * p.Q - 1) : -1;
     // this lane's half of the key as bf16 (B operand), and the squared norm
     // B operand: this lane's half of the key in bf16.  E4M3 codes and bf16 keys are
     // exact in bf16 (the E4M3 scale multiplies the dot product afterwards), so one
@@ -384,13 +379,14 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     bool ovf = false;
     u32x4 reg[CPT];
     float creg;
-    gload(0, reg, creg);
-    lstore(0, reg, creg);
+    int ireg;
+    gload(0, reg, creg, ireg);
+    lstore(0, reg, creg, ireg);
     __syncthreads();
     for (int tl = 0; tl < ntl; ++tl) {
       const int t0 = tl * 32, b = tl & 1;
       const bool more = tl + 1 < ntl;
-      if (more) gload(tl + 1, reg, creg);
+      if (more) gload(tl + 1, reg, creg, ireg);
       v16f acc;
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[v] = 0.0f;
@@ -418,10 +414,16 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * j + e;
           A[v] = (nx + cv[e]) - 2.0f * acc[v];
-          tmin = __builtin_fminf(tmin, A[v]);
+          if constexpr (CERT) {
+            if (csl[b][8 * j + 4 * g + e] != own) tmin = __builtin_fminf(tmin, A[v]);
+          } else {
+            tmin = __builtin_fminf(tmin, A[v]);
+          }
         }
       }
-      if (tmin <= amin + E2) {
+      if constexpr (CERT) {
+        amin = __builtin_fminf(amin, tmin);   // smallest A over the listed slots but the own one
+      } else if (tmin <= amin + E2) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           if (A[v] <= amin + E2) {
@@ -448,8 +450,36 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
       } else {
         aout = __builtin_fminf(aout, tmin);
       }
-      if (more) lstore(b ^ 1, reg, creg);
+      if (more) lstore(b ^ 1, reg, creg, ireg);
       __syncthreads();
+    }
+    if constexpr (CERT) {
+      // the key keeps its slot if the slot is certainly nearest: its distance (upper
+      // bound widened by the slot's drift, else the exact distance) is below the lower
+      // bound of every listed slot (A - E) and of every unlisted one (the previous lower
+      // bound shrunk by the largest drift among them)
+      amin = __builtin_fminf(amin, __shfl_xor(amin, 32));
+      const float m2 = amin - 1.01f * E;
+      if (active && g == 0) {
+        float u1 = (p.ub[x] + p.prev_drift[own]) * (1.0f + EPS_B);
+        const float l1 = __builtin_fmaxf(p.lb[x] - *p.rest_drift, 0.0f) * (1.0f - EPS_B);
+        const float ub2 = u1 * u1 * (1.0f + EPS_D);
+        const float lb2 = l1 * l1 * (1.0f - EPS_D);
+        bool keep = ub2 < lb2 && ub2 < m2;
+        if (!keep) {
+          const float da = sqdist_row<DT, D>(p.keys + (size_t)x * (D * Elem<DT>::bytes), ksc,
+                                             p.prev.cent + (size_t)own * D);
+          keep = da < lb2 && da < m2;
+          if (keep) u1 = __builtin_sqrtf(da) * (1.0f + EPS_B);
+        }
+        if (keep) {
+          p.ub[x] = u1;
+          p.lb[x] = __builtin_fminf(l1, __builtin_sqrtf(__builtin_fmaxf(m2, 0.0f)) * (1.0f - EPS_B));
+        } else {
+          p.work[atomicAdd(p.work_count, 1)] = (int)x;
+        }
+      }
+      continue;
     }
     // both halves of the wave hold the same key: final cut, then exact distances of
     // this lane's survivors
@@ -661,13 +691,13 @@ template <int DT, int D>
 static hipError_t launch_refit_t(const RefitParams& p, hipStream_t s) {
   const int nslots = p.r * p.Q;
   hipLaunchKernelGGL(k_refit_begin, dim3(1), dim3(64), 0, s, p);
+  hipLaunchKernelGGL((k_refit_prep<DT, D>), dim3((nslots + 255) / 256), dim3(256), 0, s, p);
   const int64_t n_old = p.B_prev - p.S;
   if (n_old > 0) {
-    hipLaunchKernelGGL((k_refit_old<DT, D>), dim3((unsigned)((n_old + 255) / 256)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(k_refit_hsel, dim3(1), dim3(1024), 0, s, p);
+    hipLaunchKernelGGL((k_refit_screen<DT, D, true>), dim3(2048), dim3(256), 0, s, p);
   }
-  const int nslots_ = p.r * p.Q;
-  hipLaunchKernelGGL((k_refit_prep<DT, D>), dim3((nslots_ + 255) / 256), dim3(256), 0, s, p);
-  hipLaunchKernelGGL((k_refit_screen<DT, D>), dim3(2048), dim3(256), 0, s, p);
+  hipLaunchKernelGGL((k_refit_screen<DT, D, false>), dim3(2048), dim3(256), 0, s, p);
   RefitParams po = p;
   po.brute_ovf = 1;
   hipLaunchKernelGGL((k_refit_brute<DT, D>), dim3(256), dim3(256), 0, s, po);

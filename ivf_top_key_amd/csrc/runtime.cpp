@@ -113,6 +113,10 @@ struct idx_index {
   unsigned* tile_cmax = nullptr;
   int* ovf = nullptr;
   int* ovf_count = nullptr;
+  uint32_t* hkey = nullptr;      // refit certification: drift keys, listed slots, their count, rest drift
+  int* hlist = nullptr;
+  int* nlist = nullptr;
+  float* rest_drift = nullptr;
   float* srep = nullptr;
   int* cand = nullptr;
   int* cand_len = nullptr;
@@ -295,7 +299,10 @@ int idx_create(const idx_config* cfg, void* stream, idx_index** out) {
          ix->alloc(&ix->cbf, 2 * std::max<int64_t>(ix->ep_slot_cap, 1) * c.dim) &&
          ix->alloc(&ix->cnrm, std::max<int64_t>(ix->ep_slot_cap, 1)) &&
          ix->alloc(&ix->tile_cmax, std::max<int64_t>((ix->ep_slot_cap + 31) / 32, 1)) &&
-         ix->alloc(&ix->ovf, c.max_keys) && ix->alloc(&ix->ovf_count, 1);
+         ix->alloc(&ix->ovf, c.max_keys) && ix->alloc(&ix->ovf_count, 1) &&
+         ix->alloc(&ix->hkey, std::max<int64_t>(ix->ep_slot_cap, 1)) &&
+         ix->alloc(&ix->hlist, std::max<int64_t>(ix->ep_slot_cap, 1)) && ix->alloc(&ix->nlist, 1) &&
+         ix->alloc(&ix->rest_drift, 1);
   }
   if (!ok) {
     (void)hipStreamSynchronize(ix->fill_stream);
@@ -427,7 +434,6 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   const StoreView pv = ix->epoch_view(r - 1);
   p.prev = pv;
   p.prev_drift = r >= 2 ? ix->ep[(r - 1) % 3].drift : nullptr;
-  p.prev_drift_max = r >= 2 ? ix->ep[(r - 1) % 3].drift_max : nullptr;
   p.seal = ix->seal_view();
   p.assign = ix->assign;
   p.ub = ix->ub;
@@ -451,6 +457,10 @@ int idx_refit(idx_index* ix, void* stream, void* side_stream, int32_t* launched)
   p.ovf = ix->ovf;
   p.ovf_count = ix->ovf_count;
   p.brute_ovf = 0;
+  p.hkey = ix->hkey;
+  p.hlist = ix->hlist;
+  p.nlist = ix->nlist;
+  p.rest_drift = ix->rest_drift;
   p.tile = TILE;
   p.n_tiles = (int)((p.B_r - p.S + TILE - 1) / TILE);
   e = launch_refit(p, c.dtype, c.dim, side);
