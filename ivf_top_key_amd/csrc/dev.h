@@ -555,12 +555,9 @@ __device__ __forceinline__ void load_query_wregs(QueryFrag<DT, D, HT>& f, const 
 // also quiet signalling NaNs first, which costs a second instruction.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
 
-// This lane's half of the score of its column (key): sum over the head rows the lane
-// holds (rows 8j + 4g + e of each head tile, in the order ht, j, e) of
-// w' * ReLU(q . k).  The other half is in lane l ^ 32.
+// The contraction of one 32-key tile: acc[ht] = q (head tile ht) . k over d.
 template <int DT, int D, int HT>
-__device__ __forceinline__ float tile_partial(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
-  v16f acc[HT];
+__device__ __forceinline__ void tile_mfma(const QueryFrag<DT, D, HT>& f, const uint32_t* b, v16f (&acc)[HT]) {
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
 #pragma unroll
@@ -569,6 +566,13 @@ __device__ __forceinline__ float tile_partial(const QueryFrag<DT, D, HT>& f, con
     for (int s = 0; s < Geo<DT, D>::KS; ++s)
       mfma_step<DT>(acc[ht], &f.a[ht][s * Geo<DT, D>::KD], &b[s * Geo<DT, D>::KD]);
   }
+}
+
+// This lane's half of the score of its column (key): sum over the head rows the lane
+// holds (rows 8j + 4g + e of each head tile, in the order ht, j, e) of
+// w' * ReLU(q . k).  The other half is in lane l ^ 32.
+template <int DT, int D, int HT>
+__device__ __forceinline__ float tile_epilogue(const QueryFrag<DT, D, HT>& f, const v16f (&acc)[HT]) {
   float p = 0.0f;
 #pragma unroll
   for (int ht = 0; ht < HT; ++ht) {
@@ -576,6 +580,13 @@ __device__ __forceinline__ float tile_partial(const QueryFrag<DT, D, HT>& f, con
     for (int v = 0; v < 16; ++v) p = __builtin_fmaf(f.w[ht][v], relu(acc[ht][v]), p);
   }
   return p;
+}
+
+template <int DT, int D, int HT>
+__device__ __forceinline__ float tile_partial(const QueryFrag<DT, D, HT>& f, const uint32_t* b) {
+  v16f acc[HT];
+  tile_mfma<DT, D, HT>(f, b, acc);
+  return tile_epilogue<DT, D, HT>(f, acc);
 }
 
 // Score of this lane's column (key) against the query, before the key scale.
@@ -594,13 +605,22 @@ __device__ __forceinline__ float score_tile(const QueryFrag<DT, D, HT>& f, const
 // lower-half partial and the upper-half partial of its column: the same two fp32
 // values, added once, as score_tile, hence the same bits.
 template <int DT, int D, int HT>
-__device__ __forceinline__ float score_tile_pair(const QueryFrag<DT, D, HT>& f, const uint32_t* bA,
-                                                 const uint32_t* bB) {
-  const float pA = tile_partial<DT, D, HT>(f, bA);
-  const float pB = tile_partial<DT, D, HT>(f, bB);
+__device__ __forceinline__ float pair_epilogue(const QueryFrag<DT, D, HT>& f, const v16f (&accA)[HT],
+                                               const v16f (&accB)[HT]) {
+  const float pA = tile_epilogue<DT, D, HT>(f, accA);
+  const float pB = tile_epilogue<DT, D, HT>(f, accB);
   // after the swap: r[0] = [pA lanes 0..31, pB lanes 0..31], r[1] = [pA lanes 32..63, pB lanes 32..63]
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(pA), __float_as_uint(pB), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int DT, int D, int HT>
+__device__ __forceinline__ float score_tile_pair(const QueryFrag<DT, D, HT>& f, const uint32_t* bA,
+                                                 const uint32_t* bB) {
+  v16f accA[HT], accB[HT];
+  tile_mfma<DT, D, HT>(f, bA, accA);
+  tile_mfma<DT, D, HT>(f, bB, accB);
+  return pair_epilogue<DT, D, HT>(f, accA, accB);
 }
 
 // Score column blocks blk = first, first + step, ... < nblk of one query with a ring
@@ -794,16 +814,15 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, cons
   };
   auto compute = [&](int st, const u32x4* tb, const float* sb) {
     if constexpr (PAIR) {
+      // rows past nrows are zeros (the loads return zeros past the end) and their sink
+      // calls are dropped by the callers, so every pair of the stage is scored
 #pragma unroll
       for (int tt = 0; tt < TPS; tt += 2) {
-        const int r0 = st * S::SR + tt * 32;
-        if (r0 < nrows) {
-          uint32_t bA[G::HW], bB[G::HW];
-          operand(bA, tb, tt);
-          operand(bB, tb, tt + 1);
-          const float x = score_tile_pair<DT, D, HT>(f, bA, bB) * sb[tt * 32 + lane];
-          sink(r0 + lane, x);
-        }
+        uint32_t bA[G::HW], bB[G::HW];
+        operand(bA, tb, tt);
+        operand(bB, tb, tt + 1);
+        const float x = score_tile_pair<DT, D, HT>(f, bA, bB) * sb[tt * 32 + lane];
+        sink(st * S::SR + tt * 32 + lane, x);
       }
     } else {
 #pragma unroll
