@@ -11,8 +11,9 @@
 //
 // Epoch r starts from slots [0, r*Q): epoch r-1's centroids for s < (r-1)*Q and the
 // seal centroids of the R/W newest windows (the new centres) above.  The result is
-// the exact nearest-centroid assignment (fp32 distances in the fixed order, ties to
-// the lower slot) of every key in [S, B_r) followed by exact-order means, i.e. the
+// the exact nearest-centroid assignment (fp32 distances in the fixed order, each term
+// t = x_i - c_i then one fused multiply-add, ties to the lower slot) of every key in
+// [S, B_r) followed by exact-order means, i.e. the
 // bounds only skip work.  Bound arithmetic keeps a relative slack far above the
 // fp32 error of a 128-term distance (about 8e-6), so a certified key is never a
 // near tie.
@@ -48,7 +49,7 @@ __device__ __forceinline__ float sqdist(const float (&x)[D], const float* c) {
 #pragma unroll
   for (int i = 0; i < D; ++i) {
     const float t = x[i] - c[i];
-    acc = acc + t * t;
+    acc = __builtin_fmaf(t, t, acc);
   }
   return acc;
 }
@@ -64,10 +65,10 @@ __device__ __forceinline__ void sqdist4(const float (&x)[D], const float* c, flo
     const float t1 = x[i] - c[D + i];
     const float t2 = x[i] - c[2 * D + i];
     const float t3 = x[i] - c[3 * D + i];
-    a0 = a0 + t0 * t0;
-    a1 = a1 + t1 * t1;
-    a2 = a2 + t2 * t2;
-    a3 = a3 + t3 * t3;
+    a0 = __builtin_fmaf(t0, t0, a0);
+    a1 = __builtin_fmaf(t1, t1, a1);
+    a2 = __builtin_fmaf(t2, t2, a2);
+    a3 = __builtin_fmaf(t3, t3, a3);
   }
   d0 = a0;
   d1 = a1;
@@ -100,7 +101,7 @@ __device__ __forceinline__ float sqdist_row(const uint8_t* row, float sk, const 
 #pragma unroll
     for (int e = 0; e < EPC; ++e) {
       const float t = xv[e] - cv[e];
-      acc = acc + t * t;
+      acc = __builtin_fmaf(t, t, acc);
     }
   }
   return acc;
@@ -548,17 +549,26 @@ __global__ __launch_bounds__(1024) void k_tile_hist(RefitParams p) {
   for (int i = threadIdx.x; i < nslots; i += blockDim.x) out[i] = hist[i];
 }
 
-// per slot: exclusive prefix over tiles, and the slot size
+// per slot: exclusive prefix over tiles, and the slot size (16 tiles' counts loaded
+// together, then scanned: one memory round trip per 16 tiles)
 __global__ void k_tile_colscan(RefitParams p) {
   const int nslots = p.r * p.Q;
   const int s = blockIdx.x * blockDim.x + threadIdx.x;
   if (s >= nslots) return;
+  int* col = p.tile_cnt + s;
+  const int nt = p.n_tiles;
   int run = 0;
-  for (int tl = 0; tl < p.n_tiles; ++tl) {
-    int* c = p.tile_cnt + (size_t)tl * nslots + s;
-    const int v = *c;
-    *c = run;
-    run += v;
+  for (int t0 = 0; t0 < nt; t0 += 16) {
+    int v[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) v[u] = col[(size_t)min(t0 + u, nt - 1) * nslots];
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (t0 + u < nt) {
+        col[(size_t)(t0 + u) * nslots] = run;
+        run += v[u];
+      }
+    }
   }
   p.size[s] = run;
 }

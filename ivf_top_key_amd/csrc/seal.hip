@@ -8,8 +8,9 @@
 // size-capped k-means.
 //
 // Arithmetic (fixed so that the result is reproducible bit for bit):
-//   D(x, c) = sum over i ascending of (x_i - c_i)^2, each operation rounded to fp32
-//   (the library is built with floating-point contraction off);
+//   D(x, c) = sum over i ascending of (x_i - c_i)^2: t = x_i - c_i rounded to fp32,
+//   then acc = fma(t, t, acc), one rounding (the library is built with
+//   floating-point contraction off, so no other operation fuses);
 //   mean = fp32 running sum over members in ascending position, then one division.
 // Initial centroids: keys at offsets floor((2c+1) W / (2C)).  Assignment: nearest
 // centroid (ties to the lower cluster) when that respects the cap; otherwise the
@@ -167,7 +168,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
               const float t = xv[e] - cent[c * D + ch * EPC + e];
-              s = s + t * t;
+              s = __builtin_fmaf(t, t, s);
             }
             acc[c] = s;
           }

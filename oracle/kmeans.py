@@ -8,8 +8,8 @@ corrects the representative) with size-capped k-means at seal (kurate.org,
 fix one so that two implementations can agree bit for bit:
 
 * squared distance D(x, c) = sum over i = 0..d-1 in ascending order of
-  (x_i - c_i)^2, every subtraction, product and sum rounded to fp32
-  (round-to-nearest-even), no fused multiply-add;
+  (x_i - c_i)^2: t = x_i - c_i rounded to fp32, then acc = t*t + acc rounded
+  once to fp32 (a fused multiply-add, round-to-nearest-even), from acc = +0.0;
 * mean of a cluster = fp32 running sum of its members in ascending key
   position starting from +0.0, then one IEEE fp32 division by the count.
 
@@ -24,6 +24,35 @@ from __future__ import annotations
 import numpy as np
 
 
+def fma32(a, b, c) -> np.ndarray:
+    """a*b + c for fp32 arrays, rounded once to fp32 (nearest, ties to even), for
+    finite results.
+
+    The product of two fp32 values is exact in fp64 (48 significant bits).  Its
+    fp64 sum with c is rounded once; the two-sum formulas give that rounding's
+    exact error e, so a*b + c = s + e exactly.  Rounding s to fp32 is then the
+    correct rounding of a*b + c unless s landed exactly on the midpoint of two
+    fp32 neighbours while e != 0 (the fp64 rounding moved a value off one side of
+    the midpoint onto it); in that case the side is the sign of e.
+    """
+    a = np.asarray(a, dtype=np.float32)
+    b = np.asarray(b, dtype=np.float32)
+    c = np.asarray(c, dtype=np.float32)
+    p = a.astype(np.float64) * b.astype(np.float64)    # exact
+    c64 = c.astype(np.float64)
+    s = p + c64
+    bv = s - p                                         # two-sum: p + c64 = s + e
+    e = (p - (s - bv)) + (c64 - bv)
+    r = s.astype(np.float32)                           # nearest fp32, ties to even
+    r64 = r.astype(np.float64)
+    toward = np.where(s > r64, np.float32(np.inf), np.float32(-np.inf))
+    other = np.nextafter(r, toward)                    # the fp32 neighbour on s's side
+    at_mid = (s != r64) & (s == (r64 + other.astype(np.float64)) * 0.5)
+    out = np.where(at_mid & (e > 0), np.maximum(r, other), r)
+    out = np.where(at_mid & (e < 0), np.minimum(r, other), out)
+    return out.astype(np.float32)
+
+
 def sqdist_exact(X: np.ndarray, C: np.ndarray) -> np.ndarray:
     """X [n, d] fp32, C [m, d] fp32 -> D [n, m] fp32 in the fixed order above."""
     X = np.asarray(X, dtype=np.float32)
@@ -31,8 +60,7 @@ def sqdist_exact(X: np.ndarray, C: np.ndarray) -> np.ndarray:
     acc = np.zeros((X.shape[0], C.shape[0]), dtype=np.float32)
     for i in range(X.shape[1]):
         diff = X[:, i:i + 1] - C[None, :, i]      # fp32 subtraction
-        sq = diff * diff                          # fp32 product
-        acc = acc + sq                            # fp32 sum, dimension i after i-1
+        acc = fma32(diff, diff, acc)              # diff^2 + acc, one rounding; dimension i after i-1
     return acc
 
 

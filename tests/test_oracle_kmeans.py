@@ -3,6 +3,10 @@
 * Distances and means against float64 (scipy / numpy) within the fp32 error
   bound of a sequential sum, which fails on a dropped term, a transposed
   operand or a wrong axis.
+* The fused multiply-add (one rounding of a*b + c) against rational
+  arithmetic rounded to fp32 from the format's definition, including values a
+  hair off a midpoint of two fp32 neighbours, and the distance chain replayed
+  term by term in rational arithmetic (which a two-rounding chain fails).
 * The capped greedy assignment against an independent certificate: an
   assignment equals the greedy walk over (distance, key, cluster) in ascending
   order if and only if, for every key, each cluster it prefers to its own is
@@ -11,14 +15,91 @@
 * A non-binding cap reduces seal to textbook Lloyd from the same initial
   centres: scikit-learn's KMeans (algorithm="lloyd") is the library reference.
 """
+from fractions import Fraction
+
 import numpy as np
 import pytest
 from scipy.spatial.distance import cdist
 from sklearn.cluster import KMeans
 
-from oracle.kmeans import capped_greedy_assign, mean_exact, nearest, seal_window, sqdist_exact
+from oracle.kmeans import capped_greedy_assign, fma32, mean_exact, nearest, seal_window, sqdist_exact
 
 U = 2.0 ** -24
+
+
+def _round_f32(x: Fraction) -> float:
+    """The fp32 value nearest to the rational x, ties to the even significand
+    (written from the format's definition: 24-bit significands, subnormals below
+    2^-126 with quantum 2^-149, no overflow handling)."""
+    if x == 0:
+        return 0.0
+    sign = -1 if x < 0 else 1
+    x = abs(x)
+    e = x.numerator.bit_length() - x.denominator.bit_length()
+    if Fraction(2) ** e > x:
+        e -= 1
+    quantum = Fraction(2) ** (max(e, -126) - 23)
+    q = x / quantum
+    n = q.numerator // q.denominator
+    rest = q - n
+    if rest > Fraction(1, 2) or (rest == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return sign * float(n * quantum)
+
+
+def _fma_ref(a, b, c) -> float:
+    return _round_f32(Fraction(float(a)) * Fraction(float(b)) + Fraction(float(c)))
+
+
+def test_fma32_is_the_single_rounding_of_a_times_b_plus_c():
+    rng = np.random.default_rng(13)
+    n = 3000
+    a = (rng.standard_normal(n) * 2.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    b = (rng.standard_normal(n) * 2.0 ** rng.integers(-30, 30, n)).astype(np.float32)
+    c = (rng.standard_normal(n) * 2.0 ** rng.integers(-60, 60, n)).astype(np.float32)
+    got = fma32(a, b, c)
+    want = np.array([_fma_ref(x, y, z) for x, y, z in zip(a, b, c)], dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    # a plain product-then-sum rounds twice and differs somewhere
+    assert not np.array_equal((a * b + c).view(np.uint32), want.view(np.uint32))
+
+
+def test_fma32_when_the_wide_sum_lands_on_a_midpoint():
+    """a*b + c a hair off the midpoint of two fp32 neighbours, closer than fp64 can
+    tell apart: a rounding of the fp64 sum would take the even neighbour, the single
+    rounding must take the side the exact value is on."""
+    u = 2.0 ** -24
+    c = np.float32(1 + 2 * u)                       # odd last bit
+    a = np.float32(1 + 2.0 ** -15)
+    b = np.float32((1 - 2.0 ** -15) * u)            # a*b = u (1 - 2^-30)
+    assert float(fma32(a, b, c)) == float(c)        # just below c + u: stays at c
+    assert float(fma32(-a, b, c)) == float(c)       # just above c - u: rounds up to c
+    assert _fma_ref(a, b, c) == float(c) and _fma_ref(-a, b, c) == float(c)
+    # an exact tie goes to the even neighbour
+    h = np.float32(2.0 ** -12)
+    assert float(fma32(h, h, c)) == 1 + 4 * u == _fma_ref(h, h, c)
+
+
+def test_sqdist_is_the_fused_chain_in_ascending_dimension():
+    """Each term: t = x_i - c_i rounded to fp32, then acc = t*t + acc rounded once,
+    i ascending from acc = +0; replayed here in rational arithmetic."""
+    rng = np.random.default_rng(14)
+    X = rng.standard_normal((6, 24)).astype(np.float32)
+    C = rng.standard_normal((4, 24)).astype(np.float32)
+    D = sqdist_exact(X, C)
+    for j in range(6):
+        for c in range(4):
+            acc = 0.0
+            for i in range(24):
+                t = _round_f32(Fraction(float(X[j, i])) - Fraction(float(C[c, i])))
+                acc = _round_f32(Fraction(t) * Fraction(t) + Fraction(acc))
+            assert float(D[j, c]) == acc
+    # the plain two-rounding chain gives other bits on these rows
+    two = np.zeros((6, 4), np.float32)
+    for i in range(24):
+        t = X[:, i:i + 1] - C[None, :, i]
+        two = two + t * t
+    assert not np.array_equal(two.view(np.uint32), D.view(np.uint32))
 
 
 def test_sqdist_within_sequential_sum_bound():
