@@ -61,9 +61,10 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   constexpr int CPR = RB / 16;                // chunks per row
   constexpr int DPW = 4 / Elem<DT>::bytes;    // elements per 32-bit word
   constexpr int QPR = D / DPW;                // words per row
-  // The window's keys are staged in LDS when they fit in 128 KB (row chunk ch of key
-  // m at slot m*CPR + (ch ^ (m & (CPR-1))), so that the rows read by consecutive
-  // threads fall in different banks).
+  // The window's keys are staged in LDS, row after row, when they fit in 128 KB.  (The
+  // distance pass reads whole rows, one per thread, and spends hundreds of VALU
+  // operations per 16-byte chunk, so its bank conflicts cost little; the means read
+  // words of one row across a wave, and address a row with one multiply-add.)
   constexpr bool STAGE = SEAL_MAXW * RB <= 131072;
   __shared__ uint4 kst[STAGE ? SEAL_MAXW * CPR : 1];
   __shared__ float ksc[(STAGE && DT == DT_E4M3) ? SEAL_MAXW : 1];
@@ -71,8 +72,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   __shared__ int cnt[CS], clo[CS], plo[CS], pfill[CS];
   __shared__ uint32_t amax[CS];
   __shared__ int wcnt[16 * CS];
-  __shared__ int member[SEAL_MAXW];
-  __shared__ float msc[DT == DT_E4M3 ? SEAL_MAXW : 1];   // member scales, in member order
+  __shared__ int2 mem2[SEAL_MAXW];   // member list: key offset and the bits of its scale
   __shared__ __align__(16) uint64_t prop[SEAL_MAXW + 8 * CS];
   __shared__ int s_over;
   __shared__ uint32_t s_dirty;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
       for (int k = 0; k < 4; ++k) {
         const int c = c0 + k * bd + tid;
         const int m = c / CPR, ch = c % CPR;
-        if (c < nch) kst[m * CPR + (ch ^ (m & (CPR - 1)))] = v[k];
+        if (c < nch) kst[m * CPR + ch] = v[k];
       }
     }
     if constexpr (DT == DT_E4M3) {
@@ -105,14 +105,14 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
   // chunk ch, word q, scale of window key m
   auto chunk = [&](int m, int ch) -> uint4 {
     if constexpr (STAGE) {
-      return kst[m * CPR + (ch ^ (m & (CPR - 1)))];
+      return kst[m * CPR + ch];
     } else {
       return reinterpret_cast<const uint4*>(wrows + (size_t)m * RB)[ch];
     }
   };
   auto word = [&](int m, int q) -> uint32_t {
     if constexpr (STAGE) {
-      return reinterpret_cast<const uint32_t*>(kst + m * CPR + ((q >> 2) ^ (m & (CPR - 1))))[q & 3];
+      return reinterpret_cast<const uint32_t*>(kst)[m * QPR + q];
     } else {
       return reinterpret_cast<const uint32_t*>(wrows + (size_t)m * RB)[q];
     }
@@ -286,8 +286,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
     __syncthreads();
     if (tid < W) {
       const int r = clo[a] + wcnt[wv * CS + a] + myrank;
-      member[r] = tid;
-      if constexpr (DT == DT_E4M3) msc[r] = key_scale(tid);
+      mem2[r] = make_int2(tid, __float_as_int(key_scale(tid)));
     }
     __syncthreads();
 
@@ -298,7 +297,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
       const int c = idx / QPR, q = idx % QPR;
       const int nc = cnt[c];
       if (nc > 0 && ((dirty >> c) & 1u)) {
-        const int* mem = member + clo[c];
+        const int2* mem = mem2 + clo[c];
         float s[DPW];
 #pragma unroll
         for (int e = 0; e < DPW; ++e) s[e] = 0.0f;
@@ -308,9 +307,9 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
           float sk[8];
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
-            wd[u] = word(mem[r + u], q);
-            if constexpr (DT == DT_E4M3) sk[u] = msc[clo[c] + r + u];
-            else sk[u] = 1.0f;
+            const int2 me = mem[r + u];
+            wd[u] = word(me.x, q);
+            sk[u] = __int_as_float(me.y);
           }
 #pragma unroll
           for (int u = 0; u < 8; ++u) {
@@ -322,7 +321,8 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
         }
         for (; r < nc; ++r) {
           float x[DPW];
-          word_to_f32<DT>(word(mem[r], q), x, DT == DT_E4M3 ? msc[clo[c] + r] : 1.0f);
+          const int2 me = mem[r];
+          word_to_f32<DT>(word(me.x, q), x, __int_as_float(me.y));
 #pragma unroll
           for (int e = 0; e < DPW; ++e) s[e] = s[e] + x[e];
         }
@@ -341,7 +341,7 @@ __global__ __launch_bounds__(1024) void k_seal(SealParams p) {
     amax[tid] = 0u;
     if constexpr (DT != DT_E4M3) p.rsc[slot0 + tid] = 1.0f;
   }
-  for (int r = tid; r < W; r += bd) p.members[(size_t)w * W + r] = (int)(base + member[r]);
+  for (int r = tid; r < W; r += bd) p.members[(size_t)w * W + r] = (int)(base + mem2[r].x);
   __syncthreads();
   for (int idx = tid; idx < CS * D; idx += bd) {
     const float x = cent[idx];
