@@ -99,13 +99,17 @@ typedef struct {
                             and cluster_size = 128: max_keys < S + 1025 * 1024), else ECAPACITY */
 } idx_config;
 
-/* Candidate rescoring of idx_route_topk.  Both give bit-identical results.
- *   QUERY:   each query gathers and scores all of its candidates' key rows.
+/* Candidate rescoring of idx_route_topk.  All give bit-identical results.
+ *   QUERY:   each query gathers and scores all of its candidates' key rows; the
+ *            cluster cut writes each candidate's gather row to device memory first.
  *   CLUSTER: the (query, cluster) selections are grouped by cluster; each selected
  *            cluster's key rows are read once and scored against every query that
  *            selected it (pays off when many queries of a call share clusters).
- *   AUTO:    the library's choice; currently QUERY, which is the faster one on the
- *            measured workloads (1M-key E4M3 prefill chunk of 4096 queries). */
+ *   AUTO:    QUERY with the cut in the rescoring kernel for calls of more than 64
+ *            queries whose max(budget, n_sink + window) is at most 8192 (the ranked
+ *            clusters stay in on-chip memory, no candidate list goes through device
+ *            memory), QUERY otherwise; the fastest on the measured workloads (1M-key
+ *            E4M3 prefill chunk of 4096 queries). */
 enum { IDX_RESCORE_AUTO = 0, IDX_RESCORE_QUERY = 1, IDX_RESCORE_CLUSTER = 2 };
 
 /* How sealed windows are grouped.
@@ -143,8 +147,10 @@ typedef struct {
   int32_t* version;      /* [T, 4]: epoch r, sealed windows m, visible slots, open start */
   void** events;         /* host array of 8 hipEvent_t, recorded in pairs around the four
                             stages: representative scores; cluster cut + fill + grouping of
-                            the selections by cluster; cluster-by-cluster candidate scores;
-                            sink and open-window scores + top-k                            */
+                            the selections by cluster (or, when AUTO fuses them, cut,
+                            rescoring and top-k in one kernel); cluster-by-cluster or split
+                            candidate scores; candidate scores + top-k (fused: only the
+                            queries whose cut went to the full kernel)                     */
   int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut kernel at this
                             size so the full cut kernel takes over sooner (testing)        */
   float* cand_scores;    /* [T, cand_cap]: exact score of each candidate, fill order      */

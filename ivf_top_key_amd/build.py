@@ -17,7 +17,7 @@ OUT_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libivftk.so")
 INCLUDE = os.path.join(os.path.dirname(HERE), "include")
 
-SOURCES = ["score.hip", "route.hip", "seal.hip", "refit.hip", "encoder.hip", "runtime.cpp"]
+SOURCES = ["score.hip", "rescore.hip", "rescore_f32.hip", "rescore_bf16.hip", "rescore_e4m3.hip", "route.hip", "seal.hip", "refit.hip", "encoder.hip", "runtime.cpp"]
 
 # -ffp-contract=off: the clustering arithmetic is defined operation by operation
 #   (no fused multiply-add); the score epilogue calls fmaf explicitly.

@@ -168,6 +168,16 @@ __device__ __forceinline__ uint64_t make_comp(float score, uint32_t id) {
 __device__ __forceinline__ uint32_t comp_id(uint64_t c) { return ~(uint32_t)c; }
 __device__ __forceinline__ float comp_score(uint64_t c) { return from_order_bits((uint32_t)(c >> 32)); }
 
+// The first K of a descending composite list of `avail` entries; missing entries
+// (zero composites or past avail) are -1 / -inf.
+__device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
+  for (int i = threadIdx.x; i < K; i += blockDim.x) {
+    const uint64_t v = i < avail ? buf[i] : 0ull;
+    oi[i] = v ? (int)comp_id(v) : -1;
+    if (os) os[i] = v ? comp_score(v) : -__builtin_inff();
+  }
+}
+
 __host__ __device__ __forceinline__ int next_pow2(int n) {
   int p = 1;
   while (p < n) p <<= 1;

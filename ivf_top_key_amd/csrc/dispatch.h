@@ -12,18 +12,26 @@
     default: return hipErrorInvalidValue;        \
   }
 
+// One format's dimensions (a statement that returns when DIM matches).
+#define IVFTK_DISPATCH_F32(FN, DIM, HT_, ...)                                    \
+  if ((DIM) == 32) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 32, HT_, __VA_ARGS__)    \
+  if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 64, HT_, __VA_ARGS__)    \
+  if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 128, HT_, __VA_ARGS__)
+#define IVFTK_DISPATCH_BF16(FN, DIM, HT_, ...)                                   \
+  if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_BF16, 64, HT_, __VA_ARGS__)   \
+  if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_BF16, 128, HT_, __VA_ARGS__)
+#define IVFTK_DISPATCH_E4M3(FN, DIM, HT_, ...)                                   \
+  if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_E4M3, 64, HT_, __VA_ARGS__)   \
+  if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_E4M3, 128, HT_, __VA_ARGS__)
+
 #define IVFTK_DISPATCH(FN, DTYPE, DIM, HT_, ...)                                   \
   do {                                                                            \
     if ((DTYPE) == ivftk::DT_F32) {                                               \
-      if ((DIM) == 32) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 32, HT_, __VA_ARGS__) \
-      if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 64, HT_, __VA_ARGS__) \
-      if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_F32, 128, HT_, __VA_ARGS__) \
+      IVFTK_DISPATCH_F32(FN, DIM, HT_, __VA_ARGS__)                               \
     } else if ((DTYPE) == ivftk::DT_BF16) {                                       \
-      if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_BF16, 64, HT_, __VA_ARGS__) \
-      if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_BF16, 128, HT_, __VA_ARGS__) \
+      IVFTK_DISPATCH_BF16(FN, DIM, HT_, __VA_ARGS__)                              \
     } else if ((DTYPE) == ivftk::DT_E4M3) {                                       \
-      if ((DIM) == 64) IVFTK_DISPATCH_HT(FN, ivftk::DT_E4M3, 64, HT_, __VA_ARGS__) \
-      if ((DIM) == 128) IVFTK_DISPATCH_HT(FN, ivftk::DT_E4M3, 128, HT_, __VA_ARGS__) \
+      IVFTK_DISPATCH_E4M3(FN, DIM, HT_, __VA_ARGS__)                              \
     }                                                                             \
     return hipErrorInvalidValue;                                                  \
   } while (0)

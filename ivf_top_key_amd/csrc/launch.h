@@ -16,11 +16,18 @@ hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s);
 hipError_t launch_exh_finalize(const ExhParams& p, hipStream_t s);
 hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s);
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s);
+// The full cut kernel alone (queries with redo[t] = 1; the others return at once).
+hipError_t launch_route_select_full(const RouteParams& p, int max_slots, hipStream_t s);
 hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s);
 hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s);
 hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s);
 hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
 hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
+// Cut, rescoring and top-k fused (query-major batches; queries whose cluster list
+// overflows are marked in redo[] for the two kernels above).
+hipError_t launch_route_rescore(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
+// Largest candidate capacity of one call that the fused kernel takes.
+int route_rescore_max_cands();
 // True if one rescoring block holds cand_cap candidates and k winners.
 bool rescore_fits(int cand_cap, int k);
 hipError_t launch_seal(const SealParams& p, int dtype, int dim, int n_windows, hipStream_t s);

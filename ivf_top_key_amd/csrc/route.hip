@@ -12,38 +12,23 @@
 // count first reaches the free budget without sorting every visible cluster.  Only
 // the selected clusters are sorted, and the fill writes their members with one
 // binary search per candidate slot.
+#include "cut.h"
 #include "dev.h"
 #include "launch.h"
 #include "params.h"
+#include "routing.h"
 
 namespace ivftk {
 
-struct QV {
-  int64_t n;
-  int m, r, split, cvis;
-  int64_t open_lo;
-};
-
-__device__ __forceinline__ QV qversion(const RouteParams& p, int t) {
-  QV v;
-  v.n = (p.qpos ? p.qpos[t] : p.q_pos0 + t) + 1;
-  v.m = v.n >= p.S ? (int)((v.n - p.S) / p.W) : 0;
-  v.r = p.wpr ? min(p.P, v.m / p.wpr) : 0;
-  v.split = v.r * p.wpr * p.Cs;
-  v.cvis = v.m * p.Cs;
-  v.open_lo = (int64_t)p.S + (int64_t)v.m * p.W;
-  return v;
-}
-
 // Unified id of visible slot `slot` for a query of version v (see RouteParams).
-__device__ __forceinline__ int unified_id(const RouteParams& p, const QV& v, int slot) {
+__device__ __forceinline__ int unified_id(const RouteParams& p, const QVer& v, int slot) {
   return slot < v.split ? p.id_seal + (v.r % 3) * p.id_ep + slot : slot;
 }
 
 // Records the query's selected clusters (rank order) for the cluster-major
 // rescoring and counts one selection per cluster id.  first[i] = the list index of
 // cluster i's first candidate.  All threads call.
-__device__ inline void record_selection(const RouteParams& p, const QV& v, int t, const uint64_t* comp,
+__device__ inline void record_selection(const RouteParams& p, const QVer& v, int t, const uint64_t* comp,
                                         const int* pre, int base_len, int nsel) {
   if (!p.cluster_major) return;
   int* sid = p.sel_id + (size_t)t * p.sel_ld;
@@ -69,7 +54,7 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   __shared__ int s_total, s_nsel;
   const int tid = threadIdx.x, bd = blockDim.x;
   const int t = blockIdx.x;
-  const QV v = qversion(p, t);
+  const QVer v = query_version(p, t);
   const StoreView ep = p.ep[v.r % 3];
   int* cand = p.cand + (size_t)t * p.cand_ld;
   int* crow = p.cand_row + (size_t)t * p.cand_ld;
@@ -188,41 +173,9 @@ __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_po
   }
 }
 
-// Fast version: one pass builds a 4096-bin histogram of the live clusters' score
-// keys (linear bins between the smallest and largest key), weighted by cluster
-// size; the bin holding the cut is found by a suffix scan, and only clusters in
-// that bin or above (the selected ones plus the cut bin's other members) are
-// gathered and sorted exactly.  If that list would exceed LIST_CAP the query is
-// left to the full kernel.
-constexpr int LIST_CAP = 1024;
-constexpr int SF_NBIN = 2048;   // value bins of the cluster-cut histogram
-
-__device__ inline void find_bin_desc(const int* hist, int nbins, int need, int* wtmp, int* o_digit) {
-  const int tid = threadIdx.x, bd = blockDim.x;
-  const int per = (nbins + bd - 1) / bd;
-  int s = 0;
-  for (int q = 0; q < per; ++q) {
-    const int d = nbins - 1 - tid * per - q;
-    if (d >= 0) s += hist[d];
-  }
-  int tot;
-  const int excl = block_exclusive_scan(s, wtmp, &tot);
-  if (excl < need && need <= excl + s) {
-    int acc = excl;
-    for (int q = 0; q < per; ++q) {
-      const int d = nbins - 1 - tid * per - q;
-      if (d < 0) break;
-      if (acc + hist[d] >= need) {
-        *o_digit = d;
-        break;
-      }
-      acc += hist[d];
-    }
-  }
-  __syncthreads();
-}
-
-constexpr int SF_SLOTS = 8192;        // routed slots at most (checked when an index is created)
+// Fast version (cut_clusters in cut.h): a size-weighted value histogram finds the
+// bin holding the cut and only the clusters at or above it are sorted; a query whose
+// list would exceed LIST_CAP is left to the full kernel above.
 constexpr int SF_THREADS = 512;       // threads per query in large batches
 constexpr int SF_SMALL_BATCH = 64;    // batches this small leave most CUs idle: a block of
 constexpr int SF_SMALL_THREADS = 1024;   // 1024 threads per query halves the per-thread chains
@@ -230,19 +183,17 @@ constexpr int SF_SMALL_THREADS = 1024;   // 1024 threads per query halves the pe
 // NT threads per block; each thread holds SF_SLOTS / NT slots.
 template <int NT>
 __global__ __launch_bounds__(NT) void k_route_select_fast(RouteParams p) {
-  constexpr int SF_PT = SF_SLOTS / NT;
-  static_assert(SF_SLOTS % NT == 0 && NT <= 1024, "block shape");
   __shared__ int hist[SF_NBIN];
   __shared__ uint64_t list[LIST_CAP];
   __shared__ int pre[LIST_CAP + 1];
   __shared__ int moff[LIST_CAP];   // first member index; epoch store if >= 0, else seal store at ~moff
   __shared__ int wtmp[16];
   __shared__ uint32_t mm_tmp[2 * NT / 64];
-  __shared__ int s_digit, s_cnt, s_nsel;
+  __shared__ CutWords cw;
   const int tid = threadIdx.x, bd = NT;
   const int wave = tid >> 6, lane = tid & 63, nw = bd >> 6;
   const int t = blockIdx.x;
-  const QV v = qversion(p, t);
+  const QVer v = query_version(p, t);
   const StoreView ep = p.ep[v.r % 3];
   int* cand = p.cand + (size_t)t * p.cand_ld;
   int* crow = p.cand_row + (size_t)t * p.cand_ld;
@@ -271,106 +222,13 @@ __global__ __launch_bounds__(NT) void k_route_select_fast(RouteParams p) {
     return;
   }
   const float* srep = p.srep + (size_t)t * p.srep_ld;
-  // this thread's slots s = u * bd + tid: score order key and size (0 = dead or not
-  // visible).  The loads are unconditional (slots past the visible ones read the
-  // last visible slot and are masked afterwards) so that all of them are in flight
-  // together.
-  uint32_t ks[SF_PT];
-  int szs[SF_PT];
-  float scs[SF_PT];
-#pragma unroll
-  for (int u = 0; u < SF_PT; ++u) {
-    const int s = min(u * bd + tid, v.cvis - 1);
-    szs[u] = (s < v.split ? ep.size : p.seal.size)[s];
-    scs[u] = srep[s];
-  }
-#pragma unroll
-  for (int u = 0; u < SF_PT; ++u) {
-    const bool vis = u * bd + tid < v.cvis;
-    ks[u] = vis ? order_bits(scs[u]) : 0u;
-    szs[u] = vis ? szs[u] : 0;
-  }
-  for (int i = tid; i < SF_NBIN; i += bd) hist[i] = 0;
-  if (tid == 0) {
-    s_cnt = 0;
-    s_digit = 0;
-    s_nsel = 0;
-  }
-  // value bins over [min, max] of the live clusters' scores
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int u = 0; u < SF_PT; ++u) {
-    if (szs[u] > 0) {
-      mn = ks[u] < mn ? ks[u] : mn;
-      mx = ks[u] > mx ? ks[u] : mx;
-    }
-  }
-  block_minmax(mn, mx, mm_tmp);
-  const ValBins bins = make_bins(mn, mx < mn ? mn : mx, SF_NBIN);
-  int bn[SF_PT];
-  int mine = 0;
-#pragma unroll
-  for (int u = 0; u < SF_PT; ++u) {
-    bn[u] = (int)bins(ks[u]);
-    if (szs[u] > 0) {
-      atomicAdd(&hist[bn[u]], szs[u]);
-      mine += szs[u];
-    }
-  }
-  int total;
-  block_exclusive_scan(mine, wtmp, &total);
-  // total <= room: every live cluster is taken (bin 0 and up)
-  if (total > room) find_bin_desc(hist, SF_NBIN, room, wtmp, &s_digit);
-  const uint32_t cut_bin = (uint32_t)s_digit;
-#pragma unroll
-  for (int u = 0; u < SF_PT; ++u) {
-    if (szs[u] > 0 && (uint32_t)bn[u] >= cut_bin) {
-      const int i = atomicAdd(&s_cnt, 1);
-      if (i < LIST_CAP) list[i] = ((uint64_t)ks[u] << 32) | (uint64_t)(~(uint32_t)(u * bd + tid));
-    }
-  }
-  __syncthreads();
-  const int cnt = s_cnt;
-  if (cnt > (p.list_cap > 0 ? min(p.list_cap, LIST_CAP) : LIST_CAP)) {
+  const int cap = p.list_cap > 0 ? min(p.list_cap, LIST_CAP) : LIST_CAP;
+  const CutResult cr = cut_clusters<NT>(p, srep, v.cvis, v.split, ep, room, cap, hist, list, pre, moff, wtmp, mm_tmp, cw);
+  if (cr.nsel < 0) {
     if (tid == 0) p.redo[t] = 1;
     return;
   }
-  if (cnt <= 64) {
-    if (tid < 64) list[tid] = wave_sort_desc(tid < cnt ? list[tid] : 0ull);
-    __syncthreads();
-  } else {
-    const int P2 = next_pow2(cnt);
-    for (int i = cnt + tid; i < P2; i += bd) list[i] = 0ull;
-    __syncthreads();
-    bitonic_sort_desc(list, P2);
-  }
-  // prefix sums of member counts in rank order; pre[cnt] = total of the list
-  int run = 0;
-  for (int b0 = 0; b0 < cnt; b0 += bd) {
-    const int i = b0 + tid;
-    int sz = 0, mo = 0;
-    if (i < cnt) {
-      const int s = (int)comp_id(list[i]);
-      const bool from_epoch = s < v.split;
-      sz = (from_epoch ? ep.size : p.seal.size)[s];
-      const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
-      mo = from_epoch ? off : ~off;
-    }
-    int tot;
-    const int ex = block_exclusive_scan(sz, wtmp, &tot);
-    if (i < cnt) {
-      pre[i] = run + ex;
-      moff[i] = mo;
-    }
-    run += tot;
-    __syncthreads();
-  }
-  if (tid == 0) pre[cnt] = run;
-  const int used = min(room, run);
-  for (int i = tid; i < cnt; i += bd)
-    if (pre[i] < used && (i == cnt - 1 || pre[i + 1] >= used)) s_nsel = i + 1;
-  __syncthreads();
-  const int nsel = s_nsel;
+  const int nsel = cr.nsel, used = cr.used;
   record_selection(p, v, t, list, pre, base_len, nsel);
   // fill: one wave per selected cluster copies its first `take` members, four
   // clusters per step; the loads are unconditional (clamped inside the cluster) so
@@ -508,6 +366,10 @@ hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t 
     hipLaunchKernelGGL(k_route_select_fast<SF_THREADS>, dim3(p.T), dim3(SF_THREADS), 0, s, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
+  return launch_route_select_full(p, max_slots, s);
+}
+
+hipError_t launch_route_select_full(const RouteParams& p, int max_slots, hipStream_t s) {
   const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);
   const size_t lds = (size_t)slot_pow2 * (sizeof(uint64_t) + sizeof(int));
   hipError_t e = hipFuncSetAttribute((const void*)k_route_select, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -637,20 +637,33 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   auto mark = [&](int i) {
     if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
   };
+  // AUTO with a large batch: cut, rescoring and top-k in one kernel; a query whose
+  // cluster list overflows goes through the full cut kernel and the rescoring kernel
+  // (both return at once for every other query)
+  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
+  const bool fused = c.rescore_mode == IDX_RESCORE_AUTO && !p.cluster_major && !p.prescored &&
+                     call_cap <= route_rescore_max_cands();
   mark(0);
   if (max_slots > 0 && e == hipSuccess) e = launch_rep_score(p, c.dtype, c.dim, ix->HT, max_slots, s);
   mark(1);
   mark(2);
-  if (p.cluster_major && e == hipSuccess) e = launch_pairs_zero(p, s);
-  if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
-  if (p.cluster_major && e == hipSuccess) e = launch_pairs_group(p, s);
+  if (fused) {
+    if (e == hipSuccess) e = launch_route_rescore(p, c.dtype, c.dim, ix->HT, call_cap, s);
+  } else {
+    if (p.cluster_major && e == hipSuccess) e = launch_pairs_zero(p, s);
+    if (e == hipSuccess) e = launch_route_select(p, max_slots, s);
+    if (p.cluster_major && e == hipSuccess) e = launch_pairs_group(p, s);
+  }
   mark(3);
-  const int call_cap = (int)round_up(std::max<int64_t>(budget, (int64_t)c.n_sink + c.window), 32);
   mark(4);
   if (p.cluster_major && e == hipSuccess) e = launch_cluster_score(p, c.dtype, c.dim, ix->HT, s);
   if (p.prescored && e == hipSuccess) e = launch_cand_score(p, c.dtype, c.dim, ix->HT, call_cap, s);
   mark(5);
   mark(6);
+  if (fused) {
+    p.only_redo = 1;
+    if (e == hipSuccess) e = launch_route_select_full(p, max_slots, s);
+  }
   if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
   mark(7);
   if (e != hipSuccess) return device_error(ix, e, "route launch");

@@ -10,6 +10,7 @@
 #include "dispatch.h"
 #include "launch.h"
 #include "params.h"
+#include "routing.h"
 
 namespace ivftk {
 
@@ -170,16 +171,6 @@ __global__ __launch_bounds__(1024) void k_exh_threshold(ExhParams p) {
 hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_exh_threshold, dim3(p.Tb), dim3(1024), 0, s, p);
   return hipGetLastError();
-}
-
-// The first K of a descending composite list of `avail` entries; missing entries
-// (zero composites or past avail) are -1 / -inf.
-__device__ inline void write_topk(const uint64_t* buf, int avail, int K, int* oi, float* os) {
-  for (int i = threadIdx.x; i < K; i += blockDim.x) {
-    const uint64_t v = i < avail ? buf[i] : 0ull;
-    oi[i] = v ? (int)comp_id(v) : -1;
-    if (os) os[i] = v ? comp_score(v) : -__builtin_inff();
-  }
 }
 
 // Each row's top k from its survivors, or the row onto the fallback list: the k-th
@@ -444,31 +435,6 @@ hipError_t launch_topk_rows(const ExhParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_topk_rows, dim3(p.Tb), dim3(1024), 0, s, p);
   return hipGetLastError();
 }
-
-// ---------------------------------------------------------------------------
-// query version (routed path)
-// ---------------------------------------------------------------------------
-struct QVer {
-  int64_t n;       // prefix length
-  int m;           // sealed windows inside the prefix
-  int r;           // refit epoch used
-  int split;       // slots below come from the epoch store
-  int cvis;        // visible slots [0, cvis)
-  int64_t open_lo; // open window [open_lo, n)
-};
-
-__device__ __forceinline__ QVer query_version(const RouteParams& p, int t) {
-  QVer v;
-  v.n = (p.qpos ? p.qpos[t] : p.q_pos0 + t) + 1;
-  v.m = v.n >= p.S ? (int)((v.n - p.S) / p.W) : 0;
-  v.r = p.wpr ? min(p.P, v.m / p.wpr) : 0;
-  v.split = v.r * p.wpr * p.Cs;
-  v.cvis = v.m * p.Cs;
-  v.open_lo = (int64_t)p.S + (int64_t)v.m * p.W;
-  return v;
-}
-
-__device__ __forceinline__ StoreView epoch_store(const RouteParams& p, int r) { return p.ep[r % 3]; }
 
 // ---------------------------------------------------------------------------
 // representative scores: block = 4 queries, one chunk of slots
@@ -761,485 +727,6 @@ static hipError_t launch_cluster_score_t(const RouteParams& p, hipStream_t s) {
 
 hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s) {
   IVFTK_DISPATCH(launch_cluster_score_t, dtype, dim, ht, p, s);
-}
-
-// ---------------------------------------------------------------------------
-// candidate key rows
-// ---------------------------------------------------------------------------
-// The three sources a query's candidate rows come from: the position-ordered keys
-// (sinks and open window), the seal store's member-ordered copy and the query's
-// epoch store's copy (CROW_* in params.h).  Rows are clamped below n_keys, which
-// bounds every source.
-// The per-lane choice of source is arithmetic on byte offsets from the first source
-// (masks, no selects), which keeps the compiler from turning it into a table in
-// scratch memory.
-struct RowSources {
-  const uint8_t* key0;
-  int64_t dk1, dk2;      // key1 - key0, key2 - key0 (bytes)
-  const float* scale0;
-  int64_t ds1, ds2;      // scale1 - scale0, scale2 - scale0 (bytes)
-};
-
-__device__ __forceinline__ RowSources row_sources(const RouteParams& p, int r) {
-  const int e = r % 3;
-  const uint8_t* k2 = e == 0 ? p.ep[0].ckeys : (e == 1 ? p.ep[1].ckeys : p.ep[2].ckeys);
-  const float* s2 = e == 0 ? p.ep[0].cscale : (e == 1 ? p.ep[1].cscale : p.ep[2].cscale);
-  RowSources rs;
-  rs.key0 = p.keys;
-  rs.dk1 = (int64_t)(uintptr_t)p.seal.ckeys - (int64_t)(uintptr_t)p.keys;
-  rs.dk2 = (int64_t)(uintptr_t)k2 - (int64_t)(uintptr_t)p.keys;
-  rs.scale0 = p.kscale;
-  rs.ds1 = (int64_t)(uintptr_t)p.seal.cscale - (int64_t)(uintptr_t)p.kscale;
-  rs.ds2 = (int64_t)(uintptr_t)s2 - (int64_t)(uintptr_t)p.kscale;
-  return rs;
-}
-
-template <int DT, int D>
-__device__ __forceinline__ void load_cand_row(const RowSources& rs, int code, int nk1, uint32_t* buf, float& scl) {
-  const int src = (int)((uint32_t)code >> CROW_SHIFT);
-  int j = code & CROW_MASK;
-  j = j > nk1 ? nk1 : j;
-  const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
-  const uint8_t* kb = rs.key0 + ((rs.dk1 & m1) | (rs.dk2 & m2));
-  load_half_row<DT, D>(buf, kb + (size_t)j * Geo<DT, D>::RB);
-  if constexpr (DT == DT_E4M3) {
-    const float* sb = reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(rs.scale0) +
-                                                     ((rs.ds1 & m1) | (rs.ds2 & m2)));
-    scl = sb[j];
-  } else {
-    scl = 1.0f;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// split candidate scoring for small batches
-// ---------------------------------------------------------------------------
-// A batch of a few queries leaves most of the chip idle with one block per query,
-// so block (t, b) scores candidates [b*CSB, (b+1)*CSB) of query t into sbuf (the
-// same score tile, hence the same bits) and the final kernel only selects.
-constexpr int CSB = 256;   // candidates per block
-
-template <int DT, int D, int HT>
-__global__ __launch_bounds__(256) void k_cand_score(RouteParams p) {
-  using G = Geo<DT, D>;
-  __shared__ float wq_s[HT * 32];
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = lane & 31;
-  const int t = blockIdx.x;
-  const int L = p.cand_len[t];
-  const int i0 = blockIdx.y * CSB;
-  if (i0 >= L) return;
-  const int n = min(CSB, L - i0);
-  const int* crow = p.cand_row + (size_t)t * p.cand_ld + i0;
-  float* out = p.sbuf + (size_t)t * p.cand_ld + i0;
-  const int nk1 = (int)(p.n_keys - 1);
-  const RowSources rs = row_sources(p, query_version(p, t).r);
-  if (wave == 0)
-    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
-  QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-  __syncthreads();
-  load_query_wregs<DT, D, HT>(f, wq_s);
-  score_gather<DT, D, HT, 2>(
-      f, wave, 4, (n + 31) >> 5,
-      [&](int blk) -> int {
-        const int i = blk * 32 + col;
-        return crow[i < n ? i : n - 1];
-      },
-      [rs, nk1](int code, uint32_t* buf, float& scl) { load_cand_row<DT, D>(rs, code, nk1, buf, scl); },
-      [&](int blk, float x) {
-        const int i = blk * 32 + col;
-        if (lane < 32 && i < n) out[i] = x;
-      });
-}
-
-template <int DT, int D, int HT>
-static hipError_t launch_cand_score_t(const RouteParams& p, int cand_cap, hipStream_t s) {
-  hipLaunchKernelGGL((k_cand_score<DT, D, HT>), dim3(p.T, (cand_cap + CSB - 1) / CSB), dim3(256), 0, s, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s) {
-  IVFTK_DISPATCH(launch_cand_score_t, dtype, dim, ht, p, cand_cap, s);
-}
-
-// ---------------------------------------------------------------------------
-// candidate rescoring + top-k: one block per query
-// ---------------------------------------------------------------------------
-// The candidates' scores go to LDS as 32-bit order keys while the waves gather
-// and score key rows (ring of row loads in flight per wave).  Then every thread
-// takes its PT keys and candidate ids into registers, which frees the LDS for the
-// selection: a value-binned histogram between the block's min and max score
-// finds the bin holding the k-th score; entries in higher bins are placed by bin
-// offset plus rank inside their bin, the cut bin is sorted exactly.  Ties at the
-// k-th score go to the lowest positions; the k winners come out sorted by
-// (score desc, position asc).  Degenerate cases (all scores equal, a crowded cut
-// bin) use an exact radix select.
-constexpr int RS_NBIN = 1024;     // value bins of the top-k histogram
-constexpr int RS_TIE_CAP = 512;   // largest cut bin resolved by a local sort
-constexpr int RS_THREADS = 256;        // scoring + selection blocks
-constexpr int RS_SEL_THREADS = 1024;   // selection-only blocks (candidates scored beforehand)
-
-// LDS bytes of the selection region for a candidate capacity and k (both powers of two).
-__host__ __device__ constexpr size_t rescore_region_bytes(int cap_pow2, int k_pow2) {
-  return (size_t)cap_pow2 * 4 > (size_t)(k_pow2 + RS_TIE_CAP) * 8 + (size_t)RS_NBIN * 8
-             ? (size_t)cap_pow2 * 4
-             : (size_t)(k_pow2 + RS_TIE_CAP) * 8 + (size_t)RS_NBIN * 8;
-}
-
-// NT threads per block.  With NT = RS_SEL_THREADS the block only selects: every
-// candidate was scored into sbuf beforehand (small batches), and the selection's
-// per-thread chains are a quarter as long, which is what a lone query waits on.
-template <int DT, int D, int HT, int PT, int NT>
-__global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) {
-  using G = Geo<DT, D>;
-  constexpr bool SELECT_ONLY = NT != RS_THREADS;
-  constexpr int KPT = 4096 / NT;   // winners per thread at the largest k
-  static_assert(RS_NBIN % NT == 0 && NT % 64 == 0 && NT <= 1024, "block shape");
-  extern __shared__ uint64_t lds[];
-  __shared__ float wq_s[HT * 32];
-  __shared__ Select32Scratch sc;
-  __shared__ uint32_t mm_tmp[2 * NT / 64];
-  __shared__ int wtmp[16];
-  __shared__ int s_cnt, s_tie, s_bstar;
-  uint32_t* okey = reinterpret_cast<uint32_t*>(lds);   // scoring: [L] score keys
-  uint64_t* sel = lds;                                 // selection: [k_pow2] winners
-  uint64_t* tie = lds + k_pow2;                        // [RS_TIE_CAP] cut bin
-  int* hist = reinterpret_cast<int*>(lds + k_pow2 + RS_TIE_CAP);   // [RS_NBIN]
-  int* offs = hist + RS_NBIN;                                      // [RS_NBIN]
-  const int tid = threadIdx.x, bd = NT;
-  const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
-  const int t = blockIdx.x;
-  const int L = p.cand_len[t];
-  const int* cand = p.cand_row + (size_t)t * p.cand_ld;   // gather rows; positions derived below
-  const int K = p.k;
-  const int nk1 = (int)(p.n_keys - 1);
-  if constexpr (!SELECT_ONLY) {
-  if (wave == 0)
-    load_query_weights<HT>(wq_s, p.w + (size_t)t * p.H, p.qscale ? p.qscale + (size_t)t * p.H : nullptr, p.H);
-  QueryFrag<DT, D, HT> f;
-  load_query<DT, D, HT>(f, p.q + (size_t)t * p.H * G::RB, p.H);
-  __syncthreads();
-  load_query_wregs<DT, D, HT>(f, wq_s);
-  // the sinks and the open window are scored here, and with cluster-major rescoring
-  // the selected clusters' candidates [base_len, L) were scored into sbuf; a small
-  // batch has every candidate scored into sbuf already (base_len = 0); otherwise
-  // every candidate is gathered and scored here
-  const QVer qv = query_version(p, t);
-  const int n_sink = (int)(qv.n < p.S ? qv.n : p.S);
-  const int base_len =
-      p.prescored ? 0 : (p.cluster_major ? min(L, n_sink + (qv.n > qv.open_lo ? (int)(qv.n - qv.open_lo) : 0)) : L);
-  const int nb = (base_len + 31) >> 5;
-  const int* crow = p.cand_row + (size_t)t * p.cand_ld;
-  const RowSources rs = row_sources(p, qv.r);
-  // rows in flight per wave: two at 32 entries per thread keep the kernel under 168
-  // VGPRs, i.e. three waves per SIMD (more loads in flight per CU than three rows
-  // at two waves); at 64 entries the registers allow only two waves either way
-  constexpr int RING = PT <= 32 ? 2 : 3;
-  score_gather<DT, D, HT, RING>(
-      f, wave, nw, nb,
-      [&](int blk) -> int {
-        const int i = blk * 32 + col;
-        return crow[i < base_len ? i : base_len - 1];
-      },
-      [rs, nk1](int code, uint32_t* buf, float& scl) { load_cand_row<DT, D>(rs, code, nk1, buf, scl); },
-      [&](int blk, float x) {
-        const int i = blk * 32 + col;
-        if (lane < 32 && i < base_len) {
-          okey[i] = order_bits(x);
-          if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x;
-        }
-      });
-  {
-    // eight loads in flight per thread before the first store
-    const int tail_end = p.prescored ? 0 : L;   // prescored lists are read below
-    for (int i0 = base_len + tid; i0 < tail_end; i0 += 8 * bd) {
-      float x[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * bd;
-        x[u] = i < L ? p.sbuf[(size_t)t * p.cand_ld + i] : 0.0f;
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int i = i0 + u * bd;
-        if (i < L) {
-          okey[i] = order_bits(x[u]);
-          if (p.dbg_cand_scores && i < p.dbg_cand_ld) p.dbg_cand_scores[(size_t)t * p.dbg_cand_ld + i] = x[u];
-        }
-      }
-    }
-  }
-  __syncthreads();
-  }   // !SELECT_ONLY
-  // this thread's entries: groups of four consecutive list entries, ent(u) below,
-  // with their score keys and candidate positions (16-byte loads)
-  auto ent = [&](int u) { return 4 * ((u >> 2) * bd + tid) + (u & 3); };
-  uint32_t kv[PT];
-  uint32_t cv[PT];
-  // prescored: the scores come straight from sbuf into registers (no LDS pass);
-  // kv holds the raw float bits until every load has been issued
-  if (SELECT_ONLY || p.prescored) {
-    const uint32_t* sb = reinterpret_cast<const uint32_t*>(p.sbuf + (size_t)t * p.cand_ld);
-#pragma unroll
-    for (int u4 = 0; u4 < PT / 4; ++u4) {
-      const int i0 = 4 * (u4 * bd + tid);
-      if (i0 + 3 < L) {
-        const uint4 x4 = *reinterpret_cast<const uint4*>(sb + i0);
-        const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
-        kv[4 * u4] = x4.x, kv[4 * u4 + 1] = x4.y, kv[4 * u4 + 2] = x4.z, kv[4 * u4 + 3] = x4.w;
-        cv[4 * u4] = (uint32_t)c4.x, cv[4 * u4 + 1] = (uint32_t)c4.y, cv[4 * u4 + 2] = (uint32_t)c4.z,
-        cv[4 * u4 + 3] = (uint32_t)c4.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[4 * u4 + e] = i0 + e < L ? sb[i0 + e] : 0u;
-          cv[4 * u4 + e] = i0 + e < L ? (uint32_t)cand[i0 + e] : 0u;
-        }
-      }
-    }
-    float* dbs = p.dbg_cand_scores ? p.dbg_cand_scores + (size_t)t * p.dbg_cand_ld : nullptr;
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int i = ent(u);
-      if (dbs && i < L && i < p.dbg_cand_ld) dbs[i] = __uint_as_float(kv[u]);
-      kv[u] = i < L ? order_bits(__uint_as_float(kv[u])) : 0u;
-    }
-  } else if constexpr (!SELECT_ONLY) {
-#pragma unroll
-    for (int u4 = 0; u4 < PT / 4; ++u4) {
-      const int i0 = 4 * (u4 * bd + tid);
-      if (i0 + 3 < L) {
-        const uint4 k4 = *reinterpret_cast<const uint4*>(okey + i0);
-        const int4 c4 = *reinterpret_cast<const int4*>(cand + i0);
-        kv[4 * u4 + 0] = k4.x;
-        kv[4 * u4 + 1] = k4.y;
-        kv[4 * u4 + 2] = k4.z;
-        kv[4 * u4 + 3] = k4.w;
-        cv[4 * u4 + 0] = (uint32_t)c4.x;
-        cv[4 * u4 + 1] = (uint32_t)c4.y;
-        cv[4 * u4 + 2] = (uint32_t)c4.z;
-        cv[4 * u4 + 3] = (uint32_t)c4.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int i = i0 + e;
-          kv[4 * u4 + e] = i < L ? okey[i] : 0u;
-          cv[4 * u4 + e] = i < L ? (uint32_t)cand[i] : 0u;
-        }
-      }
-    }
-  }
-  {
-    // positions: source 0 rows are positions; a store copy's row j holds that store's
-    // member j.  Every lane loads (source 0 reads a valid dummy word), then selects.
-    const QVer qv2 = query_version(p, t);
-    const int e = qv2.r % 3;
-    const int* mem0 = p.cand_len + t;
-    const int* mem2 = e == 0 ? p.ep[0].members : (e == 1 ? p.ep[1].members : p.ep[2].members);
-    const int64_t d1 = (int64_t)(uintptr_t)p.seal.members - (int64_t)(uintptr_t)mem0;
-    const int64_t d2 = (int64_t)(uintptr_t)mem2 - (int64_t)(uintptr_t)mem0;
-    const int jmax = (int)max((int64_t)0, p.n_keys - 1 - p.S);
-    int mv[PT];
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int src = (int)(cv[u] >> CROW_SHIFT);
-      const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
-      const int* mb = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(mem0) + ((d1 & m1) | (d2 & m2)));
-      const int j = (int)(cv[u] & (uint32_t)CROW_MASK);
-      mv[u] = mb[src == 0 ? 0 : (j < jmax ? j : jmax)];
-    }
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int src = (int)(cv[u] >> CROW_SHIFT);
-      cv[u] = src == 0 ? (cv[u] & (uint32_t)CROW_MASK) : (uint32_t)mv[u];
-    }
-  }
-  if (tid == 0) {
-    s_cnt = 0;
-    s_tie = 0;
-  }
-  __syncthreads();   // the LDS region is free from here on
-  int* oi = p.topk_idx + (size_t)t * K;
-  float* os = p.topk_score ? p.topk_score + (size_t)t * K : nullptr;
-  auto comp = [](uint32_t key, uint32_t pos) -> uint64_t { return ((uint64_t)key << 32) | (uint64_t)(~pos); };
-  if (L <= K) {
-    const int P2 = next_pow2(L > 0 ? L : 1);
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int i = ent(u);
-      if (i < P2) sel[i] = i < L ? comp(kv[u], cv[u]) : 0ull;
-    }
-    __syncthreads();
-    bitonic_sort_desc(sel, P2);
-    write_topk(sel, L, K, oi, os);
-    return;
-  }
-  uint32_t mn = 0xFFFFFFFFu, mx = 0u;
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    if (ent(u) < L) {
-      mn = kv[u] < mn ? kv[u] : mn;
-      mx = kv[u] > mx ? kv[u] : mx;
-    }
-  }
-  block_minmax(mn, mx, mm_tmp);
-  bool fallback = (mn == mx);
-  ValBins bins;
-  int bstar = 0, above = 0, in_bin = 0;
-  if (!fallback) {
-    bins = make_bins(mn, mx, RS_NBIN);
-    for (int i = tid; i < RS_NBIN; i += bd) hist[i] = 0;
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PT; ++u)
-      if (ent(u) < L) atomicAdd(&hist[bins(kv[u])], 1);
-    __syncthreads();
-    // offs[b] = entries in bins above b (descending order); the bin holding the K-th
-    constexpr int per = RS_NBIN / NT;
-    int sum = 0;
-#pragma unroll
-    for (int q = 0; q < per; ++q) sum += hist[RS_NBIN - 1 - tid * per - q];
-    int tot;
-    int run = block_exclusive_scan(sum, wtmp, &tot);
-#pragma unroll
-    for (int q = 0; q < per; ++q) {
-      const int bb = RS_NBIN - 1 - tid * per - q;
-      const int c = hist[bb];
-      offs[bb] = run;
-      if (run < K && K <= run + c) s_bstar = bb;
-      run += c;
-    }
-    __syncthreads();
-    bstar = s_bstar;
-    above = offs[bstar];
-    in_bin = hist[bstar];
-    fallback = in_bin > RS_TIE_CAP;
-    __syncthreads();   // every thread has read hist[bstar] before hist becomes the cursors
-  }
-  if (!fallback) {
-    // scatter: bins above the cut go to their bin's range of sel, the cut bin to tie
-    for (int i = tid; i < RS_NBIN; i += bd) hist[i] = offs[i];
-    __syncthreads();
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      if (ent(u) < L) {
-        const int bb = (int)bins(kv[u]);
-        if (bb > bstar) sel[atomicAdd(&hist[bb], 1)] = comp(kv[u], cv[u]);
-        else if (bb == bstar) tie[atomicAdd(&s_tie, 1)] = comp(kv[u], cv[u]);
-      }
-    }
-    const int P2 = next_pow2(in_bin);
-    __syncthreads();
-    if (P2 <= 64) {
-      if (tid < 64) tie[tid] = wave_sort_desc(tid < in_bin ? tie[tid] : 0ull);
-    } else {
-      for (int i = in_bin + tid; i < P2; i += bd) tie[i] = 0ull;
-      __syncthreads();
-      bitonic_sort_desc(tie, P2);
-    }
-    // entries above the cut move to bin start + rank inside the bin (ranks are taken
-    // before any entry moves), the cut bin's winners follow them
-    uint64_t pv[KPT];
-    int pp[KPT];
-#pragma unroll
-    for (int q = 0; q < KPT; ++q) {
-      const int i = q * bd + tid;
-      pp[q] = -1;
-      if (i < above) {
-        const uint64_t v = sel[i];
-        const int bb = (int)bins((uint32_t)(v >> 32));
-        const int lo = offs[bb], hi = offs[bb - 1];
-        int rank = 0;
-        int j = lo;
-        for (; j + 4 <= hi; j += 4) {   // four LDS reads in flight
-          const uint64_t a0 = sel[j], a1 = sel[j + 1], a2 = sel[j + 2], a3 = sel[j + 3];
-          rank += (a0 > v) + (a1 > v) + (a2 > v) + (a3 > v);
-        }
-        for (; j < hi; ++j) rank += sel[j] > v;
-        pv[q] = v;
-        pp[q] = lo + rank;
-      }
-    }
-    __syncthreads();
-#pragma unroll
-    for (int q = 0; q < KPT; ++q)
-      if (pp[q] >= 0) sel[pp[q]] = pv[q];
-    for (int r = tid; r < K - above; r += bd) sel[above + r] = tie[r];
-    __syncthreads();
-    write_topk(sel, K, K, oi, os);
-    return;
-  }
-  // ---- fallback: exact radix select (all keys equal, or a crowded cut bin) ----
-  __syncthreads();
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    const int i = ent(u);
-    if (i < L) okey[i] = kv[u];
-  }
-  __syncthreads();
-  const uint32_t thr = radix_select32_desc(okey, L, K, sc);
-  const int need = K - sc.above;
-  const int n_eq = sc.hist[thr & 255u];
-  uint32_t t2 = 0u;
-  __syncthreads();
-  if (n_eq != need) {
-    // more candidates share the k-th score than slots remain: lowest positions win
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int i = ent(u);
-      if (i < L) okey[i] = (kv[u] == thr) ? ~cv[u] : 0u;
-    }
-    __syncthreads();
-    t2 = radix_select32_desc(okey, L, need, sc);
-    __syncthreads();
-  }
-#pragma unroll
-  for (int u = 0; u < PT; ++u) {
-    if (ent(u) < L) {
-      const uint32_t v = kv[u];
-      if (v > thr || (v == thr && (n_eq == need || ~cv[u] >= t2))) sel[atomicAdd(&s_cnt, 1)] = comp(v, cv[u]);
-    }
-  }
-  __syncthreads();
-  for (int i = K + tid; i < k_pow2; i += bd) sel[i] = 0ull;
-  __syncthreads();
-  bitonic_sort_desc(sel, k_pow2);
-  write_topk(sel, K, K, oi, os);
-}
-
-template <int DT, int D, int HT, int PT, int NT>
-static hipError_t launch_rescore_pt(const RouteParams& p, int cap_pow2, int k_pow2, hipStream_t s) {
-  const size_t lds = rescore_region_bytes(cap_pow2, k_pow2);
-  hipError_t e = hipFuncSetAttribute((const void*)k_rescore_topk<DT, D, HT, PT, NT>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((k_rescore_topk<DT, D, HT, PT, NT>), dim3(p.T), dim3(NT), lds, s, p, k_pow2);
-  return hipGetLastError();
-}
-
-template <int DT, int D, int HT>
-static hipError_t launch_rescore_topk_t(const RouteParams& p, int cand_cap, hipStream_t s) {
-  const int cap_pow2 = next_pow2(cand_cap);
-  const int k_pow2 = next_pow2(p.k);
-  if (p.prescored) {   // selection only: four times the threads, a quarter of the entries each
-    if (cap_pow2 <= 8 * RS_SEL_THREADS) return launch_rescore_pt<DT, D, HT, 8, RS_SEL_THREADS>(p, cap_pow2, k_pow2, s);
-    if (cap_pow2 <= 16 * RS_SEL_THREADS)
-      return launch_rescore_pt<DT, D, HT, 16, RS_SEL_THREADS>(p, cap_pow2, k_pow2, s);
-    return hipErrorInvalidValue;
-  }
-  if (cap_pow2 <= 32 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 32, RS_THREADS>(p, cap_pow2, k_pow2, s);
-  if (cap_pow2 <= 64 * RS_THREADS) return launch_rescore_pt<DT, D, HT, 64, RS_THREADS>(p, cap_pow2, k_pow2, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s) {
-  IVFTK_DISPATCH(launch_rescore_topk_t, dtype, dim, ht, p, cand_cap, s);
-}
-
-bool rescore_fits(int cand_cap, int k) {
-  const int cap_pow2 = next_pow2(cand_cap), k_pow2 = next_pow2(k);
-  // the region plus the kernel's static LDS (head weights, radix scratch, a few words)
-  return cap_pow2 <= 64 * RS_THREADS && rescore_region_bytes(cap_pow2, k_pow2) + 4096 <= 163840;
 }
 
 }  // namespace ivftk

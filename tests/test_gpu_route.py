@@ -130,7 +130,9 @@ def test_route_positional_blocks(name):
     ("e4m3_small", dict(T=300, q_pos0=11000)),
 ])
 def test_route_rescore_modes_bit_identical(name, over):
-    """Query-major and cluster-major rescoring give the same candidates, scores and top-k bits."""
+    """The fused cut + rescoring kernel (auto), query-major rescoring from a candidate
+    list in memory and cluster-major rescoring give the same candidates, scores and
+    top-k bits."""
     import torch
     import ivf_top_key_amd as ivf
     ensure_built()
@@ -140,7 +142,7 @@ def test_route_rescore_modes_bit_identical(name, over):
     qs = to_dev(inp["q_scale"]) if inp["q_scale"] is not None else None
     w = to_dev(inp["w"])
     out = {}
-    for mode in ("query", "cluster"):
+    for mode in ("auto", "query", "cluster"):
         ix = gpu_index(wl, inp, rescore=mode)
         try:
             dbg = ivf.make_route_debug(T, budget + wl["window"] + 64, 8, 8)
@@ -150,14 +152,18 @@ def test_route_rescore_modes_bit_identical(name, over):
                          dbg["cand_scores"].cpu().numpy(), dbg["cand_len"].cpu().numpy())
         finally:
             ivf.idx_destroy(ix)
-    a, b = out["query"], out["cluster"]
-    assert np.array_equal(a[4], b[4])
-    for t in range(T):
-        L = int(a[4][t])
-        assert np.array_equal(a[2][t, :L], b[2][t, :L]), f"query {t}: candidate lists differ"
-        assert np.array_equal(a[3][t, :L].view(np.uint32), b[3][t, :L].view(np.uint32)), f"query {t}: scores differ"
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
-    say(f"  {name}: {T} queries, query-major and cluster-major bit-identical")
+    a = out["query"]
+    for other in ("auto", "cluster"):
+        b = out[other]
+        assert np.array_equal(a[4], b[4]), f"{other}: candidate counts differ"
+        for t in range(T):
+            L = int(a[4][t])
+            assert np.array_equal(a[2][t, :L], b[2][t, :L]), f"{other}, query {t}: candidate lists differ"
+            assert np.array_equal(a[3][t, :L].view(np.uint32), b[3][t, :L].view(np.uint32)), \
+                f"{other}, query {t}: scores differ"
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32)), \
+            f"{other}: top-k differs"
+    say(f"  {name}: {T} queries, fused, query-major and cluster-major bit-identical")
 
 
 @pytest.mark.parametrize("name", ["c1r", "e4m3_small"])
