@@ -278,6 +278,11 @@ def main():
 
     dominant = max(kern, key=kern.get)
     roof = roof_of(dominant)
+    if fused and dominant == "route_rescore":
+        # the candidates' contraction against the MFMA peak of the format, next to the
+        # bytes that bound the kernel
+        roof["algorithmic_flops"] = rescore_flops
+        roof["mfma_frac"] = round(rescore_flops / (kern[dominant] * 1e-3) / 1e12 / peak_mfma, 4)
     kernel_roofs = {n: {kk: v for kk, v in roof_of(n).items() if kk in ("bound", "achieved", "unit", "frac")}
                     for n in names if work[n][1] > 0}
 

@@ -16,16 +16,17 @@ hipError_t launch_exh_threshold(const ExhParams& p, hipStream_t s);
 hipError_t launch_exh_finalize(const ExhParams& p, hipStream_t s);
 hipError_t launch_rep_score(const RouteParams& p, int dtype, int dim, int ht, int max_slots, hipStream_t s);
 hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t s);
-// The full cut kernel alone (queries with redo[t] = 1; the others return at once).
-hipError_t launch_route_select_full(const RouteParams& p, int max_slots, hipStream_t s);
 hipError_t launch_pairs_zero(const RouteParams& p, hipStream_t s);
 hipError_t launch_pairs_group(const RouteParams& p, hipStream_t s);
 hipError_t launch_cluster_score(const RouteParams& p, int dtype, int dim, int ht, hipStream_t s);
 hipError_t launch_cand_score(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
 hipError_t launch_rescore_topk(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
-// Cut, rescoring and top-k fused (query-major batches; queries whose cluster list
-// overflows are marked in redo[] for the two kernels above).
+// Cut, rescoring and top-k fused (query-major batches); queries whose cluster list
+// overflows go to the overflow list, which launch_route_overflow then serves (and
+// leaves empty).
 hipError_t launch_route_rescore(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, hipStream_t s);
+hipError_t launch_route_overflow(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, int max_slots,
+                                 hipStream_t s);
 // Largest candidate capacity of one call that the fused kernel takes.
 int route_rescore_max_cands();
 // True if one rescoring block holds cand_cap candidates and k winners.

@@ -59,9 +59,10 @@ struct RouteParams {
                        // read-back); the rescoring derives positions from cand_row
   int64_t cand_ld;
   int* cand_len;       // [T]
-  int* redo;           // [T]: 1 when the fast cut (alone or fused with the rescoring)
-                       // left the query to the full cut kernel
-  int only_redo;       // 1: the cut-list kernels handle only queries with redo[t] = 1
+  int* redo;           // [T]: 1 when the fast cut kernel left the query to the full one
+  int* ovf;            // [2 + T]: overflow list of the fused cut + rescoring kernel:
+                       // [0] entries, [1] finished blocks of the overflow kernel,
+                       // [2..] query indices; zero entries between calls
   int* topk_idx;       // [T, k]
   float* topk_score;   // [T, k] or null
   // optional debug outputs (null when unused)

@@ -306,20 +306,16 @@ __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, 
 // gather row code to cand_row.  NT threads per block.  With NT = RS_SEL_THREADS the
 // block only selects: every candidate was scored into sbuf beforehand (small
 // batches), and the selection's per-thread chains are a quarter as long, which is
-// what a lone query waits on.  With only_redo set, blocks of queries the fused
-// kernel handled (redo[t] = 0) return at once.
+// what a lone query waits on.  lds = the selection region; wq_s holds HT * 32 floats.
+// All threads of the block call.
 template <int DT, int D, int HT, int PT, int NT>
-__global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) {
+__device__ inline void rescore_query(const RouteParams& p, int t, int k_pow2, uint64_t* lds, float* wq_s,
+                                     SelWords<NT>& sw) {
   using G = Geo<DT, D>;
   constexpr bool SELECT_ONLY = NT != RS_THREADS;
-  extern __shared__ uint64_t lds[];
-  __shared__ float wq_s[HT * 32];
-  __shared__ SelWords<NT> sw;
   uint32_t* okey = reinterpret_cast<uint32_t*>(lds);   // scoring: [L] score keys
   const int tid = threadIdx.x, bd = NT;
   const int wave = tid >> 6, lane = tid & 63, col = lane & 31, nw = bd >> 6;
-  const int t = blockIdx.x;
-  if (p.only_redo && p.redo[t] == 0) return;
   const int L = p.cand_len[t];
   const int* cand = p.cand_row + (size_t)t * p.cand_ld;   // gather rows; positions derived below
   const int nk1 = (int)(p.n_keys - 1);
@@ -440,6 +436,14 @@ __global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) 
   topk_select<PT, NT>(p, t, L, k_pow2, kv, cv, lds, sw);
 }
 
+template <int DT, int D, int HT, int PT, int NT>
+__global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) {
+  extern __shared__ uint64_t lds[];
+  __shared__ float wq_s[HT * 32];
+  __shared__ SelWords<NT> sw;
+  rescore_query<DT, D, HT, PT, NT>(p, blockIdx.x, k_pow2, lds, wq_s, sw);
+}
+
 // ---------------------------------------------------------------------------
 // cut + rescoring + top-k in one block per query (query-major batches)
 // ---------------------------------------------------------------------------
@@ -449,8 +453,8 @@ __global__ __launch_bounds__(NT) void k_rescore_topk(RouteParams p, int k_pow2) 
 // window, then the members of the ranked clusters in order (cluster s's member c at
 // list index base_len + pre[s] + c is row seg[s] + pre[s] + c of its store's
 // member-ordered copy).  No candidate list goes through memory.  A query whose
-// cluster list overflows is marked in redo[] and left to k_route_select and
-// k_rescore_topk (only_redo), which run after this kernel.
+// cluster list overflows is appended to the overflow list (ovf) and left to
+// k_route_overflow, which runs after this kernel.
 //
 // Largest s < n with pre[s] <= c (pre ascending, pre[0] = 0 <= c, n >= 1).
 __device__ __forceinline__ int seg_search(const int* pre, int n, int c) {
@@ -496,7 +500,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_rescore(RouteParams p, int
     const CutResult cr = cut_clusters<NT>(p, p.srep + (size_t)t * p.srep_ld, qv.cvis, qv.split, ep, room, cap, hist,
                                           list, pre, reinterpret_cast<int*>(seg), sw.wtmp, sw.mm_tmp, cw);
     if (cr.nsel < 0) {
-      if (tid == 0) p.redo[t] = 1;
+      if (tid == 0) p.ovf[2 + atomicAdd(&p.ovf[0], 1)] = t;
       return;
     }
     nsel = cr.nsel;
@@ -512,7 +516,6 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_rescore(RouteParams p, int
   const int L = base_len + used;
   if (tid == 0) {
     p.cand_len[t] = L;
-    p.redo[t] = 0;
     if (p.dbg_n_order) p.dbg_n_order[t] = nsel;
   }
   __syncthreads();   // seg is complete; the histogram and the list are no longer read
@@ -580,6 +583,38 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_rescore(RouteParams p, int
   topk_select<PT, NT>(p, t, L, k_pow2, kv, cv, lds, sw);
 }
 
+// The queries k_route_rescore appended to the overflow list: the full cut
+// (select_full, candidate rows through memory) and then the list-based rescoring,
+// one query at a time per block, blocks striding over the list.  The block that
+// finishes last clears the list for the next call.
+constexpr int OVF_BLOCKS = 256;
+
+template <int DT, int D, int HT, int PT>
+__global__ __launch_bounds__(RS_THREADS) void k_route_overflow(RouteParams p, int slot_pow2, int k_pow2) {
+  extern __shared__ uint64_t lds[];   // the full cut's composites and sizes, then the selection region
+  __shared__ FullCutShared fc;
+  __shared__ float wq_s[HT * 32];
+  __shared__ SelWords<RS_THREADS> sw;
+  __shared__ int s_n;
+  if (threadIdx.x == 0) s_n = __hip_atomic_load(&p.ovf[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const int n = s_n;
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int t = p.ovf[2 + i];
+    select_full(p, t, slot_pow2, lds, fc);
+    __syncthreads();   // the candidate rows and count are written
+    rescore_query<DT, D, HT, PT, RS_THREADS>(p, t, k_pow2, lds, wq_s, sw);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    __threadfence();
+    if (atomicAdd(&p.ovf[1], 1) == (int)gridDim.x - 1) {
+      p.ovf[0] = 0;
+      p.ovf[1] = 0;
+    }
+  }
+}
+
 template <int DT, int D, int HT, int PT, int NT>
 static hipError_t launch_rescore_pt(const RouteParams& p, int cap_pow2, int k_pow2, hipStream_t s) {
   const size_t lds = rescore_region_bytes(cap_pow2, k_pow2);
@@ -631,6 +666,23 @@ static hipError_t launch_route_rescore_t(const RouteParams& p, int cand_cap, hip
   return hipErrorInvalidValue;
 }
 
+template <int DT, int D, int HT>
+static hipError_t launch_route_overflow_t(const RouteParams& p, int cand_cap, int max_slots, hipStream_t s) {
+  const int cap_pow2 = next_pow2(cand_cap);
+  const int k_pow2 = next_pow2(p.k);
+  const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);
+  if (cap_pow2 > 32 * RS_THREADS) return hipErrorInvalidValue;
+  const size_t cut = (size_t)slot_pow2 * (sizeof(uint64_t) + sizeof(int));
+  const size_t sel = rescore_region_bytes(cap_pow2, k_pow2);
+  const size_t lds = cut > sel ? cut : sel;
+  hipError_t e = hipFuncSetAttribute((const void*)k_route_overflow<DT, D, HT, 32>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((k_route_overflow<DT, D, HT, 32>), dim3(OVF_BLOCKS), dim3(RS_THREADS), lds, s, p, slot_pow2,
+                     k_pow2);
+  return hipGetLastError();
+}
+
 // The launchers of one format (defined in rescore_<format>.hip).
 #define IVFTK_RESCORE_LAUNCHERS(SUF, DISPATCH)                                                              \
   hipError_t launch_cand_score_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s) {   \
@@ -644,12 +696,19 @@ static hipError_t launch_route_rescore_t(const RouteParams& p, int cand_cap, hip
   hipError_t launch_route_rescore_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s) { \
     DISPATCH(launch_route_rescore_t, dim, ht, p, cand_cap, s)                                               \
     return hipErrorInvalidValue;                                                                            \
+  }                                                                                                         \
+  hipError_t launch_route_overflow_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, int max_slots,  \
+                                         hipStream_t s) {                                                   \
+    DISPATCH(launch_route_overflow_t, dim, ht, p, cand_cap, max_slots, s)                                   \
+    return hipErrorInvalidValue;                                                                            \
   }
 
 #define IVFTK_RESCORE_DECLARE(SUF)                                                                         \
   hipError_t launch_cand_score_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s);   \
   hipError_t launch_rescore_topk_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s); \
-  hipError_t launch_route_rescore_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s);
+  hipError_t launch_route_rescore_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, hipStream_t s);  \
+  hipError_t launch_route_overflow_##SUF(const RouteParams& p, int dim, int ht, int cand_cap, int max_slots,  \
+                                         hipStream_t s);
 
 IVFTK_RESCORE_DECLARE(f32)
 IVFTK_RESCORE_DECLARE(bf16)

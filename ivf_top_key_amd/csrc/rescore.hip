@@ -23,6 +23,11 @@ hipError_t launch_route_rescore(const RouteParams& p, int dtype, int dim, int ht
   IVFTK_RESCORE_BY_FORMAT(launch_route_rescore, p, dim, ht, cand_cap, s)
 }
 
+hipError_t launch_route_overflow(const RouteParams& p, int dtype, int dim, int ht, int cand_cap, int max_slots,
+                                 hipStream_t s) {
+  IVFTK_RESCORE_BY_FORMAT(launch_route_overflow, p, dim, ht, cand_cap, max_slots, s)
+}
+
 int route_rescore_max_cands() { return 32 * RS_THREADS; }
 
 bool rescore_fits(int cand_cap, int k) {

@@ -20,157 +20,14 @@
 
 namespace ivftk {
 
-// Unified id of visible slot `slot` for a query of version v (see RouteParams).
-__device__ __forceinline__ int unified_id(const RouteParams& p, const QVer& v, int slot) {
-  return slot < v.split ? p.id_seal + (v.r % 3) * p.id_ep + slot : slot;
-}
-
-// Records the query's selected clusters (rank order) for the cluster-major
-// rescoring and counts one selection per cluster id.  first[i] = the list index of
-// cluster i's first candidate.  All threads call.
-__device__ inline void record_selection(const RouteParams& p, const QVer& v, int t, const uint64_t* comp,
-                                        const int* pre, int base_len, int nsel) {
-  if (!p.cluster_major) return;
-  int* sid = p.sel_id + (size_t)t * p.sel_ld;
-  int* sdst = p.sel_dst + (size_t)t * p.sel_ld;
-  for (int i = threadIdx.x; i < nsel; i += blockDim.x) {
-    const int id = unified_id(p, v, (int)comp_id(comp[i]));
-    sid[i] = id;
-    sdst[i] = base_len + pre[i];
-    atomicAdd(&p.pc_cnt[id], 1);
-  }
-  if (threadIdx.x == 0) p.n_sel[t] = nsel;
-}
-
-// Full version: every visible cluster in LDS, weighted radix select over composite
-// keys.  Runs only for queries the fast kernel handed over (redo[t] = 1).
+// Full version (select_full in cut.h): every visible cluster in LDS, weighted radix
+// select over composite keys.  Runs only for queries the fast kernel handed over
+// (redo[t] = 1).
 __global__ __launch_bounds__(256) void k_route_select(RouteParams p, int slot_pow2) {
   if (p.redo[blockIdx.x] == 0) return;
   extern __shared__ uint64_t lds[];
-  uint64_t* comp = lds;                                   // [slot_pow2]
-  int* wt = reinterpret_cast<int*>(lds + slot_pow2);      // [slot_pow2]: sizes, later prefix sums
-  __shared__ SelectScratch sc;
-  __shared__ int wtmp[16];
-  __shared__ int s_total, s_nsel;
-  const int tid = threadIdx.x, bd = blockDim.x;
-  const int t = blockIdx.x;
-  const QVer v = query_version(p, t);
-  const StoreView ep = p.ep[v.r % 3];
-  int* cand = p.cand + (size_t)t * p.cand_ld;
-  int* crow = p.cand_row + (size_t)t * p.cand_ld;
-
-  // sinks [0, min(S, n)) then the open window [open_lo, n); their keys are gathered
-  // from the position-ordered keys
-  const int n_sink = (int)(v.n < p.S ? v.n : p.S);
-  const int n_open = v.n > v.open_lo ? (int)(v.n - v.open_lo) : 0;
-  const int base_len = n_sink + n_open;
-  for (int i = tid; i < base_len; i += bd) {
-    const int pos = i < n_sink ? i : (int)(v.open_lo + (i - n_sink));
-    if (p.write_cand) cand[i] = pos;
-    crow[i] = pos;
-  }
-  if (p.dbg_version && tid == 0) {
-    p.dbg_version[4 * t + 0] = v.r;
-    p.dbg_version[4 * t + 1] = v.m;
-    p.dbg_version[4 * t + 2] = v.cvis;
-    p.dbg_version[4 * t + 3] = (int)v.open_lo;
-  }
-  const int room = p.budget - base_len;
-  if (room <= 0 || v.cvis == 0) {
-    if (tid == 0) {
-      p.cand_len[t] = base_len;
-      if (p.cluster_major) p.n_sel[t] = 0;
-      if (p.dbg_n_order) p.dbg_n_order[t] = 0;
-    }
-    return;
-  }
-
-  // composites and sizes of the visible slots; empty slots get key 0
-  const float* srep = p.srep + (size_t)t * p.srep_ld;
-  int alive_total = 0;
-  for (int s = tid; s < slot_pow2; s += bd) {
-    uint64_t c = 0;
-    int sz = 0;
-    if (s < v.cvis) {
-      sz = (s < v.split ? ep.size : p.seal.size)[s];
-      if (sz > 0) c = make_comp(srep[s], (uint32_t)s);
-    }
-    comp[s] = c;
-    wt[s] = sz;
-    alive_total += sz;
-  }
-  int total;
-  block_exclusive_scan(alive_total, wtmp, &total);
-  const uint64_t thr = (total <= room) ? 1ull : radix_select_desc(comp, wt, v.cvis, room, sc);
-
-  // stable in-place compaction of the selected clusters (comp >= thr, nonzero)
-  if (tid == 0) s_nsel = 0;
-  __syncthreads();
-  for (int b0 = 0; b0 < v.cvis; b0 += bd) {
-    const int i = b0 + tid;
-    const uint64_t c = i < v.cvis ? comp[i] : 0ull;
-    const int flag = (c != 0 && c >= thr) ? 1 : 0;
-    int tot;
-    const int ex = block_exclusive_scan(flag, wtmp, &tot);
-    const int base = s_nsel;
-    __syncthreads();
-    if (flag) comp[base + ex] = c;
-    __syncthreads();
-    if (tid == 0) s_nsel = base + tot;
-    __syncthreads();
-  }
-  const int nsel = s_nsel;
-  const int P2 = next_pow2(nsel);
-  for (int i = nsel + tid; i < P2; i += bd) comp[i] = 0ull;
-  __syncthreads();
-  bitonic_sort_desc(comp, P2);
-
-  // prefix sums of member counts in rank order
-  int chunk_base = 0;
-  for (int b0 = 0; b0 < nsel; b0 += bd) {
-    const int i = b0 + tid;
-    int sz = 0;
-    if (i < nsel) {
-      const int s = (int)comp_id(comp[i]);
-      sz = (s < v.split ? ep.size : p.seal.size)[s];
-    }
-    int tot;
-    const int ex = block_exclusive_scan(sz, wtmp, &tot);
-    if (i < nsel) wt[i] = chunk_base + ex;
-    chunk_base += tot;
-    __syncthreads();
-  }
-  if (tid == 0) s_total = chunk_base;
-  __syncthreads();
-  const int used = min(room, s_total);
-  record_selection(p, v, t, comp, wt, base_len, nsel);
-
-  // fill: candidate c -> cluster i with wt[i] <= c < wt[i+1]
-  for (int c = tid; c < used; c += bd) {
-    int lo = 0, hi = nsel - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (wt[mid] <= c) lo = mid; else hi = mid - 1;
-    }
-    const int s = (int)comp_id(comp[lo]);
-    const bool from_epoch = s < v.split;
-    const int off = max((from_epoch ? ep.off : p.seal.off)[s], 0);
-    const int j = off + (c - wt[lo]);
-    if (p.write_cand) cand[base_len + c] = (from_epoch ? ep.members : p.seal.members)[j];
-    crow[base_len + c] = ((from_epoch ? 2 + v.r % 3 : 1) << CROW_SHIFT) | j;
-  }
-  if (p.dbg_order) {
-    for (int i = tid; i < nsel && i < p.dbg_order_cap; i += bd) {
-      const int s = (int)comp_id(comp[i]);
-      const int sz = (s < v.split ? ep.size : p.seal.size)[s];
-      p.dbg_order[(size_t)t * p.dbg_order_cap + i] = s;
-      if (p.dbg_take) p.dbg_take[(size_t)t * p.dbg_order_cap + i] = min(sz, room - wt[i]);
-    }
-  }
-  if (tid == 0) {
-    p.cand_len[t] = base_len + used;
-    if (p.dbg_n_order) p.dbg_n_order[t] = nsel;
-  }
+  __shared__ FullCutShared sh;
+  select_full(p, blockIdx.x, slot_pow2, lds, sh);
 }
 
 // Fast version (cut_clusters in cut.h): a size-weighted value histogram finds the
@@ -366,10 +223,6 @@ hipError_t launch_route_select(const RouteParams& p, int max_slots, hipStream_t 
     hipLaunchKernelGGL(k_route_select_fast<SF_THREADS>, dim3(p.T), dim3(SF_THREADS), 0, s, p);
   hipError_t e0 = hipGetLastError();
   if (e0 != hipSuccess) return e0;
-  return launch_route_select_full(p, max_slots, s);
-}
-
-hipError_t launch_route_select_full(const RouteParams& p, int max_slots, hipStream_t s) {
   const int slot_pow2 = next_pow2(max_slots > 0 ? max_slots : 1);
   const size_t lds = (size_t)slot_pow2 * (sizeof(uint64_t) + sizeof(int));
   hipError_t e = hipFuncSetAttribute((const void*)k_route_select, hipFuncAttributeMaxDynamicSharedMemorySize,

@@ -121,6 +121,7 @@ struct idx_index {
   int* cand = nullptr;
   int* cand_len = nullptr;
   int* redo = nullptr;
+  int* route_ovf = nullptr;      // [max_queries + 2] overflow list of the fused cut + rescoring
   int64_t* qpos = nullptr;   // positions of a decode batch (idx_route_topk_pos)
   // cluster-major rescoring: selections per query, pairs grouped by cluster, work items
   int64_t sel_cap = 0, pair_cap = 0, item_cap = 0;
@@ -271,7 +272,7 @@ int idx_create(const idx_config* cfg, void* stream, idx_index** out) {
             ix->alloc(&ix->sl_ckeys, ix->member_cap * ix->RB) &&
             (c.dtype != IDX_E4M3 || ix->alloc(&ix->sl_cscale, ix->member_cap)) &&
             ix->alloc(&ix->cand_len, c.max_queries) && ix->alloc(&ix->redo, c.max_queries) &&
-            ix->alloc(&ix->qpos, c.max_queries);
+            ix->alloc(&ix->route_ovf, (int64_t)c.max_queries + 2) && ix->alloc(&ix->qpos, c.max_queries);
   if (ok && c.rescore_mode == IDX_RESCORE_CLUSTER)
     ok = ix->alloc(&ix->sel_id, (int64_t)c.max_queries * ix->sel_cap) &&
             ix->alloc(&ix->sel_dst, (int64_t)c.max_queries * ix->sel_cap) && ix->alloc(&ix->n_sel, c.max_queries) &&
@@ -595,6 +596,7 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   p.cand_ld = ix->cand_cap;
   p.cand_len = ix->cand_len;
   p.redo = ix->redo;
+  p.ovf = ix->route_ovf;
   p.topk_idx = topk_idx;
   p.topk_score = topk_score;
   p.cluster_major = c.rescore_mode == IDX_RESCORE_CLUSTER;
@@ -661,10 +663,10 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   mark(5);
   mark(6);
   if (fused) {
-    p.only_redo = 1;
-    if (e == hipSuccess) e = launch_route_select_full(p, max_slots, s);
+    if (e == hipSuccess) e = launch_route_overflow(p, c.dtype, c.dim, ix->HT, call_cap, max_slots, s);
+  } else {
+    if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
   }
-  if (e == hipSuccess) e = launch_rescore_topk(p, c.dtype, c.dim, ix->HT, call_cap, s);
   mark(7);
   if (e != hipSuccess) return device_error(ix, e, "route launch");
   if (dbg) {
