@@ -202,3 +202,39 @@ def test_route_small_batches_bit_identical(name):
         say(f"  {name}: {T} queries as one batch and as batches of 64, 1, 35 and 60: bit-identical")
     finally:
         ivf.idx_destroy(ix)
+
+
+def test_route_overflow_list_across_calls():
+    """The fused kernel hands queries whose short cluster list overflows to the
+    overflow kernel through a device list that each call leaves empty.  Calls in a
+    row that alternate between many overflowing queries (a cluster-list capacity of
+    3) and none, over queries from before the first seal to past two refits, give
+    the bits of the list-based path every time."""
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload("c1r", q_pos0=900, T=3300)
+    T, k, budget, q_pos0 = wl["T"], wl["k"], 1200, wl["q_pos0"]
+    q = to_dev(inp["q"][:T])
+    w = to_dev(inp["w"][:T])
+    ref = {}
+    ix = gpu_index(wl, inp, rescore="query", max_queries=T, max_budget=budget)
+    try:
+        for cap in (0, 3):
+            idx, sc = ivf.idx_route_topk(ix, q, None, w, q_pos0, k, budget, debug={"list_cap": cap})
+            torch.cuda.synchronize()
+            ref[cap] = (idx.cpu().numpy(), sc.cpu().numpy())
+    finally:
+        ivf.idx_destroy(ix)
+    assert np.array_equal(ref[0][0], ref[3][0]) and np.array_equal(ref[0][1].view(np.uint32), ref[3][1].view(np.uint32))
+    ix = gpu_index(wl, inp, rescore="auto", max_queries=T, max_budget=budget)
+    try:
+        for call, cap in enumerate((3, 0, 3, 3, 0)):
+            idx, sc = ivf.idx_route_topk(ix, q, None, w, q_pos0, k, budget, debug={"list_cap": cap})
+            torch.cuda.synchronize()
+            assert np.array_equal(idx.cpu().numpy(), ref[cap][0]), f"call {call} (list capacity {cap}): top-k differs"
+            assert np.array_equal(sc.cpu().numpy().view(np.uint32), ref[cap][1].view(np.uint32)), \
+                f"call {call} (list capacity {cap}): scores differ"
+    finally:
+        ivf.idx_destroy(ix)
+    say(f"  {T} queries, five calls alternating overflow and none: fused = list-based, bit for bit")
