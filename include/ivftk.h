@@ -151,8 +151,9 @@ typedef struct {
                             rescoring and top-k in one kernel); cluster-by-cluster or split
                             candidate scores; candidate scores + top-k (fused: only the
                             queries whose cut went to the full kernel)                     */
-  int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut kernel at this
-                            size so the full cut kernel takes over sooner (testing)        */
+  int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut (in the cut
+                            kernel or the fused cut + rescoring kernel) at this size, so
+                            the full radix-select cut takes over sooner (testing)          */
   float* cand_scores;    /* [T, cand_cap]: exact score of each candidate, fill order      */
 } idx_route_debug;
 
