@@ -11,19 +11,29 @@ chunk's queries, launch the next refit if one is due (side stream).
   the same protocol;
 * the 128K bf16 workload (16 chunks of 8192): every query's candidates lie in
   its prefix, its version is the one the protocol publishes, and the candidate
-  count is min(prefix, max(budget, sinks + open window)).
+  count is min(prefix, max(budget, sinks + open window)); and 16 seeded queries of
+  every chunk equal the oracle's routing over the clusters the library published
+  (read back with idx_export: the sealed windows and the epochs the chunk uses).
 """
 import numpy as np
 import pytest
 
 from gpu_common import check_routed_query, ensure_built, oracle_cfg, say, to_dev, workload
-from oracle import OracleIndex
-from oracle.index import key_values, query_values
+from oracle import OracleIndex, codec
+from oracle.index import key_values, make_cluster, query_values
 
 pytestmark = pytest.mark.gpu
 
 
-def _stream(name, check_every=None, seed=0, **over):
+def _exported_clusters(exp, dtype):
+    out = []
+    for s in range(exp["sizes"].shape[0]):
+        sz, off = int(exp["sizes"][s]), int(exp["offsets"][s])
+        out.append(make_cluster(s, exp["members"][off:off + sz].astype(np.int64), exp["centroids"][s], dtype))
+    return out
+
+
+def _stream(name, check_every=None, exported_every=None, seed=0, **over):
     import torch
     import ivf_top_key_amd as ivf
     ensure_built()
@@ -42,6 +52,10 @@ def _stream(name, check_every=None, seed=0, **over):
     oix = OracleIndex(oracle_cfg(wl)) if check_every else None
     rng = np.random.default_rng(seed)
     stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
+    if exported_every:
+        kv_all = key_values(inp["keys"], inp["k_scale"], dt)
+        X_all = codec.dequantize(inp["keys"], inp["k_scale"], dt)
+        n_exported = 0
     try:
         for c0 in range(0, N, chunk):
             c1 = min(N, c0 + chunk)
@@ -92,7 +106,27 @@ def _stream(name, check_every=None, seed=0, **over):
                 if oix.refit_due() and oix.computed == oix.published:
                     oix.refit()
                 assert launched == (oix.computed > oix.published)
-        say(f"  ok, {N} queries; oracle comparisons {stats}")
+            if exported_every:
+                # the oracle routes over the clusters the library published: every sealed
+                # window, and the epochs this chunk's queries use (synchronized above, so a
+                # refit launched after the route has finished and wrote a newer epoch slot)
+                eix = OracleIndex(oracle_cfg(wl))
+                eix.kv, eix.X = kv_all, X_all
+                seal = _exported_clusters(ivf.idx_export(ix, -1), dt)
+                eix.seals = [seal[i:i + Cs] for i in range(0, len(seal), Cs)]
+                for r in sorted(set(r_t.tolist())):
+                    if r >= 1:
+                        eix.epochs[r] = _exported_clusters(ivf.idx_export(ix, r), dt)
+                eix.computed = eix.published = P
+                qv = query_values(_queries(inp, c0, c1, wl), _qscale(inp, c0, c1, wl), dt)
+                wv = _weights(inp, c0, c1, wl).astype(np.float64)
+                for t in np.sort(rng.choice(n_q, min(exported_every, n_q), replace=False)):
+                    _, _, od = eix.route(_queries(inp, c0 + t, c0 + t + 1, wl), _qscale(inp, c0 + t, c0 + t + 1, wl),
+                                         _weights(inp, c0 + t, c0 + t + 1, wl), c0 + int(t), k, budget, debug=True)
+                    check_routed_query(int(t), d, od[0], eix, qv, wv, k, budget, dt, stats)
+                    n_exported += 1
+        say(f"  ok, {N} queries; oracle comparisons {stats}"
+            + (f"; {n_exported} of them over the exported clusters" if exported_every else ""))
     finally:
         ivf.idx_destroy(ix)
 
@@ -115,4 +149,4 @@ def test_streaming_parity_bf16_reduced():
 
 
 def test_streaming_causality_128k_bf16():
-    _stream("c3", check_every=None, T=131072)
+    _stream("c3", check_every=None, exported_every=16, T=131072)
