@@ -53,7 +53,10 @@ def test_shape_index_route_exhaustive(name, over):
 
 
 def test_largest_k():
-    """k = 4096 (the largest) with an 8192-candidate budget: the selection's widest case."""
+    """k = 4096 (the largest) with an 8192-candidate budget: the selection's widest case,
+    in a small batch (split scoring) and in a batch of more than 64 queries (the fused
+    cut + rescoring kernel)."""
     route_parity("bf16_small", k=4096, budget=8192, T=48, q_pos0=12240)
+    route_parity("e4m3_small", k=4096, budget=8192, T=100, q_pos0=12188)
     from test_gpu_exhaustive import _run
     _run("bf16_small", q_pos0=12240, T=48, k=4096)
