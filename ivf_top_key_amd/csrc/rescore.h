@@ -107,15 +107,57 @@ __device__ __forceinline__ int sel_entry(int u) {
   return 4 * ((u >> 2) * NT + (int)threadIdx.x) + (u & 3);
 }
 
+// Gather row code (CROW_*) -> key position: source 0 rows are positions, a store
+// copy's row j holds that store's member j (the seal store, or the epoch store of the
+// query's epoch).  Every lane loads (source 0 reads a valid dummy word and drops it).
+struct PosMap {
+  const int* mem0;   // the dummy word; the members of source s sit at mem0 + d_s bytes
+  int64_t d1, d2;
+  int jmax;
+  __device__ __forceinline__ const int* addr(uint32_t code) const {
+    const int src = (int)(code >> CROW_SHIFT);
+    const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
+    const int* mb = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(mem0) + ((d1 & m1) | (d2 & m2)));
+    const int j = (int)(code & (uint32_t)CROW_MASK);
+    return mb + (src == 0 ? 0 : (j < jmax ? j : jmax));
+  }
+  __device__ __forceinline__ uint32_t position(uint32_t code, int loaded) const {
+    return (code >> CROW_SHIFT) == 0 ? (code & (uint32_t)CROW_MASK) : (uint32_t)loaded;
+  }
+};
+
+__device__ __forceinline__ PosMap pos_map(const RouteParams& p, int t) {
+  const QVer qv = query_version(p, t);
+  const int e = qv.r % 3;
+  PosMap m;
+  m.mem0 = p.cand_len + t;
+  const int* mem2 = e == 0 ? p.ep[0].members : (e == 1 ? p.ep[1].members : p.ep[2].members);
+  m.d1 = (int64_t)(uintptr_t)p.seal.members - (int64_t)(uintptr_t)m.mem0;
+  m.d2 = (int64_t)(uintptr_t)mem2 - (int64_t)(uintptr_t)m.mem0;
+  m.jmax = (int)max((int64_t)0, p.n_keys - 1 - p.S);
+  return m;
+}
+
+constexpr int POS_BATCH = 8;   // positions one thread resolves with its loads in flight together
+
+// The code source of an eager selection (the codes arrive in cv).
+struct NoCodes {
+  __device__ void operator()(const int (&)[POS_BATCH], uint32_t (&)[POS_BATCH]) const {}
+};
+
 // Top-k of one query's L scored candidates held in registers: kv[u] = the order key
-// of entry sel_entry(u)'s score, cv[u] = its gather row code (CROW_*); entries >= L
-// are ignored.  The codes become key positions (source 0 rows are positions; a store
-// copy's row j holds that store's member j), the k winners by (score desc, position
-// asc) go to topk_idx / topk_score.  lds = the selection region (free on entry after
-// a barrier that follows every thread's last read of it).  All NT threads call.
-template <int PT, int NT>
+// of entry sel_entry(u)'s score; entries >= L are ignored.  The k winners by (score
+// desc, position asc) go to topk_idx / topk_score.  lds = the selection region (free
+// on entry after a barrier that follows every thread's last read of it).  All NT
+// threads call.
+// Eager (LAZY = false): cv[u] = entry u's gather row code; every entry's position is
+// resolved first.  LAZY: codes(idx, code) gives the codes of POS_BATCH list entries;
+// the entries are binned and placed by their list index, and only those that can win
+// (the bins at and above the one holding the k-th score: about k of the L) are then
+// resolved to positions, as a dense list that every lane of the block shares.
+template <int PT, int NT, bool LAZY, class Codes>
 __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, int k_pow2, uint32_t (&kv)[PT],
-                                            uint32_t (&cv)[PT], uint64_t* lds, SelWords<NT>& sw) {
+                                            uint32_t (&cv)[PT], Codes codes, uint64_t* lds, SelWords<NT>& sw) {
   constexpr int KPT = 4096 / NT;   // winners per thread at the largest k
   static_assert(RS_NBIN % NT == 0 && NT % 64 == 0 && NT <= 1024, "block shape");
   uint32_t* okey = reinterpret_cast<uint32_t*>(lds);   // fallback: [L] score keys
@@ -125,30 +167,56 @@ __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, 
   int* offs = hist + RS_NBIN;                                      // [RS_NBIN]
   const int tid = threadIdx.x, bd = NT;
   const int K = p.k;
-  {
-    // positions: every lane loads (source 0 reads a valid dummy word), then selects
-    const QVer qv = query_version(p, t);
-    const int e = qv.r % 3;
-    const int* mem0 = p.cand_len + t;
-    const int* mem2 = e == 0 ? p.ep[0].members : (e == 1 ? p.ep[1].members : p.ep[2].members);
-    const int64_t d1 = (int64_t)(uintptr_t)p.seal.members - (int64_t)(uintptr_t)mem0;
-    const int64_t d2 = (int64_t)(uintptr_t)mem2 - (int64_t)(uintptr_t)mem0;
-    const int jmax = (int)max((int64_t)0, p.n_keys - 1 - p.S);
+  const PosMap pm = pos_map(p, t);
+  // positions of every entry, POS_BATCH at a time with their loads in flight together
+  auto resolve_all = [&]() {
+    if constexpr (LAZY) {
+#pragma unroll
+      for (int u0 = 0; u0 < PT; u0 += POS_BATCH) {
+        int idx[POS_BATCH];
+        uint32_t code[POS_BATCH];
+#pragma unroll
+        for (int c = 0; c < POS_BATCH; ++c) idx[c] = min(sel_entry<NT>(u0 + c), max(L - 1, 0));
+        codes(idx, code);
+#pragma unroll
+        for (int c = 0; c < POS_BATCH; ++c) cv[u0 + c] = code[c];
+      }
+    }
     int mv[PT];
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int src = (int)(cv[u] >> CROW_SHIFT);
-      const int64_t m1 = -(int64_t)(src == 1), m2 = -(int64_t)(src >= 2);
-      const int* mb = reinterpret_cast<const int*>(reinterpret_cast<const uint8_t*>(mem0) + ((d1 & m1) | (d2 & m2)));
-      const int j = (int)(cv[u] & (uint32_t)CROW_MASK);
-      mv[u] = mb[src == 0 ? 0 : (j < jmax ? j : jmax)];
-    }
+    for (int u = 0; u < PT; ++u) mv[u] = *pm.addr(cv[u]);
 #pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int src = (int)(cv[u] >> CROW_SHIFT);
-      cv[u] = src == 0 ? (cv[u] & (uint32_t)CROW_MASK) : (uint32_t)mv[u];
+    for (int u = 0; u < PT; ++u) cv[u] = pm.position(cv[u], mv[u]);
+  };
+  // LAZY: arr[0..n) hold (score key << 32) | list index; the low word becomes ~position
+  auto resolve_dense = [&](uint64_t* arr, int n) {
+    for (int b0 = 0; b0 < n; b0 += NT * POS_BATCH) {
+      uint64_t v[POS_BATCH];
+      int idx[POS_BATCH];
+      uint32_t code[POS_BATCH];
+#pragma unroll
+      for (int c = 0; c < POS_BATCH; ++c) {
+        const int a = b0 + c * NT + tid;
+        v[c] = a < n ? arr[a] : 0ull;
+        idx[c] = a < n ? (int)(uint32_t)v[c] : 0;
+      }
+      codes(idx, code);
+      int mv[POS_BATCH];
+#pragma unroll
+      for (int c = 0; c < POS_BATCH; ++c) mv[c] = *pm.addr(code[c]);
+#pragma unroll
+      for (int c = 0; c < POS_BATCH; ++c) {
+        const int a = b0 + c * NT + tid;
+        if (a < n) arr[a] = (v[c] & 0xFFFFFFFF00000000ull) | (uint64_t)(~pm.position(code[c], mv[c]));
+      }
     }
-  }
+  };
+  if constexpr (!LAZY) resolve_all();
+  // the low word of a placed entry: ~position, or (LAZY) the list index until resolved
+  auto low = [&](int u) -> uint32_t {
+    if constexpr (LAZY) return (uint32_t)sel_entry<NT>(u);
+    else return ~cv[u];
+  };
   if (tid == 0) {
     sw.cnt = 0;
     sw.tie = 0;
@@ -162,9 +230,13 @@ __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, 
 #pragma unroll
     for (int u = 0; u < PT; ++u) {
       const int i = sel_entry<NT>(u);
-      if (i < P2) sel[i] = i < L ? comp(kv[u], cv[u]) : 0ull;
+      if (i < P2) sel[i] = i < L ? (((uint64_t)kv[u] << 32) | low(u)) : 0ull;
     }
     __syncthreads();
+    if constexpr (LAZY) {
+      resolve_dense(sel, L);
+      __syncthreads();
+    }
     bitonic_sort_desc(sel, P2);
     write_topk(sel, L, K, oi, os);
     return;
@@ -219,12 +291,18 @@ __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, 
     for (int u = 0; u < PT; ++u) {
       if (sel_entry<NT>(u) < L) {
         const int bb = (int)bins(kv[u]);
-        if (bb > bstar) sel[atomicAdd(&hist[bb], 1)] = comp(kv[u], cv[u]);
-        else if (bb == bstar) tie[atomicAdd(&sw.tie, 1)] = comp(kv[u], cv[u]);
+        const uint64_t v = ((uint64_t)kv[u] << 32) | low(u);
+        if (bb > bstar) sel[atomicAdd(&hist[bb], 1)] = v;
+        else if (bb == bstar) tie[atomicAdd(&sw.tie, 1)] = v;
       }
     }
     const int P2 = next_pow2(in_bin);
     __syncthreads();
+    if constexpr (LAZY) {
+      resolve_dense(sel, above);
+      resolve_dense(tie, in_bin);
+      __syncthreads();
+    }
     if (P2 <= 64) {
       if (tid < 64) tie[tid] = wave_sort_desc(tid < in_bin ? tie[tid] : 0ull);
     } else {
@@ -265,6 +343,7 @@ __device__ __forceinline__ void topk_select(const RouteParams& p, int t, int L, 
     return;
   }
   // ---- fallback: exact radix select (all keys equal, or a crowded cut bin) ----
+  if constexpr (LAZY) resolve_all();
   __syncthreads();
 #pragma unroll
   for (int u = 0; u < PT; ++u) {
@@ -433,7 +512,7 @@ __device__ inline void rescore_query(const RouteParams& p, int t, int k_pow2, ui
       }
     }
   }
-  topk_select<PT, NT>(p, t, L, k_pow2, kv, cv, lds, sw);
+  topk_select<PT, NT, false>(p, t, L, k_pow2, kv, cv, NoCodes{}, lds, sw);
 }
 
 template <int DT, int D, int HT, int PT, int NT>
@@ -561,8 +640,7 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_rescore(RouteParams p, int
   }
   __syncthreads();
   uint32_t kv[PT];
-  uint32_t cv[PT];
-  int s = 0;
+  uint32_t cv[PT];   // written by the selection where it needs every entry's position
 #pragma unroll
   for (int u4 = 0; u4 < PT / 4; ++u4) {
     const int i0 = 4 * (u4 * NT + tid);
@@ -576,11 +654,30 @@ __global__ __launch_bounds__(RS_THREADS) void k_route_rescore(RouteParams p, int
 #pragma unroll
       for (int e = 0; e < 4; ++e) kv[4 * u4 + e] = i0 + e < L ? okey[i0 + e] : 0u;
     }
-    if (i0 >= base_len && i0 < L) s = seg_search(pre, nsel, i0 - base_len);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) cv[4 * u4 + e] = i0 + e < L ? code_at(i0 + e, s) : 0u;
   }
-  topk_select<PT, NT>(p, t, L, k_pow2, kv, cv, lds, sw);
+  // row codes of POS_BATCH list entries (each < L): the sinks and the open window
+  // directly, cluster members through a binary search over the prefix sums, the
+  // batch's searches stepping together
+  auto codes = [&](const int (&idx)[POS_BATCH], uint32_t (&code)[POS_BATCH]) {
+    int sx[POS_BATCH];
+#pragma unroll
+    for (int c = 0; c < POS_BATCH; ++c) sx[c] = 0;
+    if (nsel > 0) {
+      for (int step = 1 << (31 - __builtin_clz((unsigned)nsel)); step > 0; step >>= 1) {
+#pragma unroll
+        for (int c = 0; c < POS_BATCH; ++c) {
+          const int cc = idx[c] - base_len;
+          if (cc >= 0 && sx[c] + step < nsel && pre[sx[c] + step] <= cc) sx[c] += step;
+        }
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < POS_BATCH; ++c) {
+      const int i = idx[c];
+      code[c] = i < base_len ? (i < n_sink ? (uint32_t)i : open_d + (uint32_t)i) : seg[sx[c]] + (uint32_t)(i - base_len);
+    }
+  };
+  topk_select<PT, NT, true>(p, t, L, k_pow2, kv, cv, codes, lds, sw);
 }
 
 // The queries k_route_rescore appended to the overflow list: the full cut
