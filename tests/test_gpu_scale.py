@@ -20,7 +20,7 @@ the ones the oracle can make one output at a time:
   (epoch r-1's centroids and the newer seal centroids): a float64 distance screen,
   then the fixed-order fp32 distances for each key whose two nearest lie within
   the fp32 evaluation's error bound of each other;
-* 64 seeded routed queries = the oracle's routing over the published clusters.
+* 1024 seeded routed queries = the oracle's routing over the published clusters.
 """
 import numpy as np
 import pytest
@@ -238,7 +238,7 @@ def test_scale_1m_e4m3():
         oix.seals = [sc_all[i:i + Cs] for i in range(0, len(sc_all), Cs)]
         oix.epochs[P] = _clusters(ep, dt)
         oix.computed = oix.published = P
-        picks = np.sort(rng.choice(T, 64, replace=False))
+        picks = np.sort(rng.choice(T, 1024, replace=False))
         d = _debug_rows(dbg, picks)
         d["topk_idx"], d["topk_score"] = idx, sc
         stats = dict(order_swaps=0, topk_exempt=0, max_err=0.0)
@@ -246,7 +246,7 @@ def test_scale_1m_e4m3():
             _, _, od = oix.route(inp["q"][t:t + 1], inp["q_scale"][t:t + 1], inp["w"][t:t + 1], q_pos0 + int(t), k,
                                  wl["budget"], debug=True)
             check_routed_query(int(t), d, od[0], oix, qv, wv, k, wl["budget"], dt, stats)
-        say(f"  routed: 64 seeded queries match the oracle's routing over the published clusters {stats}")
+        say(f"  routed: 1024 seeded queries match the oracle's routing over the published clusters {stats}")
         rec = np.mean([np.intersect1d(a[a >= 0], b[b >= 0]).size / k for a, b in zip(idx, eidx)])
         say(f"  recall vs exhaustive {rec:.4f}")
     finally:
