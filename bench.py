@@ -232,16 +232,18 @@ def main():
         # contractions: flops against the MFMA peak of the format
         "rep_score": ("mfma", float(2 * H * d * c_vis.sum())),
         "cluster_score": ("mfma", float(2 * H * d * clus_t.sum())),
-        # cut + fill: read each query's representative scores and cluster sizes, write its
-        # list (the gather row of every candidate)
-        "route_select": ("hbm", float((c_vis * 8).sum() + cand_t.sum() * 4)),
+        # cut + fill: read each query's representative scores and the visible clusters'
+        # sizes (one array shared by every query, counted once), write its list (the
+        # gather row of every candidate)
+        "route_select": ("hbm", float((c_vis * 4).sum() + c_vis.max() * 4 + cand_t.sum() * 4)),
     }
     if fused:
-        # the cut's reads (each query's representative scores and its visible clusters'
-        # sizes) and the method's rescoring bytes: every candidate's key row and scale,
-        # the query (row, head weight and scale per head), the top-k written (position
-        # and score); the member positions this design also reads are not counted
-        work["route_rescore"] = ("hbm", float((c_vis * 8).sum() + cand_t.sum() * (rb + scale_b)
+        # the cut's reads (each query's representative scores; the visible clusters'
+        # sizes, one array shared by every query, counted once) and the method's
+        # rescoring bytes: every candidate's key row and scale, the query (row, head
+        # weight and scale per head), the top-k written (position and score); the
+        # member positions this design also reads are not counted
+        work["route_rescore"] = ("hbm", float((c_vis * 4).sum() + c_vis.max() * 4 + cand_t.sum() * (rb + scale_b)
                                               + T * H * (rb + 8) + T * k * 8))
         work["split_score"] = ("mfma", 0.0)
         work["overflow_path"] = ("hbm", 0.0)
