@@ -778,7 +778,9 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, cons
   // the key is the row over two), so tile tt's slots are tile 0's plus tt*32*CPR.
   static_assert(S::CPR <= 32 && 32 % S::CPR == 0, "tile offsets independent of the swizzle");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, col = tid & 31, g = (tid >> 5) & 1;
-  const int nst = (nrows + S::SR - 1) / S::SR;
+  // nrows is the same in every lane (often read from LDS, which the compiler cannot
+  // tell): the stage loop and the loads' scalar offsets stay in scalar registers
+  const int nst = __builtin_amdgcn_readfirstlane((nrows + S::SR - 1) / S::SR);
   if (nst == 0) return;
   const __amdgpu_buffer_rsrc_t rrow = buffer_rsrc(base, nrows * S::RB);
   const __amdgpu_buffer_rsrc_t rscl = buffer_rsrc(scale, scale ? nrows * 4 : 0);
@@ -803,14 +805,16 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, cons
       lds.sc1[i] = 1.0f;
     }
   }
+  // st is the same in every lane: its offsets are read into scalar registers
   auto dma = [&](int st, u32x4* rows, float* sc) {
+    const int soff = __builtin_amdgcn_readfirstlane(st * S::SR * S::RB);
 #pragma unroll
     for (int k = 0; k < CPT; ++k)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rrow, (lds_void*)(rows + (k * NW + wave) * 64), 16, voff[k],
-                                               st * S::SR * S::RB, 0, 0);
+                                               soff, 0, 0);
     if (scale && wave * 64 < S::SR)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rscl, (lds_void*)(sc + wave * 64), 4, (wave * 64 + lane) * 4,
-                                               st * S::SR * 4, 0, 0);
+                                               __builtin_amdgcn_readfirstlane(st * S::SR * 4), 0, 0);
   };
   auto operand = [&](uint32_t* bf, const u32x4* tb, int tt) {
 #pragma unroll
@@ -822,18 +826,35 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, cons
       bf[4 * i + 3] = v.w;
     }
   };
+  // Paired tiles hand their scores to the sink one stage late, right after the next
+  // barrier: the sink's stores (or its ballot and branch) then neither split the
+  // stage's contraction into separate blocks of code nor hold up the barrier's
+  // wait for this wave's memory operations.
+  constexpr int NPEND = PAIR ? TPS / 2 : 1;
+  float pend[NPEND];
+  int pend_st = -1;
+  auto flush = [&]() {
+    if (pend_st >= 0) {
+#pragma unroll
+      for (int i = 0; i < NPEND; ++i) sink(pend_st * S::SR + 2 * i * 32 + lane, pend[i]);
+    }
+  };
   auto compute = [&](int st, const u32x4* tb, const float* sb) {
     if constexpr (PAIR) {
       // rows past nrows are zeros (the loads return zeros past the end) and their sink
       // calls are dropped by the callers, so every pair of the stage is scored
+      flush();
+      float scl[NPEND];
+#pragma unroll
+      for (int tt = 0; tt < TPS; tt += 2) scl[tt / 2] = sb[tt * 32 + lane];
 #pragma unroll
       for (int tt = 0; tt < TPS; tt += 2) {
         uint32_t bA[G::HW], bB[G::HW];
         operand(bA, tb, tt);
         operand(bB, tb, tt + 1);
-        const float x = score_tile_pair<DT, D, HT>(f, bA, bB) * sb[tt * 32 + lane];
-        sink(st * S::SR + tt * 32 + lane, x);
+        pend[tt / 2] = score_tile_pair<DT, D, HT>(f, bA, bB) * scl[tt / 2];
       }
+      pend_st = st;
     } else {
 #pragma unroll
       for (int tt = 0; tt < TPS; ++tt) {
@@ -862,6 +883,7 @@ __device__ __forceinline__ void score_staged(const QueryFrag<DT, D, HT>& f, cons
     __builtin_amdgcn_s_waitcnt(0x0F70);
     __syncthreads();
   }
+  if constexpr (PAIR) flush();
 }
 
 }  // namespace ivftk
