@@ -242,13 +242,14 @@ __global__ __launch_bounds__(256) void k_refit_brute(RefitParams p) {
 // bf16(v), v_lo = bf16(v - v_hi), |e| <= 2^-16 |v|, as hi.hi + hi.lo + lo.hi (the
 // products are exact).  E4M3 codes and bf16 keys are exact in bf16, so for them the
 // key is not split (x_lo = 0, and the E4M3 key scale multiplies the accumulated
-// dot product, one more rounding and the 2^-24 rounding of each scaled key value,
-// both far inside the bound below).  |A - D| for the fixed-order distance D is at most
+// dot product inside the final fused multiply-add; the 2^-24 rounding of each
+// scaled key value in the norm is far inside the bound below).  |A - D| for the fixed-order distance D is at most
 //   E(x) = 2.5e-4 |x| cmax + 6e-5 (|x| + cmax)^2 + 1e-30   (cmax >= every |c|):
 // the split drops lo.lo and e terms (< 3.1 * 2^-16 |x||c| per dot product), the
 // fp32 sums of 3d products add < 384 * 2^-23 * 1.01 |x||c|, both doubled by the
-// factor 2, and the norms, the final operations and the fixed-order evaluation's
-// own error stay below 4e-5 (|x|+|c|)^2 for d <= 128.  The exact nearest c* has
+// factor 2, and the norms, the final operations (one add, then one fused
+// multiply-add that applies -2 and the key scale to the dot product) and the
+// fixed-order evaluation's own error stay below 4e-5 (|x|+|c|)^2 for d <= 128.  The exact nearest c* has
 // A(c*) - E <= D(c*) <= D(c_min) <= Amin + E, so only slots with A <= Amin + 2E can
 // be it; those are evaluated in the fixed order, and the result equals the brute
 // force.  The cut carries 1% slack on E against fp32 rounding of the comparison.  A
@@ -368,6 +369,7 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     const float sum = nxr + cmr;
     const float E = (2.5e-4f * nxr * cmr + 6e-5f * sum * sum + 1e-30f) * (1.0f + 1e-5f);
     const float E2 = 2.02f * E;   // the cut Amin + 2E with 1% slack
+    const float m2k = -2.0f * ksc;  // A = fma(-2 sk, <x, c>', |x|^2 + |c|^2): one rounding for the product term
     float amin = __builtin_inff();
     float aout = __builtin_inff();   // smallest A among slots that cannot survive the cut
     int ls[SCR_LIST];
@@ -401,10 +403,6 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
         if constexpr (SPLIT_KEY) mfma_step<DT_BF16>(acc, a, &bl[4 * i]);
         mfma_step<DT_BF16>(acc, al, &bx[4 * i]);
       }
-      if constexpr (DT == DT_E4M3) {
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = acc[v] * ksc;
-      }
       float A[16];
       float tmin = __builtin_inff();
 #pragma unroll
@@ -414,7 +412,7 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int v = 4 * j + e;
-          A[v] = (nx + cv[e]) - 2.0f * acc[v];
+          A[v] = __builtin_fmaf(m2k, acc[v], nx + cv[e]);
           if constexpr (CERT) {
             if (csl[b][8 * j + 4 * g + e] != own) tmin = __builtin_fminf(tmin, A[v]);
           } else {
