@@ -150,7 +150,9 @@ typedef struct {
                             the selections by cluster (or, when AUTO fuses them, cut,
                             rescoring and top-k in one kernel); cluster-by-cluster or split
                             candidate scores; candidate scores + top-k (fused: only the
-                            queries whose cut went to the full kernel)                     */
+                            queries whose cut went to the full kernel).  A NULL entry is
+                            not recorded (each record costs a few microseconds of stream
+                            time)                                                          */
   int32_t list_cap;      /* > 0: cap the short cluster list of the fast cut (in the cut
                             kernel or the fused cut + rescoring kernel) at this size, so
                             the full radix-select cut takes over sooner (testing)          */

@@ -637,7 +637,7 @@ static int route_common(idx_index* ix, const void* q, const float* q_scale, cons
   hipEvent_t* ev = (dbg && dbg->events) ? reinterpret_cast<hipEvent_t*>(dbg->events) : nullptr;
   hipError_t e = hipSuccess;
   auto mark = [&](int i) {
-    if (ev && e == hipSuccess) e = hipEventRecord(ev[i], s);
+    if (ev && ev[i] && e == hipSuccess) e = hipEventRecord(ev[i], s);
   };
   // AUTO with a large batch: cut, rescoring and top-k in one kernel; a query whose
   // cluster list overflows goes through the full cut kernel and the rescoring kernel
