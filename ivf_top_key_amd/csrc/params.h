@@ -186,7 +186,8 @@ struct RefitParams {
   int* ovf_count;
   int brute_ovf;       // 1: the brute-force kernel takes its keys from ovf
   // certification of the keys of epoch r-1 (see refit.hip)
-  uint32_t* hkey;      // [(r-1)*Q] selection keys of the old slots' drifts
+  uint32_t* hkey;      // [(r-1)*Q] selection keys of the old slots' drifts, then each old
+                       // slot's place in hlist (0xFFFFFFFF: not listed)
   int* hlist;          // [r*Q] listed slots: the most-moved old slots, then the new ones
   int* nlist;          // device scalar: listed slots
   float* rest_drift;   // device scalar: largest drift of an unlisted live old slot

@@ -171,8 +171,17 @@ __global__ __launch_bounds__(1024) void k_refit_hsel(RefitParams p) {
   const int m = min(n_old, max(32, (n_old / 4 + 31) / 32 * 32));
   uint32_t T = 0u;   // listed: live slots with key > T
   if (s_alive > m) T = radix_select32_desc(p.hkey, n_old, m + 1, sc);
-  for (int s = tid; s < n_old; s += blockDim.x)
-    if (p.hkey[s] > T) p.hlist[atomicAdd(&s_n, 1)] = s;
+  __syncthreads();
+  // hkey[s] becomes slot s's place in the list (0xFFFFFFFF: not listed), which the
+  // certifying screen uses to find the one tile that holds a key's own slot
+  for (int s = tid; s < n_old; s += blockDim.x) {
+    uint32_t at = 0xFFFFFFFFu;
+    if (p.hkey[s] > T) {
+      at = (uint32_t)atomicAdd(&s_n, 1);
+      p.hlist[at] = s;
+    }
+    p.hkey[s] = at;
+  }
   __syncthreads();
   const int nh = s_n;
   for (int i = tid; i < p.Q; i += blockDim.x) p.hlist[nh + i] = n_old + i;
@@ -340,6 +349,9 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
     else if (item < total) x = (int64_t)p.work[item - n_new];
     x = min(max(x, (int64_t)p.S), (CERT ? p.B_prev : p.B_r) - 1);
     const int own = CERT ? min(max(p.assign[x], 0), (p.r - 1) * p.Q - 1) : -1;
+    // the tile of the list that holds the own slot (-1: the own slot is not listed);
+    // only tiles that hold some lane's own slot compare slot ids
+    const int own_tile = CERT ? (int)p.hkey[own] >> 5 : -1;
     // this lane's half of the key as bf16 (B operand), and the squared norm
     // B operand: this lane's half of the key in bf16.  E4M3 codes and bf16 keys are
     // exact in bf16 (the E4M3 scale multiplies the dot product afterwards), so one
@@ -410,15 +422,15 @@ __global__ __launch_bounds__(256) void k_refit_screen(RefitParams p) {
         const float4 c4 = *reinterpret_cast<const float4*>(&cn[b][8 * j + 4 * g]);
         const float cv[4] = {c4.x, c4.y, c4.z, c4.w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int v = 4 * j + e;
-          A[v] = __builtin_fmaf(m2k, acc[v], nx + cv[e]);
-          if constexpr (CERT) {
-            if (csl[b][8 * j + 4 * g + e] != own) tmin = __builtin_fminf(tmin, A[v]);
-          } else {
-            tmin = __builtin_fminf(tmin, A[v]);
-          }
-        }
+        for (int e = 0; e < 4; ++e) A[4 * j + e] = __builtin_fmaf(m2k, acc[4 * j + e], nx + cv[e]);
+      }
+      if (CERT && __ballot(own_tile == tl) != 0ull) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (csl[b][8 * (v >> 2) + 4 * g + (v & 3)] != own) tmin = __builtin_fminf(tmin, A[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tmin = __builtin_fminf(tmin, A[v]);
       }
       if constexpr (CERT) {
         amin = __builtin_fminf(amin, tmin);   // smallest A over the listed slots but the own one
