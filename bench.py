@@ -201,9 +201,10 @@ def main():
     # launch that follows (queries whose short cluster list overflowed: none here) is
     # inside the step but not timed on its own.
     fused = args.rescore == "auto" and T > 64 and max(budget, wl["n_sink"] + W) <= 8192
-    evs = [[hip.event() for _ in range(8)] for _ in range(args.steps)]
     if fused:
-        evs = [[e[0], None, e[2], e[3], None, None, None, None] for e in evs]
+        evs = [[hip.event(), None, hip.event(), hip.event(), None, None, None, None] for _ in range(args.steps)]
+    else:
+        evs = [[hip.event() for _ in range(8)] for _ in range(args.steps)]
     start, stop = hip.event(), hip.event()
     torch.cuda.synchronize()
     hip.h.hipEventRecord(ctypes.c_void_p(start), ctypes.c_void_p(stream.cuda_stream))
