@@ -390,7 +390,8 @@ def main():
         "vs_baseline": None,
         "dtype": dt,
         "data": "synthetic",
-        "config": {"workload": f"1M-token prefix ({N} keys), {dt} keys+queries with fp32 scales, H={H}, d={d}, "
+        "config": {"workload": f"{'1M' if N == 1 << 20 else str(N // 1024) + 'K'}-token prefix ({N} keys), {dt} "
+                               f"keys+queries{' with fp32 scales' if dt == 'e4m3' else ''}, H={H}, d={d}, "
                                f"{T} tail queries, k={k}, budget {budget}",
                    "global_batch": T, "seq_len": N, "parallelism": "single GPU",
                    "rescore": "query-major" if args.rescore != "cluster" else "cluster-major"},
