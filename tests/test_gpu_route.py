@@ -238,3 +238,51 @@ def test_route_overflow_list_across_calls():
     finally:
         ivf.idx_destroy(ix)
     say(f"  {T} queries, five calls alternating overflow and none: fused = list-based, bit for bit")
+
+
+def test_route_debug_events_null_entries_skipped():
+    """Timing events in the debug struct: all eight marks, or only some (NULL entries
+    are not recorded), leave the outputs bit-identical to a call without events, and
+    the recorded marks give ordered, non-negative spans."""
+    import ctypes
+    import torch
+    import ivf_top_key_amd as ivf
+    ensure_built()
+    wl, inp = workload("e4m3_small")
+    T, k, budget, q_pos0 = wl["T"], wl["k"], wl["budget"], wl["q_pos0"]
+    q = to_dev(inp["q"])
+    qs = to_dev(inp["q_scale"])
+    w = to_dev(inp["w"])
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+
+    def event():
+        ev = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(ev)) == 0
+        return ev.value
+
+    def elapsed(a, b):
+        ms = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) == 0
+        return ms.value
+
+    ix = gpu_index(wl, inp)
+    try:
+        runs = {}
+        all8 = [event() for _ in range(8)]
+        some = [event(), None, event(), event(), None, None, None, None]
+        for name, dbg in (("none", None), ("all", {"events": all8}), ("some", {"events": some})):
+            idx, sc = ivf.idx_route_topk(ix, q, qs, w, q_pos0, k, budget, debug=dbg)
+            torch.cuda.synchronize()
+            runs[name] = (idx.cpu().numpy(), sc.cpu().numpy())
+        for name in ("all", "some"):
+            assert np.array_equal(runs["none"][0], runs[name][0]), name
+            assert np.array_equal(runs["none"][1].view(np.uint32), runs[name][1].view(np.uint32)), name
+        spans = [elapsed(all8[i], all8[i + 1]) for i in range(7)]
+        assert all(x >= 0.0 for x in spans), spans
+        assert elapsed(some[0], some[2]) >= 0.0 and elapsed(some[2], some[3]) > 0.0
+        say(f"  {T} queries: outputs unchanged by events; spans (ms) {[round(x, 4) for x in spans]}")
+        for e in all8 + [e for e in some if e]:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    finally:
+        ivf.idx_destroy(ix)
